@@ -1,0 +1,53 @@
+"""Build the HIP library (libq4adamw.so) for gfx950, in-tree.
+
+hipcc flags: -ffp-contract=off (no FMA contraction, so every FP32 operation
+rounds where it is written); HIP's default IEEE division and square root;
+packed FP32 instructions disabled at the target-feature level.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD_DIR = os.path.join(HERE, "_build")
+LIB_PATH = os.path.join(BUILD_DIR, "libq4adamw.so")
+SOURCES = [os.path.join(CSRC, "q4_kernels.hip"), os.path.join(CSRC, "q4_abi.cpp")]
+DEPS = SOURCES + [os.path.join(CSRC, "q4_internal.h"), os.path.join(CSRC, "q4_codebooks.inc"),
+                  os.path.join(ROOT, "include", "q4adamw.h")]
+
+HIPCC_FLAGS = [
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found: the GPU library cannot be built")
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    if not force and os.path.exists(LIB_PATH):
+        t = os.path.getmtime(LIB_PATH)
+        if all(os.path.getmtime(d) <= t for d in DEPS):
+            return LIB_PATH
+    tmp = LIB_PATH + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(force=True, verbose=True))

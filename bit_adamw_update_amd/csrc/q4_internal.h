@@ -1,0 +1,89 @@
+// q4_internal.h -- structures shared by the host ABI (q4_abi.cpp) and the
+// HIP kernels (q4_kernels.hip) of the fused 4-bit AdamW step.  Not part of
+// the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace q4 {
+
+constexpr int kBlock = 128;            // elements per quantization block
+constexpr int kBlocksPerChunk = 4;     // one wavefront step: 4 blocks = 512 elements
+constexpr int kChunkElems = kBlock * kBlocksPerChunk;
+constexpr int kWavesPerGroup = 4;      // 256-thread work-groups
+constexpr int kBandRows = 256;         // rows per band of the row/column partial kernel
+constexpr int kTileCols = 512;         // columns per tile (64 lanes x 8 BF16)
+constexpr int kGroup = 256;            // rows (columns) per finalize work-group
+
+enum Kind : int32_t { KIND_PACKED = 0, KIND_FACTORED = 1, KIND_FP32 = 2 };
+
+// One tensor as the step kernel sees it (128 bytes, read with scalar loads).
+struct alignas(16) DevTensor {
+    float* param;
+    const uint16_t* grad;
+    uint8_t* m_codes;
+    float* m_scales;
+    uint8_t* v_codes;
+    float* v_scales;
+    float* v_row;
+    float* v_col;
+    float* m32;
+    float* v32;
+    int64_t numel;
+    int64_t cols;          // factored matrix: numel / shape[0]; else 0
+    int64_t chunk_begin;   // first chunk of this tensor in the step kernel
+    const float* inv_meanR;  // factored matrix: slot written by the finalize kernel
+    uint32_t tensor_id;
+    uint32_t flags;
+    int32_t kind;
+    int32_t pad;
+};
+static_assert(sizeof(DevTensor) == 128, "DevTensor layout");
+
+// One factored matrix [rows, cols] for the row/column statistics kernels.
+struct alignas(16) DevMatrix {
+    const uint16_t* grad;
+    float* R;
+    float* C;
+    double* part_row;    // [n_ctiles][rows] partial row sums of g^2
+    double* part_col;    // [n_bands][cols] partial column sums of g^2
+    double* part_mean;   // [n_rgroups] sums of the updated R over 256-row groups
+    float* inv_meanR;    // 1 / mean(R) after the update (0 if mean(R) is 0)
+    int64_t rows, cols;
+    int64_t tile_begin;  // first tile (band x column tile) of this matrix
+    int64_t n_ctiles, n_bands;
+    int64_t rgroup_begin, n_rgroups;
+    int64_t cgroup_begin, n_cgroups;
+    int64_t pad[3];
+};
+static_assert(sizeof(DevMatrix) == 160, "DevMatrix layout");
+
+// Scalars of one step, passed by value.
+struct StepScalars {
+    float beta1, beta2, omb1, omb2, eps, eps_sr, decay, step_size, rsbc2;
+    uint32_t step;        // low 32 bits of the step count (Philox counter word)
+    uint32_t key0, key1;  // Philox key (seed)
+    uint32_t lm_head_sr;  // final-phase flag
+    uint32_t m_sr_all;    // every tensor rounds m by SR
+    uint32_t eden;        // EDEN rescale of packed v
+};
+
+// Kernel variants that exist (m codebook, v codebook, v rule).
+struct Variant { int mcb, vcb, vrule; };
+
+hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevTensor* d_tab,
+                             const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks,
+                             hipStream_t stream);
+hipError_t launch_fp32_step(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
+                            int n_tensors, int64_t total_chunks, hipStream_t stream);
+hipError_t launch_factored_stats(const DevMatrix* d_mats, int n_mats, int64_t total_tiles, int64_t total_rgroups,
+                                 int64_t total_cgroups, float beta2, float omb2, hipStream_t stream);
+hipError_t launch_fill(void* p, size_t bytes, uint8_t value, hipStream_t stream);
+hipError_t launch_dequant(int mcb, int vcb, const DevTensor& t, int64_t rows, float* m_out, float* v_out,
+                          double* ws_partials, float* ws_inv, hipStream_t stream);
+bool variant_supported(const Variant& v);
+void codebook_table(int cb, float out[16]);
+
+}  // namespace q4

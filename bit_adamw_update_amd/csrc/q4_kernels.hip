@@ -1,0 +1,773 @@
+// q4_kernels.hip -- HIP kernels of the fused 4-bit AdamW optimizer step for
+// CDNA4 (gfx950).
+//
+// What is computed follows the pages on 4-bit AdamW state quantization:
+//   "Rounding in Preconditioner Space" (paper listing): abstract, Table 1
+//   (rounding rules), Table 2 (ZIP-SR and ZE-EDEN recipes, LM-head switch);
+//   AReno "4-bit AdamW", section "State representation" (128-element
+//   parameter-local blocks; factored v for matrices, packed zero-excluding v
+//   for vectors; bounded block-local FP32 work);
+//   the news article on the two 4-bit AdamW methods (AdamW description,
+//   1.0625 B/param storage).
+//
+// How it maps onto the chip: the step is an elementwise stream at ~12 bytes
+// per parameter, so it is bound by HBM, not by the matrix cores.  A 64-lane
+// wavefront owns a chunk of four 128-element blocks; each lane owns 8
+// consecutive elements, so a block is one 16-lane DPP row and every block
+// statistic (absmax, EDEN sums, the per-level square roots of ZIP-SR) is a
+// row-local DPP or ds_bpermute exchange with no LDS traffic.  Each lane
+// moves its parameters as two 16-byte loads, its gradients as one 16-byte
+// load and each moment's 8 codes as one 4-byte load.  One launch covers
+// every tensor: waves walk a grid-stride sequence of tensor-aligned chunks
+// and follow a prefix table of chunk offsets.
+//
+// Arithmetic is FP32, round-to-nearest-even, without contraction (the
+// library is built with -ffp-contract=off) and with IEEE division and
+// square root, in the order stated for each operation, so that every code
+// decision is reproducible bit for bit on any IEEE implementation.
+
+#include <utility>
+
+#include "q4_internal.h"
+#include "../../include/q4adamw.h"
+#include "q4_codebooks.inc"
+
+namespace q4 {
+
+// ---------------------------------------------------------------------------
+// Codebooks
+// ---------------------------------------------------------------------------
+
+__host__ __device__ constexpr float bits2f(uint32_t b) { return __builtin_bit_cast(float, b); }
+
+template <int CB> struct CbBits;
+template <> struct CbBits<Q4_CB_NF4> { static constexpr uint32_t b[16] = Q4_CB_BITS_NF4; };
+template <> struct CbBits<Q4_CB_SDYN4> { static constexpr uint32_t b[16] = Q4_CB_BITS_SDYN4; };
+template <> struct CbBits<Q4_CB_DYN4> { static constexpr uint32_t b[16] = Q4_CB_BITS_DYN4; };
+template <> struct CbBits<Q4_CB_DYN4_NZ> { static constexpr uint32_t b[16] = Q4_CB_BITS_DYN4_NZ; };
+template <> struct CbBits<Q4_CB_LIN4_NZ> { static constexpr uint32_t b[16] = Q4_CB_BITS_LIN4_NZ; };
+
+// Sorted view of a codebook: N distinct levels ascending; code_of maps a
+// sorted index to its code (identity except for the sign-magnitude SDyn4,
+// whose "-0" code 8 is never produced).
+template <int CB> struct Book {
+    static constexpr int N = CB == Q4_CB_SDYN4 ? 15 : 16;
+    static constexpr int code_of(int k) {
+        return CB == Q4_CB_SDYN4 ? (k < 7 ? 15 - k : (k == 7 ? 0 : k - 7)) : k;
+    }
+    static constexpr float level(int k) { return bits2f(CbBits<CB>::b[code_of(k)]); }
+    // FP32 midpoint of adjacent levels; an exact midpoint rounds down.
+    static constexpr float mid(int k) { return (level(k) + level(k + 1)) * 0.5f; }
+    template <int J> static constexpr float midc() { constexpr float m = mid(J); return m; }
+};
+
+static constexpr bool sorted_ok(int cb) {
+    // levels strictly increasing and every midpoint strictly inside its cell
+    switch (cb) {
+#define Q4_CHECK(CB)                                                                             \
+    case CB:                                                                                     \
+        for (int k = 0; k + 1 < Book<CB>::N; ++k)                                                \
+            if (!(Book<CB>::level(k) < Book<CB>::mid(k) && Book<CB>::mid(k) < Book<CB>::level(k + 1))) \
+                return false;                                                                    \
+        return true;
+        Q4_CHECK(Q4_CB_NF4) Q4_CHECK(Q4_CB_SDYN4) Q4_CHECK(Q4_CB_DYN4) Q4_CHECK(Q4_CB_DYN4_NZ)
+        Q4_CHECK(Q4_CB_LIN4_NZ)
+#undef Q4_CHECK
+    }
+    return false;
+}
+static_assert(sorted_ok(Q4_CB_NF4) && sorted_ok(Q4_CB_SDYN4) && sorted_ok(Q4_CB_DYN4) &&
+                  sorted_ok(Q4_CB_DYN4_NZ) && sorted_ok(Q4_CB_LIN4_NZ),
+              "codebook levels must be strictly increasing with interior midpoints");
+
+// Device copies, indexed at run time when the LDS tables are filled.
+__constant__ uint32_t c_decode[5][16] = {Q4_CB_BITS_NF4, Q4_CB_BITS_SDYN4, Q4_CB_BITS_DYN4, Q4_CB_BITS_DYN4_NZ,
+                                         Q4_CB_BITS_LIN4_NZ};
+
+template <int CB> __device__ __forceinline__ float sorted_level_rt(int k) {
+    return bits2f(c_decode[CB][Book<CB>::code_of(k)]);
+}
+
+void codebook_table(int cb, float out[16]) {
+    static const uint32_t host[5][16] = {Q4_CB_BITS_NF4, Q4_CB_BITS_SDYN4, Q4_CB_BITS_DYN4, Q4_CB_BITS_DYN4_NZ,
+                                         Q4_CB_BITS_LIN4_NZ};
+    for (int i = 0; i < 16; ++i) out[i] = bits2f(host[cb][i]);
+}
+
+// Round-to-nearest sorted index: the number of midpoints strictly below x,
+// as a sum of compares against compile-time constants.
+template <int CB, int... J>
+__device__ __forceinline__ int rtn_count(float x, std::integer_sequence<int, J...>) {
+    return (0 + ... + (x > Book<CB>::template midc<J>() ? 1 : 0));
+}
+template <int CB> __device__ __forceinline__ int rtn_index(float x) {
+    return rtn_count<CB>(x, std::make_integer_sequence<int, Book<CB>::N - 1>{});
+}
+
+// ---------------------------------------------------------------------------
+// Small device primitives
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
+// 32x32->64 multiplies with the published multipliers, the key bumped by the
+// published Weyl constants between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    }
+    return c;
+}
+
+// The 8 uniforms of a lane whose first element index e0 is a multiple of 8:
+// element i uses word i mod 4 of Philox(ctr = (i/4, step, tensor, stream)),
+// its top 24 bits scaled by 2^-24.
+__device__ __forceinline__ void uniforms8(uint64_t e0, uint32_t step, uint32_t tid, uint32_t stream, uint32_t k0,
+                                          uint32_t k1, float u[8]) {
+    const uint32_t c0 = (uint32_t)(e0 >> 2);
+    const uint4 a = philox4x32_10(make_uint4(c0, step, tid, stream), k0, k1);
+    const uint4 b = philox4x32_10(make_uint4(c0 + 1u, step, tid, stream), k0, k1);
+    const float s = 5.9604644775390625e-8f;  // 2^-24
+    u[0] = (float)(a.x >> 8) * s; u[1] = (float)(a.y >> 8) * s; u[2] = (float)(a.z >> 8) * s;
+    u[3] = (float)(a.w >> 8) * s; u[4] = (float)(b.x >> 8) * s; u[5] = (float)(b.y >> 8) * s;
+    u[6] = (float)(b.z >> 8) * s; u[7] = (float)(b.w >> 8) * s;
+}
+
+template <int CTRL> __device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// DPP controls within a 16-lane row: swap neighbours, swap pairs, mirror
+// each half-row, mirror the row.  Applied in that order, each lane ends up
+// with the row's pairwise-tree reduction of its 16 lane values.
+constexpr int DPP_QUAD_1032 = 0xB1, DPP_QUAD_2301 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
+
+__device__ __forceinline__ float row_max16(float x) {
+    x = fmaxf(x, dpp<DPP_QUAD_1032>(x));
+    x = fmaxf(x, dpp<DPP_QUAD_2301>(x));
+    x = fmaxf(x, dpp<DPP_ROW_HALF_MIRROR>(x));
+    x = fmaxf(x, dpp<DPP_ROW_MIRROR>(x));
+    return x;
+}
+// Sum over the 16 lanes of a row, combining lanes (0,1),(2,3).. then pairs
+// of pairs, then halves: the pairwise tree over the lanes in index order
+// (IEEE addition is commutative, so both partners get the same bits).
+__device__ __forceinline__ float row_sum16(float x) {
+    x = x + dpp<DPP_QUAD_1032>(x);
+    x = x + dpp<DPP_QUAD_2301>(x);
+    x = x + dpp<DPP_ROW_HALF_MIRROR>(x);
+    x = x + dpp<DPP_ROW_MIRROR>(x);
+    return x;
+}
+__device__ __forceinline__ float tree8(const float* v) {
+    return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+}
+__device__ __forceinline__ float bperm(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(lane << 2, __float_as_int(v)));
+}
+
+// ---------------------------------------------------------------------------
+// Per-lane element I/O (8 consecutive elements starting at e0)
+// ---------------------------------------------------------------------------
+
+struct Lane8 {
+    float p[8];
+    float g[8];
+    uint32_t mc, vc;  // 8 nibbles each, element k at bits 4k..4k+3
+};
+
+__device__ __forceinline__ void load8(const DevTensor& T, int64_t e0, int nv, bool packed_v, Lane8& L) {
+    if (nv == 8) {
+        const float4 a = *reinterpret_cast<const float4*>(T.param + e0);
+        const float4 b = *reinterpret_cast<const float4*>(T.param + e0 + 4);
+        L.p[0] = a.x; L.p[1] = a.y; L.p[2] = a.z; L.p[3] = a.w;
+        L.p[4] = b.x; L.p[5] = b.y; L.p[6] = b.z; L.p[7] = b.w;
+        const uint4 gq = *reinterpret_cast<const uint4*>(T.grad + e0);
+        L.g[0] = bf16_to_f32(gq.x & 0xFFFFu); L.g[1] = bf16_to_f32(gq.x >> 16);
+        L.g[2] = bf16_to_f32(gq.y & 0xFFFFu); L.g[3] = bf16_to_f32(gq.y >> 16);
+        L.g[4] = bf16_to_f32(gq.z & 0xFFFFu); L.g[5] = bf16_to_f32(gq.z >> 16);
+        L.g[6] = bf16_to_f32(gq.w & 0xFFFFu); L.g[7] = bf16_to_f32(gq.w >> 16);
+        L.mc = *reinterpret_cast<const uint32_t*>(T.m_codes + (e0 >> 1));
+        L.vc = packed_v ? *reinterpret_cast<const uint32_t*>(T.v_codes + (e0 >> 1)) : 0u;
+    } else {
+        L.mc = 0; L.vc = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            L.p[k] = k < nv ? T.param[e0 + k] : 0.0f;
+            L.g[k] = k < nv ? bf16_to_f32(T.grad[e0 + k]) : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (2 * j < nv) {
+                L.mc |= (uint32_t)T.m_codes[(e0 >> 1) + j] << (8 * j);
+                if (packed_v) L.vc |= (uint32_t)T.v_codes[(e0 >> 1) + j] << (8 * j);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void store_params8(const DevTensor& T, int64_t e0, int nv, const float* p) {
+    if (nv == 8) {
+        *reinterpret_cast<float4*>(T.param + e0) = make_float4(p[0], p[1], p[2], p[3]);
+        *reinterpret_cast<float4*>(T.param + e0 + 4) = make_float4(p[4], p[5], p[6], p[7]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (k < nv) T.param[e0 + k] = p[k];
+    }
+}
+
+__device__ __forceinline__ void store_codes8(uint8_t* codes, int64_t e0, int nv, uint32_t word) {
+    if (nv == 8) {
+        *reinterpret_cast<uint32_t*>(codes + (e0 >> 1)) = word;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (2 * j < nv) codes[(e0 >> 1) + j] = (uint8_t)(word >> (8 * j));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K1: the fused step for packed and factored tensors
+// ---------------------------------------------------------------------------
+
+// Tables in LDS: decode by code, and the sorted levels (for SR brackets and
+// the EDEN inner product).
+struct BookLds {
+    float dec_m[16], dec_v[16], lev_m[16], lev_v[16];
+};
+
+template <int MCB, int VCB>
+__device__ __forceinline__ void fill_books(BookLds& b) {
+    const int t = threadIdx.x;
+    if (t < 16) {
+        b.dec_m[t] = bits2f(c_decode[MCB][t]);
+        b.dec_v[t] = bits2f(c_decode[VCB][t]);
+        b.lev_m[t] = t < Book<MCB>::N ? sorted_level_rt<MCB>(t) : 1.0f;
+        b.lev_v[t] = t < Book<VCB>::N ? sorted_level_rt<VCB>(t) : 1.0f;
+    }
+}
+
+// State-space SR bracket from the RTN index c of x: the lower level is c or
+// c - 1 (the FP32 midpoints lie strictly inside their cells); x below the
+// first level (zero-excluding maps only) stays at index 0; an exact level
+// hit or the top level needs no draw.
+template <int N>
+__device__ __forceinline__ void sr_bracket(const float* lev, float x, int c, int& lo, float& Llo, float& Lhi,
+                                           bool& can_move) {
+    const float Lc = lev[c];
+    const bool below = x < Lc;
+    lo = below ? (c > 0 ? c - 1 : 0) : c;
+    Llo = lev[lo];
+    const int hi = lo + 1 < N ? lo + 1 : N - 1;
+    Lhi = lev[hi];
+    can_move = !(below && c == 0) && !(Llo == x) && (lo != N - 1);
+}
+
+template <int MCB, int VCB, int VRULE>
+__global__ __launch_bounds__(256) void k_fused_step(const DevTensor* __restrict__ tab,
+                                                     const int64_t* __restrict__ chunk_begin, int n_tensors,
+                                                     int64_t total_chunks, StepScalars sc) {
+    __shared__ BookLds books;
+    fill_books<MCB, VCB>(books);
+    __syncthreads();
+
+    constexpr int NM = Book<MCB>::N, NV = Book<VCB>::N;
+    constexpr bool V_SR = VRULE == Q4_RULE_STATE_SR || VRULE == Q4_RULE_UPDATE_SR;
+    constexpr bool V_UPD = VRULE == Q4_RULE_UPDATE_SR || VRULE == Q4_RULE_UPDATE_RTN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int row = lane >> 4, sub = lane & 15;
+    const int row_base = row << 4;
+
+    int t = 0;
+    for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks;
+         c += (int64_t)gridDim.x * kWavesPerGroup) {
+        while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
+        const DevTensor T = tab[t];
+        const int64_t n = T.numel;
+        const int64_t blk = (c - T.chunk_begin) * kBlocksPerChunk + row;
+        const int64_t e0 = blk * kBlock + sub * 8;
+        const int64_t rem = n - e0;
+        const int nv = rem >= 8 ? 8 : (rem > 0 ? (int)rem : 0);
+        const bool blk_ok = blk * kBlock < n;
+        const bool packed_v = T.kind == KIND_PACKED;
+
+        Lane8 L;
+        if (nv > 0) {
+            load8(T, e0, nv, packed_v, L);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) { L.p[k] = 0.0f; L.g[k] = 0.0f; }
+            L.mc = 0; L.vc = 0;
+        }
+        const float sm_old = blk_ok ? T.m_scales[blk] : 0.0f;
+        const float sv_old = (blk_ok && packed_v) ? T.v_scales[blk] : 0.0f;
+
+        // factored second moment: v1 = (R_r C_c) / mean(R), row-major [rows, cols]
+        float vf[8];
+        if (!packed_v) {
+            const float inv_mean = *T.inv_meanR;
+            // row of the chunk's first element (wave-uniform), then a 32-bit
+            // division for the lane's offset (cols < 2^31 is validated)
+            const uint32_t cols = (uint32_t)T.cols;
+            const int64_t ce0 = (c - T.chunk_begin) * kChunkElems;
+            const int64_t rb = ce0 / T.cols;
+            const uint32_t off = (uint32_t)(e0 - rb * T.cols);
+            const uint32_t dr = off / cols;
+            uint32_t cc = off - dr * cols;
+            int64_t rr = rb + dr;
+            if (nv == 8 && cc + 8u <= cols && (cc & 3u) == 0u) {
+                const float Rr = T.v_row[rr];
+                const float4 a = *reinterpret_cast<const float4*>(T.v_col + cc);
+                const float4 b = *reinterpret_cast<const float4*>(T.v_col + cc + 4);
+                const float cv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+                for (int k = 0; k < 8; ++k) vf[k] = (Rr * cv[k]) * inv_mean;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    vf[k] = 0.0f;
+                    if (k < nv) {
+                        vf[k] = (T.v_row[rr] * T.v_col[cc]) * inv_mean;
+                        if (++cc == cols) { cc = 0; ++rr; }
+                    }
+                }
+            }
+        }
+
+        // AdamW on the unquantized moments
+        float m1[8], v1[8], sv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float g = L.g[k];
+            const float m0 = books.dec_m[(L.mc >> (4 * k)) & 15u] * sm_old;
+            const float mm = sc.beta1 * m0 + sc.omb1 * g;
+            float vv;
+            if (packed_v) {
+                const float v0 = books.dec_v[(L.vc >> (4 * k)) & 15u] * sv_old;
+                vv = sc.beta2 * v0 + sc.omb2 * (g * g);
+            } else {
+                vv = vf[k];
+            }
+            const float s = sqrtf(vv);
+            const float denom = s * sc.rsbc2 + sc.eps;
+            L.p[k] = L.p[k] * sc.decay - sc.step_size * (mm / denom);
+            const bool ok = k < nv;
+            m1[k] = ok ? mm : 0.0f;
+            v1[k] = ok ? vv : 0.0f;
+            sv[k] = s;
+        }
+        if (nv > 0) store_params8(T, e0, nv, L.p);
+
+        // first moment: absmax scale of the block, then RTN or state-space SR
+        float am = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(m1[k]));
+        const float s_m = row_max16(am);
+        const float inv_m = s_m > 0.0f ? 1.0f / s_m : 0.0f;
+        const bool m_sr = sc.m_sr_all || ((T.flags & Q4_TF_LM_HEAD) && sc.lm_head_sr);
+        float um[8];
+        if (m_sr) uniforms8((uint64_t)e0, sc.step, T.tensor_id, 0u, sc.key0, sc.key1, um);
+        uint32_t mword = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float x = fminf(fmaxf(m1[k] * inv_m, -1.0f), 1.0f);
+            int idx = rtn_index<MCB>(x);
+            if (m_sr) {
+                int lo; float Llo, Lhi; bool mv;
+                sr_bracket<NM>(books.lev_m, x, idx, lo, Llo, Lhi, mv);
+                idx = lo + ((mv && um[k] * (Lhi - Llo) < (x - Llo)) ? 1 : 0);
+            }
+            const int code = MCB == Q4_CB_SDYN4 ? (idx < 7 ? 15 - idx : (idx == 7 ? 0 : idx - 7)) : idx;
+            mword |= (uint32_t)code << (4 * k);
+        }
+        if (nv > 0) store_codes8(T.m_codes, e0, nv, mword);
+        if (blk_ok && sub == 0) T.m_scales[blk] = s_m;
+
+        if (!packed_v) continue;
+
+        // second moment: max scale of the block, the v rule, EDEN
+        float av = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) av = fmaxf(av, v1[k]);
+        const float s_v = row_max16(av);
+        const float inv_v = s_v > 0.0f ? 1.0f / s_v : 0.0f;
+        // lane `sub` of the row holds sqrt(level_sub * s_v), the square root
+        // of the state value each level would store
+        const float root_own = V_UPD ? sqrtf(books.lev_v[sub] * s_v) : 0.0f;
+        float uv[8];
+        if (V_SR) uniforms8((uint64_t)e0, sc.step, T.tensor_id, 1u, sc.key0, sc.key1, uv);
+        uint32_t vword = 0;
+        float xx[8], xq[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float x = fminf(v1[k] * inv_v, 1.0f);
+            int idx = rtn_index<VCB>(x);
+            if (VRULE != Q4_RULE_STATE_RTN) {
+                int lo; float Llo, Lhi; bool mv;
+                sr_bracket<NV>(books.lev_v, x, idx, lo, Llo, Lhi, mv);
+                bool up = false;
+                if (VRULE == Q4_RULE_STATE_SR) {
+                    up = uv[k] * (Lhi - Llo) < (x - Llo);
+                } else {
+                    const int hi = lo + 1 < NV ? lo + 1 : NV - 1;
+                    const float rlo = bperm(root_own, row_base + lo);
+                    const float rhi = bperm(root_own, row_base + hi);
+                    if (VRULE == Q4_RULE_UPDATE_SR) {
+                        // P(up) = (r(a_lo) - r(v)) / (r(a_lo) - r(a_hi)), r(a) = 1/(sqrt(a) + eps_sr),
+                        // multiplied out so that nothing cancels next to a_lo = 0
+                        const float num = (sv[k] - rlo) * (rhi + sc.eps_sr);
+                        const float den = (rhi - rlo) * (sv[k] + sc.eps_sr);
+                        up = uv[k] * den < num;
+                    } else {
+                        // nearer level in r: r(v) - r(a_hi) < r(a_lo) - r(v)
+                        const float left = (rhi - sv[k]) * (rlo + sc.eps_sr);
+                        const float right = (sv[k] - rlo) * (rhi + sc.eps_sr);
+                        up = left < right;
+                    }
+                }
+                idx = lo + ((mv && up) ? 1 : 0);
+            }
+            vword |= (uint32_t)idx << (4 * k);
+            xx[k] = x * x;
+            xq[k] = x * books.lev_v[idx];
+        }
+        if (nv > 0) store_codes8(T.v_codes, e0, nv, vword);
+        float stored = s_v;
+        if (sc.eden) {
+            // EDEN: S = <x,x> / <x,Q(x)> over the block, pairwise tree in index order
+            const float sxx = row_sum16(tree8(xx));
+            const float sxq = row_sum16(tree8(xq));
+            const float S = sxq > 0.0f ? sxx / sxq : 1.0f;
+            stored = s_v * S;
+        }
+        if (blk_ok && sub == 0) T.v_scales[blk] = stored;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K1 for the FP32 recipe (quantization off: plain 32-bit AdamW)
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_fp32_step(const DevTensor* __restrict__ tab,
+                                                    const int64_t* __restrict__ chunk_begin, int n_tensors,
+                                                    int64_t total_chunks, StepScalars sc) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int t = 0;
+    for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks;
+         c += (int64_t)gridDim.x * kWavesPerGroup) {
+        while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
+        const DevTensor T = tab[t];
+        const int64_t e0 = (c - T.chunk_begin) * kChunkElems + lane * 8;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t i = e0 + k;
+            if (i < T.numel) {
+                const float g = bf16_to_f32(T.grad[i]);
+                const float mm = sc.beta1 * T.m32[i] + sc.omb1 * g;
+                const float vv = sc.beta2 * T.v32[i] + sc.omb2 * (g * g);
+                const float denom = sqrtf(vv) * sc.rsbc2 + sc.eps;
+                T.param[i] = T.param[i] * sc.decay - sc.step_size * (mm / denom);
+                T.m32[i] = mm;
+                T.v32[i] = vv;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K2 / K3: factored second moment (row and column means of g^2)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ double shfl_xor_d(double v, int m) { return __shfl_xor(v, m, 64); }
+
+// Sum of one double per lane over the wavefront, butterfly in fixed order.
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v = v + shfl_xor_d(v, m);
+    return v;
+}
+
+// Sum over the 256 threads of a work-group, tree in LDS in fixed order.
+__device__ __forceinline__ double group_sum_d(double v, double* lds) {
+    lds[threadIdx.x] = v;
+    __syncthreads();
+    for (int s = 128; s > 0; s >>= 1) {
+        if ((int)threadIdx.x < s) lds[threadIdx.x] = lds[threadIdx.x] + lds[threadIdx.x + s];
+        __syncthreads();
+    }
+    const double r = lds[0];
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ int find_matrix(const DevMatrix* mats, int n, int64_t x, int which) {
+    // last matrix whose begin (tile / row group / column group) is <= x
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        const int64_t b = which == 0 ? mats[mid].tile_begin : (which == 1 ? mats[mid].rgroup_begin
+                                                                          : mats[mid].cgroup_begin);
+        if (b <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// K2: one work-group per (band of 256 rows) x (tile of 512 columns).  Lane
+// j of every wave owns columns 8j..8j+7 of the tile; wave w takes rows
+// w, w+4, ... of the band.  Column partials stay in registers (binary64)
+// and are combined across the 4 waves in LDS; each row's partial over the
+// tile is a wavefront butterfly.  No atomics: the order is fixed.
+__global__ __launch_bounds__(256) void k_rowcol_partial(const DevMatrix* __restrict__ mats, int n_mats) {
+    __shared__ double lds[kWavesPerGroup][kTileCols];
+    const int64_t tile = blockIdx.x;
+    const int mi = find_matrix(mats, n_mats, tile, 0);
+    const DevMatrix M = mats[mi];
+    const int64_t local = tile - M.tile_begin;
+    const int64_t band = local / M.n_ctiles, ctile = local % M.n_ctiles;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t r0 = band * kBandRows;
+    const int64_t r1 = r0 + kBandRows < M.rows ? r0 + kBandRows : M.rows;
+    const int64_t c0 = ctile * kTileCols + lane * 8;
+    const int64_t cr = M.cols - c0;
+    const int ncv = cr >= 8 ? 8 : (cr > 0 ? (int)cr : 0);
+    const bool vec = ncv == 8 && (M.cols & 7) == 0;
+    double col[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) col[k] = 0.0;
+    for (int64_t r = r0 + wave; r < r1; r += kWavesPerGroup) {
+        const uint16_t* gp = M.grad + r * M.cols + c0;
+        double d[8];
+        if (vec) {
+            const uint4 q = *reinterpret_cast<const uint4*>(gp);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float a = bf16_to_f32(w[k] & 0xFFFFu), b = bf16_to_f32(w[k] >> 16);
+                d[2 * k] = (double)(a * a);
+                d[2 * k + 1] = (double)(b * b);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float a = k < ncv ? bf16_to_f32(gp[k]) : 0.0f;
+                d[k] = (double)(a * a);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) col[k] += d[k];
+        const double rp = ((d[0] + d[1]) + (d[2] + d[3])) + ((d[4] + d[5]) + (d[6] + d[7]));
+        const double rs = wave_sum_d(rp);
+        if (lane == 0) M.part_row[ctile * M.rows + r] = rs;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) lds[wave][lane * 8 + k] = col[k];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (k < ncv) {
+                const int j = lane * 8 + k;
+                M.part_col[band * M.cols + c0 + k] = ((lds[0][j] + lds[1][j]) + lds[2][j]) + lds[3][j];
+            }
+        }
+    }
+}
+
+// K3a: finalize rows (first total_rgroups groups) and columns (the rest).
+// R_r <- b2 R_r + (1-b2) (row sum / cols), C_c likewise with rows; each row
+// group also leaves the binary64 sum of its updated R for the mean.
+__global__ __launch_bounds__(256) void k_rowcol_finalize(const DevMatrix* __restrict__ mats, int n_mats,
+                                                          int64_t total_rgroups, float beta2, float omb2) {
+    __shared__ double lds[256];
+    const int64_t g = blockIdx.x;
+    if (g < total_rgroups) {
+        const int mi = find_matrix(mats, n_mats, g, 1);
+        const DevMatrix M = mats[mi];
+        const int64_t lg = g - M.rgroup_begin;
+        const int64_t r = lg * kGroup + threadIdx.x;
+        double mine = 0.0;
+        if (r < M.rows) {
+            double rs = 0.0;
+            for (int64_t ct = 0; ct < M.n_ctiles; ++ct) rs += M.part_row[ct * M.rows + r];
+            const float Rn = beta2 * M.R[r] + omb2 * ((float)rs / (float)M.cols);
+            M.R[r] = Rn;
+            mine = (double)Rn;
+        }
+        const double s = group_sum_d(mine, lds);
+        if (threadIdx.x == 0) M.part_mean[lg] = s;
+    } else {
+        const int64_t cg = g - total_rgroups;
+        const int mi = find_matrix(mats, n_mats, cg, 2);
+        const DevMatrix M = mats[mi];
+        const int64_t cidx = (cg - M.cgroup_begin) * kGroup + threadIdx.x;
+        if (cidx < M.cols) {
+            double cs = 0.0;
+            for (int64_t b = 0; b < M.n_bands; ++b) cs += M.part_col[b * M.cols + cidx];
+            M.C[cidx] = beta2 * M.C[cidx] + omb2 * ((float)cs / (float)M.rows);
+        }
+    }
+}
+
+// K3b: one work-group per matrix: mean(R) from the group sums in order.
+__global__ __launch_bounds__(64) void k_rowcol_mean(const DevMatrix* __restrict__ mats) {
+    const DevMatrix M = mats[blockIdx.x];
+    if (threadIdx.x == 0) {
+        double s = 0.0;
+        for (int64_t i = 0; i < M.n_rgroups; ++i) s += M.part_mean[i];
+        const float meanR = (float)(s / (double)M.rows);
+        *M.inv_meanR = meanR > 0.0f ? 1.0f / meanR : 0.0f;
+    }
+}
+
+// Group sums of the stored R (same tree as K3a), for dequantization.
+__global__ __launch_bounds__(256) void k_rsum_groups(const float* __restrict__ R, int64_t rows, double* part) {
+    __shared__ double lds[256];
+    const int64_t r = (int64_t)blockIdx.x * kGroup + threadIdx.x;
+    const double s = group_sum_d(r < rows ? (double)R[r] : 0.0, lds);
+    if (threadIdx.x == 0) part[blockIdx.x] = s;
+}
+__global__ __launch_bounds__(64) void k_rsum_final(const double* __restrict__ part, int64_t n_groups, int64_t rows,
+                                                   float* inv) {
+    if (threadIdx.x == 0) {
+        double s = 0.0;
+        for (int64_t i = 0; i < n_groups; ++i) s += part[i];
+        const float meanR = (float)(s / (double)rows);
+        *inv = meanR > 0.0f ? 1.0f / meanR : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Init fill and dequantization
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_fill(uint8_t* __restrict__ p, size_t bytes, uint8_t value) {
+    const uint32_t w = value * 0x01010101u;
+    const uint4 q = make_uint4(w, w, w, w);
+    const size_t nvec = bytes / 16;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += (size_t)gridDim.x * blockDim.x)
+        reinterpret_cast<uint4*>(p)[i] = q;
+    if (blockIdx.x == 0 && threadIdx.x < bytes - nvec * 16) p[nvec * 16 + threadIdx.x] = value;
+}
+
+template <int MCB, int VCB>
+__global__ __launch_bounds__(256) void k_dequant(DevTensor T, float* __restrict__ m_out, float* __restrict__ v_out,
+                                                  const float* __restrict__ inv_meanR) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T.numel) return;
+    const int64_t blk = i / kBlock;
+    const uint32_t mc = (T.m_codes[i >> 1] >> ((i & 1) * 4)) & 15u;
+    m_out[i] = bits2f(c_decode[MCB][mc]) * T.m_scales[blk];
+    if (T.kind == KIND_PACKED) {
+        const uint32_t vc = (T.v_codes[i >> 1] >> ((i & 1) * 4)) & 15u;
+        v_out[i] = bits2f(c_decode[VCB][vc]) * T.v_scales[blk];
+    } else {
+        const int64_t r = i / T.cols, c = i % T.cols;
+        v_out[i] = (T.v_row[r] * T.v_col[c]) * *inv_meanR;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+
+static int step_grid(int64_t total_chunks) {
+    const int64_t groups = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int64_t cap = 256 * 8;  // 8 resident 256-thread groups per CU
+    return (int)(groups < cap ? (groups > 0 ? groups : 1) : cap);
+}
+
+#define Q4_VARIANTS(X)                                              \
+    X(Q4_CB_NF4, Q4_CB_DYN4, Q4_RULE_UPDATE_SR)    /* ZIP-SR */    \
+    X(Q4_CB_NF4, Q4_CB_DYN4_NZ, Q4_RULE_STATE_RTN) /* ZE-EDEN, factored */ \
+    X(Q4_CB_NF4, Q4_CB_DYN4, Q4_RULE_STATE_RTN)                     \
+    X(Q4_CB_NF4, Q4_CB_DYN4, Q4_RULE_STATE_SR)                      \
+    X(Q4_CB_NF4, Q4_CB_DYN4, Q4_RULE_UPDATE_RTN)                    \
+    X(Q4_CB_SDYN4, Q4_CB_LIN4_NZ, Q4_RULE_STATE_RTN) /* TorchAO-style */ \
+    X(Q4_CB_SDYN4, Q4_CB_DYN4_NZ, Q4_RULE_STATE_RTN)                \
+    X(Q4_CB_SDYN4, Q4_CB_DYN4, Q4_RULE_UPDATE_SR)
+
+bool variant_supported(const Variant& v) {
+#define Q4_MATCH(A, B, C) if (v.mcb == A && v.vcb == B && v.vrule == C) return true;
+    Q4_VARIANTS(Q4_MATCH)
+#undef Q4_MATCH
+    return false;
+}
+
+hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevTensor* d_tab,
+                             const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks, hipStream_t stream) {
+    if (total_chunks <= 0) return hipSuccess;
+    const int grid = step_grid(total_chunks);
+#define Q4_LAUNCH(A, B, C)                                                                              \
+    if (v.mcb == A && v.vcb == B && v.vrule == C) {                                                     \
+        k_fused_step<A, B, C><<<grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, sc); \
+        return hipGetLastError();                                                                       \
+    }
+    Q4_VARIANTS(Q4_LAUNCH)
+#undef Q4_LAUNCH
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_fp32_step(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
+                            int n_tensors, int64_t total_chunks, hipStream_t stream) {
+    if (total_chunks <= 0) return hipSuccess;
+    k_fp32_step<<<step_grid(total_chunks), 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, sc);
+    return hipGetLastError();
+}
+
+hipError_t launch_factored_stats(const DevMatrix* d_mats, int n_mats, int64_t total_tiles, int64_t total_rgroups,
+                                 int64_t total_cgroups, float beta2, float omb2, hipStream_t stream) {
+    if (n_mats <= 0) return hipSuccess;
+    k_rowcol_partial<<<(unsigned)total_tiles, 256, 0, stream>>>(d_mats, n_mats);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_rowcol_finalize<<<(unsigned)(total_rgroups + total_cgroups), 256, 0, stream>>>(d_mats, n_mats, total_rgroups,
+                                                                                     beta2, omb2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_rowcol_mean<<<n_mats, 64, 0, stream>>>(d_mats);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill(void* p, size_t bytes, uint8_t value, hipStream_t stream) {
+    if (bytes == 0) return hipSuccess;
+    size_t nvec = bytes / 16;
+    size_t groups = (nvec + 255) / 256;
+    if (groups < 1) groups = 1;
+    if (groups > 4096) groups = 4096;
+    k_fill<<<(unsigned)groups, 256, 0, stream>>>((uint8_t*)p, bytes, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant(int mcb, int vcb, const DevTensor& t, int64_t rows, float* m_out, float* v_out,
+                          double* ws_partials, float* ws_inv, hipStream_t stream) {
+    if (t.numel == 0) return hipSuccess;
+    if (t.kind == KIND_FACTORED) {
+        const int64_t ng = (rows + kGroup - 1) / kGroup;
+        k_rsum_groups<<<(unsigned)ng, 256, 0, stream>>>(t.v_row, rows, ws_partials);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        k_rsum_final<<<1, 64, 0, stream>>>(ws_partials, ng, rows, ws_inv);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const unsigned grid = (unsigned)((t.numel + 255) / 256);
+#define Q4_DQ(A, B)                                                                       \
+    if (mcb == A && vcb == B) {                                                           \
+        k_dequant<A, B><<<grid, 256, 0, stream>>>(t, m_out, v_out, ws_inv);               \
+        return hipGetLastError();                                                         \
+    }
+    Q4_DQ(Q4_CB_NF4, Q4_CB_DYN4) Q4_DQ(Q4_CB_NF4, Q4_CB_DYN4_NZ) Q4_DQ(Q4_CB_NF4, Q4_CB_LIN4_NZ)
+    Q4_DQ(Q4_CB_SDYN4, Q4_CB_DYN4) Q4_DQ(Q4_CB_SDYN4, Q4_CB_DYN4_NZ) Q4_DQ(Q4_CB_SDYN4, Q4_CB_LIN4_NZ)
+#undef Q4_DQ
+    return hipErrorInvalidValue;
+}
+
+}  // namespace q4

@@ -1,0 +1,215 @@
+"""Host-only checks of the C ABI library: it loads, exports every symbol the
+header declares, and its host logic (validation, workspace and state-byte
+arithmetic, headers, host scalars, codebook tables) behaves as documented.
+No call here launches GPU work."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import bit_adamw_update_amd as q4
+from bit_adamw_update_amd import api, build
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    if not os.path.exists(build.LIB_PATH):
+        build.build(force=False)
+    return api.load_library()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "q4adamw.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4adamw_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    # and the shared object really exports them (dynamic symbol table)
+    out = os.popen(f"nm -D --defined-only {build.LIB_PATH}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_abi_version_and_status_strings():
+    assert q4.q4adamw_abi_version() == 1
+    assert q4.q4adamw_status_string(0) == "ok"
+    assert "workspace" in q4.q4adamw_status_string(7)
+
+
+@pytest.mark.parametrize("cb", range(5))
+def test_library_codebooks_equal_oracle_construction(cb):
+    got = np.array(q4.q4adamw_codebook(cb), np.float32)
+    assert np.array_equal(got.view(np.uint32), O.codebook(cb).view(np.uint32))
+
+
+def test_default_configs_follow_table2():
+    z = q4.q4adamw_default_config(q4.RECIPE_ZIP_SR)
+    assert (z.m_codebook, z.v_codebook, z.m_rule, z.v_rule, z.eden) == (
+        q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_SR, 0)
+    e = q4.q4adamw_default_config(q4.RECIPE_ZE_EDEN)
+    assert (e.m_codebook, e.v_codebook, e.m_rule, e.v_rule, e.eden) == (
+        q4.CB_NF4, q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 1)
+    f = q4.q4adamw_default_config(q4.RECIPE_FACTORED)
+    assert (f.v_codebook, f.v_rule, f.eden) == (q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, 0)
+    assert f.block == 128 and f.abi_version == 1
+
+
+@pytest.mark.parametrize("step", [1, 2, 10, 1000, 123456789])
+def test_host_scalars_equal_oracle_bits(step):
+    for lr, b1, b2, wd in [(1e-3, 0.9, 0.999, 0.1), (6e-4, 0.95, 0.98, 0.0), (2e-4, 0.5, 0.0, 0.01)]:
+        hp = q4.Q4HParams(lr, b1, b2, 1e-8, wd, 0.0, step, 0, 0, 0)
+        got = np.array(q4.q4adamw_host_scalars(hp), np.float32)
+        ref = O.host_scalars(O.HParams(lr=lr, beta1=b1, beta2=b2, weight_decay=wd, step=step))
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+def fake_tensor(shape, tid=0, base=0x10000, fp32=False, factored=False):
+    """Tensor descriptor with fake (never dereferenced) aligned pointers."""
+    t = q4.Q4Tensor()
+    t.tensor_id = tid
+    t.ndim = len(shape)
+    n = 1
+    for d, x in enumerate(shape):
+        t.shape[d] = x
+        n *= x
+    t.numel = n
+    names = ["param", "grad", "m_codes", "m_scales"]
+    if fp32:
+        names += ["m_fp32", "v_fp32"]
+    elif factored:
+        names += ["v_row", "v_col"]
+    else:
+        names += ["v_codes", "v_scales"]
+    for k, nm in enumerate(names):
+        setattr(t, nm, base + 0x1000 * k)
+    return t
+
+
+def hp(**kw):
+    d = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, eps_sr=0.0, step=1, seed=0,
+             lm_head_sr=0, flags=0)
+    d.update(kw)
+    return q4.Q4HParams(*[d[k] for k, _ in q4.Q4HParams._fields_])
+
+
+def status_of(fn, *a):
+    with pytest.raises(q4.Q4Error) as ei:
+        fn(*a)
+    return ei.value.status
+
+
+def test_validation_accepts_good_input():
+    cfg = q4.q4adamw_default_config(q4.RECIPE_ZIP_SR)
+    q4.q4adamw_validate(cfg, hp(), [fake_tensor((256, 512)), fake_tensor((65536,), 1)])
+
+
+def test_validation_errors():
+    cfg = q4.q4adamw_default_config(q4.RECIPE_ZIP_SR)
+    good = fake_tensor((100, 7))
+    V = q4.q4adamw_validate
+    assert status_of(V, cfg, hp(step=0), [good]) == 1
+    assert status_of(V, cfg, hp(beta1=1.0), [good]) == 1
+    assert status_of(V, cfg, hp(beta2=-0.1), [good]) == 1
+    assert status_of(V, cfg, hp(eps=0.0), [good]) == 1
+    assert status_of(V, cfg, hp(lr=float("nan")), [good]) == 1
+    bad = fake_tensor((100, 7)); bad.numel = 701
+    assert status_of(V, cfg, hp(), [bad]) == 2
+    bad = fake_tensor((100, 7)); bad.ndim = 9
+    assert status_of(V, cfg, hp(), [bad]) == 2
+    bad = fake_tensor((1 << 17, 1 << 17))
+    assert status_of(V, cfg, hp(), [bad]) == 2
+    bad = fake_tensor((100, 7)); bad.m_codes = 0x10008
+    assert status_of(V, cfg, hp(), [bad]) == 3
+    bad = fake_tensor((100, 7)); bad.v_scales = None
+    assert status_of(V, cfg, hp(), [bad]) == 1
+    c2 = q4.q4adamw_default_config(q4.RECIPE_ZIP_SR); c2.block = 64
+    assert status_of(V, c2, hp(), [good]) == 1
+    c3 = q4.q4adamw_default_config(q4.RECIPE_ZIP_SR); c3.v_codebook = q4.CB_DYN4_NZ
+    assert status_of(V, c3, hp(), [good]) == 4   # a recipe fixes its codebooks
+    c4 = q4.q4adamw_default_config(q4.RECIPE_CUSTOM); c4.v_codebook = q4.CB_NF4
+    assert status_of(V, c4, hp(), [good]) == 4   # signed map for v
+    c5 = q4.q4adamw_default_config(q4.RECIPE_CUSTOM); c5.m_rule = q4.RULE_UPDATE_SR
+    assert status_of(V, c5, hp(), [good]) == 4
+    assert status_of(V, cfg, hp(), []) == 2
+    # factored matrices need their row/column vectors
+    cf = q4.q4adamw_default_config(q4.RECIPE_FACTORED)
+    q4.q4adamw_validate(cf, hp(), [fake_tensor((64, 32), factored=True), fake_tensor((64,))])
+    assert status_of(V, cf, hp(), [fake_tensor((64, 32))]) == 1
+
+
+def test_step_refuses_before_any_device_work_on_bad_input():
+    """Invalid calls return their status before touching a device."""
+    cfg = q4.q4adamw_default_config(q4.RECIPE_ZE_EDEN)
+    assert status_of(q4.q4adamw_step, cfg, hp(step=0), [fake_tensor((10,))], 0x20000, 4096, 0) == 1
+    bad = fake_tensor((10,)); bad.numel = 11
+    assert status_of(q4.q4adamw_step, cfg, hp(), [bad], 0x20000, 4096, 0) == 2
+
+
+def test_state_bytes_1_0625_per_param():
+    cfg = q4.q4adamw_default_config(q4.RECIPE_ZIP_SR)
+    ts = [fake_tensor((50304, 768)), fake_tensor((768,), 1)]
+    sb = q4.q4adamw_state_bytes(cfg, ts)
+    n = 50304 * 768 + 768
+    assert sb["adam4_total_bytes"] == 1.0625 * n
+    assert sb["adam4_quantized_state_bytes"] == n
+    f32 = q4.q4adamw_state_bytes(q4.q4adamw_default_config(q4.RECIPE_FP32),
+                                 [fake_tensor((50304, 768), fp32=True), fake_tensor((768,), 1, fp32=True)])
+    assert f32["adam4_total_bytes"] == 8 * n
+    assert round(8 / 1.0625, 2) == 7.53
+    # the oracle's count agrees
+    assert O.state_bytes(O.ZIP_SR, n - 768, 50304, True)[2] + O.state_bytes(O.ZIP_SR, 768, 768, False)[2] == \
+        sb["adam4_total_bytes"]
+
+
+def test_state_bytes_factored():
+    cfg = q4.q4adamw_default_config(q4.RECIPE_FACTORED)
+    sb = q4.q4adamw_state_bytes(cfg, [fake_tensor((1024, 2048), factored=True), fake_tensor((1024,), 1)])
+    assert sb["adam4_quantized_state_bytes"] == 1024 * 2048 // 2 + 1024
+    assert sb["adam4_scale_metadata_bytes"] == 4 * (1024 * 2048 // 128) + 4 * (1024 + 2048) + 8 * 8
+
+
+def test_workspace_bytes_monotone():
+    cfg = q4.q4adamw_default_config(q4.RECIPE_FACTORED)
+    a = q4.q4adamw_workspace_bytes(cfg, [fake_tensor((64,))])
+    b = q4.q4adamw_workspace_bytes(cfg, [fake_tensor((1024, 2048), factored=True), fake_tensor((64,), 1)])
+    assert 256 <= a < b and a % 256 == 0 and b % 256 == 0
+
+
+def test_state_header_roundtrip():
+    cfg = q4.q4adamw_default_config(q4.RECIPE_ZIP_SR)
+    h = q4.q4adamw_make_header(cfg)
+    q4.q4adamw_check_header(cfg, h)
+    other = q4.q4adamw_default_config(q4.RECIPE_ZE_EDEN)
+    assert status_of(q4.q4adamw_check_header, other, h) == 5
+    h.layout_version = 0
+    assert status_of(q4.q4adamw_check_header, cfg, h) == 5
+    h2 = q4.q4adamw_make_header(cfg); h2.magic = 0
+    assert status_of(q4.q4adamw_check_header, cfg, h2) == 5
+
+
+def test_product_path_has_no_oracle_dependency():
+    """The package never imports or links the oracle, and fails loudly without
+    its library."""
+    pkg = os.path.join(ROOT, "bit_adamw_update_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h", ".inc")):
+                src = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"(from|import)\s+oracle|q4_oracle|q4oracle|or_step", src), f
+    with pytest.raises(RuntimeError):
+        api._lib_saved = api._lib
+        try:
+            api._lib = None
+            api.load_library(os.path.join(ROOT, "does_not_exist.so"))
+        finally:
+            api._lib = api._lib_saved

@@ -1,0 +1,163 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the CPU oracle on
+the same seeded inputs.  Codes bit-exact (at most 1e-6 of them may differ,
+only at SR ties), scales bit-exact, weights within 1e-6 relative, factored
+R/C within 1e-6 relative."""
+import numpy as np
+import pytest
+import torch
+
+import bit_adamw_update_amd as q4
+from bit_adamw_update_amd import inputs
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+@pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden", "fp32", "factored"])
+def test_tiny_workload_10_steps(recipe):
+    """The tiny check: one 65,536-element vector and one 256x512 matrix,
+    Student-t grads at 1e-3 with a fixed 20% at 1e-9, 10 steps."""
+    w = inputs.tiny()
+    _flush(f"tiny {recipe}")
+    rep = parity.run(w, recipe, 10)
+    rep.check()
+    assert rep.codes_differ == 0 and rep.weights_excluded == 0
+
+
+@pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden", "factored"])
+def test_ragged_shapes(recipe):
+    """Empty-tail and ragged cases: single elements, partial blocks, partial
+    lanes, odd lengths, a single block, factored matrices with odd column
+    counts and columns shorter than a lane."""
+    shapes = [(1,), (127,), (129,), (1000,), (4097,), (128,), (3, 5), (7, 129), (300, 3), (2, 1031), (64, 520)]
+    w = inputs.custom(shapes, grad_kind="masked", seed=21)
+    _flush(f"ragged {recipe}")
+    rep = parity.run(w, recipe, 5)
+    rep.check()
+    assert rep.codes_differ == 0
+
+
+@pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden"])
+def test_zero_gradient_blocks(recipe):
+    """A tensor whose gradient is exactly zero: scales stay 0, codes stay at
+    the code of zero, weights only decay."""
+    w = inputs.custom([(512,), (1000,)], grad_kind="masked", seed=22)
+    orig = w.grads
+    w.grads = lambda step, device="cpu", consts=None: [g * (0 if i == 0 else 1) for i, g in
+                                                       enumerate(orig(step, device, consts))]
+    rep = parity.run(w, recipe, 3)
+    rep.check()
+
+
+def test_lm_head_switch_final_phase():
+    """ZIP-SR with the LM-head first moment switching to NF4-SR in the final
+    10% of 10 steps (step 10 only)."""
+    w = inputs.custom([(4096,), (64, 128), (32, 64)], grad_kind="masked", seed=23,
+                      flags=[0, 0, q4.TF_LM_HEAD])
+    rep = parity.run(w, "zip_sr", 10, lm_head_phase=True)
+    rep.check()
+    assert rep.codes_differ == 0
+
+
+@pytest.mark.parametrize("variant", [
+    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 0),
+    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_STATE_SR, 0),
+    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_RTN, 0),
+    (q4.CB_NF4, q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 0),
+    (q4.CB_SDYN4, q4.CB_LIN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 0),
+    (q4.CB_SDYN4, q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 1),
+    (q4.CB_SDYN4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_SR, 0),
+    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_SR, q4.RULE_UPDATE_SR, 0),
+])
+def test_rule_and_codebook_variants(variant):
+    """The component grid of the paper's Tables 1, 3 and 8 on the same kernel."""
+    cfg = q4.q4adamw_default_config(q4.RECIPE_CUSTOM)
+    cfg.m_codebook, cfg.v_codebook, cfg.m_rule, cfg.v_rule, cfg.eden = variant
+    w = inputs.custom([(3000,), (40, 300)], grad_kind="masked", seed=24)
+    rep = parity.run(w, "custom", 6, cfg=cfg)
+    rep.check()
+    assert rep.codes_differ == 0
+
+
+def test_determinism_and_resume():
+    """Two runs are bitwise equal; 3 steps, a state copy into fresh buffers,
+    then 3 more steps equals 6 straight steps (the uniforms are keyed on the
+    step, so resuming is exact)."""
+    w = inputs.custom([(5000,), (64, 96)], grad_kind="masked", seed=25)
+    dev = torch.device("cuda")
+    consts = w._tensor_consts("cpu")
+    grads = [[g.to(dev).reshape(-1).contiguous() for g in w.grads(s, "cpu", consts)] for s in range(1, 7)]
+
+    def fresh():
+        return [p.to(dev).reshape(-1).contiguous() for p in w.init_params("cpu")], q4.Q4State("zip_sr", w.tensors, dev)
+
+    pa, sa = fresh()
+    for s in range(1, 7):
+        sa.step(pa, grads[s - 1], s, **w.hp)
+    pb, sb = fresh()
+    for s in range(1, 7):
+        sb.step(pb, grads[s - 1], s, **w.hp)
+    pc, sc = fresh()
+    for s in range(1, 4):
+        sc.step(pc, grads[s - 1], s, **w.hp)
+    torch.cuda.synchronize()
+    saved = [{f: getattr(b, f).clone() for f in ("m_codes", "m_scales", "v_codes", "v_scales")} for b in sc.bufs]
+    hdr = q4.q4adamw_make_header(sc.cfg)
+    _, sd = fresh()
+    q4.q4adamw_check_header(sd.cfg, hdr)
+    for b, s in zip(sd.bufs, saved):
+        for f, x in s.items():
+            getattr(b, f).copy_(x)
+    for s in range(4, 7):
+        sd.step(pc, grads[s - 1], s, **w.hp)
+    torch.cuda.synchronize()
+    for x, y, z in zip(pa, pb, pc):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+        assert torch.equal(x.view(torch.int32), z.view(torch.int32))
+    for a, b, d in zip(sa.bufs, sb.bufs, sd.bufs):
+        for f in ("m_codes", "m_scales", "v_codes", "v_scales"):
+            assert torch.equal(getattr(a, f), getattr(b, f))
+            assert torch.equal(getattr(a, f), getattr(d, f))
+
+
+@pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden", "factored"])
+def test_dequant_matches_oracle(recipe):
+    w = inputs.custom([(3000,), (48, 200)], grad_kind="masked", seed=26)
+    dev = torch.device("cuda")
+    from oracle import oracle as O
+    params = w.init_params("cpu")
+    consts = w._tensor_consts("cpu")
+    gp = [p.to(dev).reshape(-1).contiguous() for p in params]
+    st = q4.Q4State(recipe, w.tensors, dev)
+    ost = [O.TensorState(parity.oracle_config(recipe), t.shape, t.tensor_id) for t in w.tensors]
+    op = [p.numpy().reshape(-1).copy() for p in params]
+    for s in range(1, 4):
+        g = w.grads(s, "cpu", consts)
+        st.step(gp, [x.to(dev).reshape(-1).contiguous() for x in g], s, **w.hp)
+        for i, o in enumerate(ost):
+            o.step(O.HParams(step=s, **w.hp), op[i], g[i].view(torch.uint16).numpy().reshape(-1).copy())
+    for i, o in enumerate(ost):
+        m, v = st.dequant(i)
+        torch.cuda.synchronize()
+        om, ov = o.dequant()
+        assert np.array_equal(m.cpu().numpy().view(np.uint32), om.view(np.uint32))
+        if recipe == "factored" and len(w.tensors[i].shape) > 1:
+            assert np.allclose(v.cpu().numpy(), ov, rtol=1e-6, atol=0)
+        else:
+            assert np.array_equal(v.cpu().numpy().view(np.uint32), ov.view(np.uint32))
+
+
+def test_gpt_162m_sampled_20_steps():
+    """GPT-style 162M parameter set (tied embedding as written: 123.6M), both
+    recipes, 20 steps, compared on windows: the first and last blocks of every
+    tensor and random interior windows."""
+    w = inputs.gpt_162m()
+    wins = parity.sample_windows(w, n_random=32)
+    for recipe in ("zip_sr", "ze_eden"):
+        _flush(f"gpt-162m {recipe}")
+        rep = parity.run(w, recipe, 20, windows=wins, grads_on="cuda", check_every_step=False)
+        rep.check()
