@@ -109,6 +109,8 @@ def _check(status: int) -> None:
 def _tensors(ts):
     if isinstance(ts, Q4Tensor):
         return C.pointer(ts), 1
+    if isinstance(ts, C.Array):
+        return ts, len(ts)
     arr = (Q4Tensor * len(ts))(*ts)
     return arr, len(ts)
 

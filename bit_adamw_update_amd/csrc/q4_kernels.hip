@@ -171,283 +171,425 @@ __device__ __forceinline__ float bperm(float v, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// Per-lane element I/O (8 consecutive elements starting at e0)
+// Global-memory views
 // ---------------------------------------------------------------------------
 
-struct Lane8 {
-    float p[8];
-    float g[8];
-    uint32_t mc, vc;  // 8 nibbles each, element k at bits 4k..4k+3
+// Pointers read from the tensor table are generic; viewing them in the
+// global address space lets the compiler issue global_load/global_store
+// rather than flat instructions (which also occupy the LDS wait counter).
+template <class T> using gptr = __attribute__((address_space(1))) T*;
+template <class T> __device__ __forceinline__ gptr<T> G(T* p) { return (gptr<T>)p; }
+template <class T> __device__ __forceinline__ gptr<const T> G(const T* p) { return (gptr<const T>)p; }
+// clang vector types copy in any address space (HIP's float4 does not)
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Round-to-nearest by bucket table
+// ---------------------------------------------------------------------------
+//
+// The RTN index of x is the number of FP32 midpoints strictly below x.
+// Buckets split |x| by its binary exponent and MB leading mantissa bits;
+// every bucket holds at most one midpoint (checked at compile time), so one
+// table entry {thr, base, level(base), level(base+1)} gives the exact count:
+// index = base + (x > thr).  A bucket of a negative x covers (-hi, -lo], one
+// of a positive x [lo, hi); magnitudes below 2^(EMIN-127) share bucket 0.
+
+struct alignas(16) BucketEntry {
+    float thr;     // the one midpoint inside the bucket, or 3 (never exceeded)
+    int32_t base;  // midpoints below every x of the bucket
+    float lv0;     // level(base)
+    float lv1;     // level(min(base + 1, N - 1))
 };
 
-__device__ __forceinline__ void load8(const DevTensor& T, int64_t e0, int nv, bool packed_v, Lane8& L) {
-    if (nv == 8) {
-        const float4 a = *reinterpret_cast<const float4*>(T.param + e0);
-        const float4 b = *reinterpret_cast<const float4*>(T.param + e0 + 4);
-        L.p[0] = a.x; L.p[1] = a.y; L.p[2] = a.z; L.p[3] = a.w;
-        L.p[4] = b.x; L.p[5] = b.y; L.p[6] = b.z; L.p[7] = b.w;
-        const uint4 gq = *reinterpret_cast<const uint4*>(T.grad + e0);
-        L.g[0] = bf16_to_f32(gq.x & 0xFFFFu); L.g[1] = bf16_to_f32(gq.x >> 16);
-        L.g[2] = bf16_to_f32(gq.y & 0xFFFFu); L.g[3] = bf16_to_f32(gq.y >> 16);
-        L.g[4] = bf16_to_f32(gq.z & 0xFFFFu); L.g[5] = bf16_to_f32(gq.z >> 16);
-        L.g[6] = bf16_to_f32(gq.w & 0xFFFFu); L.g[7] = bf16_to_f32(gq.w >> 16);
-        L.mc = *reinterpret_cast<const uint32_t*>(T.m_codes + (e0 >> 1));
-        L.vc = packed_v ? *reinterpret_cast<const uint32_t*>(T.v_codes + (e0 >> 1)) : 0u;
-    } else {
-        L.mc = 0; L.vc = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            L.p[k] = k < nv ? T.param[e0 + k] : 0.0f;
-            L.g[k] = k < nv ? bf16_to_f32(T.grad[e0 + k]) : 0.0f;
+__host__ __device__ constexpr uint32_t f2bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+template <int CB> struct Enc {
+    static constexpr int MB = 3;
+    static constexpr bool SIGNED = CB == Q4_CB_NF4 || CB == Q4_CB_SDYN4;
+    static constexpr int N = Book<CB>::N;
+    static constexpr int min_mid_exp() {
+        int e = 255;
+        for (int k = 0; k + 1 < N; ++k) {
+            const int ek = (int)((f2bits(Book<CB>::mid(k)) >> 23) & 0xFF);
+            if (ek < e) e = ek;
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (2 * j < nv) {
-                L.mc |= (uint32_t)T.m_codes[(e0 >> 1) + j] << (8 * j);
-                if (packed_v) L.vc |= (uint32_t)T.v_codes[(e0 >> 1) + j] << (8 * j);
+        return e;
+    }
+    // bucket 0 ends at 2^(EMIN-127) * 1.125, below every midpoint magnitude
+    static constexpr int EMIN = min_mid_exp() - 1;
+    static constexpr int NPOS = ((127 - EMIN) << MB) + 1;
+    static constexpr int pow2ceil(int v) { int p = 1; while (p < v) p <<= 1; return p; }
+    static constexpr int PAD = pow2ceil(NPOS);
+    static constexpr int SIZE = SIGNED ? 2 * PAD : NPOS;
+};
+
+template <int CB> struct EncTable {
+    BucketEntry e[Enc<CB>::SIZE];
+    bool ok;
+    constexpr EncTable() : e(), ok(true) {
+        using E = Enc<CB>;
+        for (int s = 0; s < (E::SIGNED ? 2 : 1); ++s) {
+            for (int b = 0; b < (E::SIGNED ? E::PAD : E::NPOS); ++b) {
+                const int bb = b < E::NPOS ? b : E::NPOS - 1;  // padding repeats the last bucket
+                const float lo = bb == 0 ? 0.0f : bits2f((uint32_t)((E::EMIN << E::MB) + bb) << (23 - E::MB));
+                const float hi = bits2f((uint32_t)((E::EMIN << E::MB) + bb + 1) << (23 - E::MB));
+                int base = 0, inside = 0;
+                float thr = 3.0f;
+                for (int k = 0; k + 1 < E::N; ++k) {
+                    const float m = Book<CB>::mid(k);
+                    if (s == 0) {          // x in [lo, hi)
+                        if (m < lo) ++base;
+                        else if (m < hi) { ++inside; thr = m; }
+                    } else {               // x in (-hi, -lo]
+                        if (m <= -hi) ++base;
+                        else if (m <= -lo) { ++inside; thr = m; }
+                    }
+                }
+                if (inside > 1) ok = false;
+                BucketEntry& d = e[s * E::PAD + b];
+                d.thr = thr;
+                d.base = base;
+                d.lv0 = Book<CB>::level(base);
+                d.lv1 = Book<CB>::level(base + 1 < E::N ? base + 1 : E::N - 1);
             }
         }
     }
+};
+
+static_assert(EncTable<Q4_CB_NF4>().ok && EncTable<Q4_CB_SDYN4>().ok && EncTable<Q4_CB_DYN4>().ok &&
+                  EncTable<Q4_CB_DYN4_NZ>().ok && EncTable<Q4_CB_LIN4_NZ>().ok,
+              "a bucket holds two midpoints: use more mantissa bits");
+
+__constant__ EncTable<Q4_CB_NF4> c_enc_nf4 = EncTable<Q4_CB_NF4>();
+__constant__ EncTable<Q4_CB_SDYN4> c_enc_sdyn4 = EncTable<Q4_CB_SDYN4>();
+__constant__ EncTable<Q4_CB_DYN4> c_enc_dyn4 = EncTable<Q4_CB_DYN4>();
+__constant__ EncTable<Q4_CB_DYN4_NZ> c_enc_dyn4nz = EncTable<Q4_CB_DYN4_NZ>();
+__constant__ EncTable<Q4_CB_LIN4_NZ> c_enc_lin4nz = EncTable<Q4_CB_LIN4_NZ>();
+
+template <int CB> __device__ __forceinline__ const BucketEntry* enc_table_global() {
+    if constexpr (CB == Q4_CB_NF4) return c_enc_nf4.e;
+    else if constexpr (CB == Q4_CB_SDYN4) return c_enc_sdyn4.e;
+    else if constexpr (CB == Q4_CB_DYN4) return c_enc_dyn4.e;
+    else if constexpr (CB == Q4_CB_DYN4_NZ) return c_enc_dyn4nz.e;
+    else return c_enc_lin4nz.e;
 }
 
-__device__ __forceinline__ void store_params8(const DevTensor& T, int64_t e0, int nv, const float* p) {
-    if (nv == 8) {
-        *reinterpret_cast<float4*>(T.param + e0) = make_float4(p[0], p[1], p[2], p[3]);
-        *reinterpret_cast<float4*>(T.param + e0 + 4) = make_float4(p[4], p[5], p[6], p[7]);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (k < nv) T.param[e0 + k] = p[k];
-    }
-}
-
-__device__ __forceinline__ void store_codes8(uint8_t* codes, int64_t e0, int nv, uint32_t word) {
-    if (nv == 8) {
-        *reinterpret_cast<uint32_t*>(codes + (e0 >> 1)) = word;
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (2 * j < nv) codes[(e0 >> 1) + j] = (uint8_t)(word >> (8 * j));
-    }
+// The bucket entry of x (LDS table).  NaN or |x| > 1 land in the last
+// bucket, so the index never leaves the table.
+template <int CB>
+__device__ __forceinline__ const BucketEntry& bucket_of(const BucketEntry* tab, float x) {
+    using E = Enc<CB>;
+    const uint32_t u = __float_as_uint(x);
+    uint32_t raw = __builtin_amdgcn_ubfe(u, 23 - E::MB, 8 + E::MB);
+    raw = raw < (uint32_t)(E::EMIN << E::MB) ? (uint32_t)(E::EMIN << E::MB) : raw;
+    raw = raw > (uint32_t)(127 << E::MB) ? (uint32_t)(127 << E::MB) : raw;
+    uint32_t idx = raw - (uint32_t)(E::EMIN << E::MB);
+    if constexpr (E::SIGNED) idx += (u >> 31) * (uint32_t)E::PAD;
+    return tab[idx];
 }
 
 // ---------------------------------------------------------------------------
 // K1: the fused step for packed and factored tensors
 // ---------------------------------------------------------------------------
 
-// Tables in LDS: decode by code, and the sorted levels (for SR brackets and
-// the EDEN inner product).
-struct BookLds {
-    float dec_m[16], dec_v[16], lev_m[16], lev_v[16];
+template <int MCB, int VCB> struct StepLds {
+    BucketEntry enc_m[Enc<MCB>::SIZE];
+    BucketEntry enc_v[Enc<VCB>::SIZE];
+    float lev_m[16], lev_v[16];  // sorted levels (rare SR paths)
 };
 
-template <int MCB, int VCB>
-__device__ __forceinline__ void fill_books(BookLds& b) {
-    const int t = threadIdx.x;
-    if (t < 16) {
-        b.dec_m[t] = bits2f(c_decode[MCB][t]);
-        b.dec_v[t] = bits2f(c_decode[VCB][t]);
-        b.lev_m[t] = t < Book<MCB>::N ? sorted_level_rt<MCB>(t) : 1.0f;
-        b.lev_v[t] = t < Book<VCB>::N ? sorted_level_rt<VCB>(t) : 1.0f;
-    }
-}
+// Per-lane constants of the codebooks: lane `sub` of each 16-lane row holds
+// the code-`sub` level of each map (decode) and the sorted level `sub` of v.
+struct LaneBooks {
+    float dec_m, dec_v, lev_v;
+};
 
-// State-space SR bracket from the RTN index c of x: the lower level is c or
-// c - 1 (the FP32 midpoints lie strictly inside their cells); x below the
-// first level (zero-excluding maps only) stays at index 0; an exact level
-// hit or the top level needs no draw.
-template <int N>
-__device__ __forceinline__ void sr_bracket(const float* lev, float x, int c, int& lo, float& Llo, float& Lhi,
-                                           bool& can_move) {
-    const float Lc = lev[c];
-    const bool below = x < Lc;
-    lo = below ? (c > 0 ? c - 1 : 0) : c;
-    Llo = lev[lo];
-    const int hi = lo + 1 < N ? lo + 1 : N - 1;
-    Lhi = lev[hi];
-    can_move = !(below && c == 0) && !(Llo == x) && (lo != N - 1);
+template <int MCB, int VCB, int VRULE, bool FULL>
+__device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc, const int64_t chunk,
+                                           const StepScalars& sc, const StepLds<MCB, VCB>& lds,
+                                           const LaneBooks& lb, const int lane) {
+    constexpr int NM = Book<MCB>::N, NV = Book<VCB>::N;
+    constexpr bool V_SR = VRULE == Q4_RULE_STATE_SR || VRULE == Q4_RULE_UPDATE_SR;
+    constexpr bool V_UPD = VRULE == Q4_RULE_UPDATE_SR || VRULE == Q4_RULE_UPDATE_RTN;
+    const int sub = lane & 15, row_base = lane & 48;
+    const int64_t n = T.numel;
+    const int64_t blk = lc * kBlocksPerChunk + (lane >> 4);
+    const int64_t e0 = blk * kBlock + sub * 8;
+    int nv = 8;
+    bool blk_ok = true;
+    if (!FULL) {
+        const int64_t rem = n - e0;
+        nv = rem >= 8 ? 8 : (rem > 0 ? (int)rem : 0);
+        blk_ok = blk * kBlock < n;
+    }
+    const bool packed_v = T.kind == KIND_PACKED;
+    const gptr<float> param = G(T.param);
+    const gptr<const uint16_t> grad = G(T.grad);
+    const gptr<uint8_t> mcodes = G(T.m_codes);
+    const gptr<uint8_t> vcodes = G(T.v_codes);
+    const gptr<float> mscales = G(T.m_scales);
+    const gptr<float> vscales = G(T.v_scales);
+
+    // ---- loads
+    float p[8], g[8];
+    uint32_t mc = 0, vc = 0;
+    if (FULL || nv == 8) {
+        const f32x4 a = *reinterpret_cast<const gptr<const f32x4>>(param + e0);
+        const f32x4 b = *reinterpret_cast<const gptr<const f32x4>>(param + e0 + 4);
+        p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
+        const u32x4 gq = *reinterpret_cast<const gptr<const u32x4>>(grad + e0);
+        g[0] = bf16_to_f32(gq.x & 0xFFFFu); g[1] = bf16_to_f32(gq.x >> 16);
+        g[2] = bf16_to_f32(gq.y & 0xFFFFu); g[3] = bf16_to_f32(gq.y >> 16);
+        g[4] = bf16_to_f32(gq.z & 0xFFFFu); g[5] = bf16_to_f32(gq.z >> 16);
+        g[6] = bf16_to_f32(gq.w & 0xFFFFu); g[7] = bf16_to_f32(gq.w >> 16);
+        mc = *reinterpret_cast<const gptr<const uint32_t>>(mcodes + (e0 >> 1));
+        if (packed_v) vc = *reinterpret_cast<const gptr<const uint32_t>>(vcodes + (e0 >> 1));
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            p[k] = k < nv ? param[e0 + k] : 0.0f;
+            g[k] = k < nv ? bf16_to_f32(grad[e0 + k]) : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (2 * j < nv) {
+                mc |= (uint32_t)mcodes[(e0 >> 1) + j] << (8 * j);
+                if (packed_v) vc |= (uint32_t)vcodes[(e0 >> 1) + j] << (8 * j);
+            }
+        }
+    }
+    const float sm_old = (FULL || blk_ok) ? mscales[blk] : 0.0f;
+    const float sv_old = ((FULL || blk_ok) && packed_v) ? vscales[blk] : 0.0f;
+    // lane `sub` of the row holds level(sub) * old scale: decoding is one
+    // ds_bpermute per element (the same product the definition forms)
+    const float dm_own = lb.dec_m * sm_old;
+    const float dv_own = lb.dec_v * sv_old;
+
+    // ---- factored second moment: v1 = (R_r C_c) / mean(R) over [rows, cols]
+    float vf[8];
+    if (!packed_v) {
+        const float inv_mean = *T.inv_meanR;
+        const gptr<const float> R = G((const float*)T.v_row);
+        const gptr<const float> Cv = G((const float*)T.v_col);
+        // row of the chunk's first element (wave-uniform), then a 32-bit
+        // division for the lane's offset (cols < 2^31 is validated)
+        const uint32_t cols = (uint32_t)T.cols;
+        const int64_t rb = (lc * kChunkElems) / T.cols;
+        const uint32_t off = (uint32_t)(e0 - rb * T.cols);
+        const uint32_t dr = off / cols;
+        uint32_t cc = off - dr * cols;
+        int64_t rr = rb + dr;
+        if ((FULL || nv == 8) && cc + 8u <= cols && (cc & 3u) == 0u) {
+            const float Rr = R[rr];
+            const f32x4 a = *reinterpret_cast<const gptr<const f32x4>>(Cv + cc);
+            const f32x4 b = *reinterpret_cast<const gptr<const f32x4>>(Cv + cc + 4);
+            const float cv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int k = 0; k < 8; ++k) vf[k] = (Rr * cv[k]) * inv_mean;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                vf[k] = 0.0f;
+                if (k < nv) {
+                    vf[k] = (R[rr] * Cv[cc]) * inv_mean;
+                    if (++cc == cols) { cc = 0; ++rr; }
+                }
+            }
+        }
+    }
+
+    // ---- AdamW on the unquantized moments
+    float m1[8], v1[8], sv[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float gk = g[k];
+        const float m0 = bperm(dm_own, row_base + (int)((mc >> (4 * k)) & 15u));
+        const float mm = sc.beta1 * m0 + sc.omb1 * gk;
+        float vv;
+        if (packed_v) {
+            const float v0 = bperm(dv_own, row_base + (int)((vc >> (4 * k)) & 15u));
+            vv = sc.beta2 * v0 + sc.omb2 * (gk * gk);
+        } else {
+            vv = vf[k];
+        }
+        const float s = sqrtf(vv);
+        const float denom = s * sc.rsbc2 + sc.eps;
+        p[k] = p[k] * sc.decay - sc.step_size * (mm / denom);
+        if (FULL) {
+            m1[k] = mm;
+            v1[k] = vv;
+        } else {
+            m1[k] = k < nv ? mm : 0.0f;
+            v1[k] = k < nv ? vv : 0.0f;
+        }
+        sv[k] = s;
+    }
+    if (FULL || nv == 8) {
+        *reinterpret_cast<gptr<f32x4>>(param + e0) = f32x4{p[0], p[1], p[2], p[3]};
+        *reinterpret_cast<gptr<f32x4>>(param + e0 + 4) = f32x4{p[4], p[5], p[6], p[7]};
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (k < nv) param[e0 + k] = p[k];
+    }
+
+    // ---- first moment: absmax scale of the block, RTN or state-space SR
+    float am = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(m1[k]));
+    const float s_m = row_max16(am);
+    const float inv_m = s_m > 0.0f ? 1.0f / s_m : 0.0f;
+    const bool m_sr = sc.m_sr_all || ((T.flags & Q4_TF_LM_HEAD) && sc.lm_head_sr);
+    uint32_t mword = 0;
+    if (!m_sr) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float x = fminf(fmaxf(m1[k] * inv_m, -1.0f), 1.0f);
+            const BucketEntry& e = bucket_of<MCB>(lds.enc_m, x);
+            const int idx = e.base + (x > e.thr ? 1 : 0);
+            const int code = MCB == Q4_CB_SDYN4 ? (idx < 7 ? 15 - idx : (idx == 7 ? 0 : idx - 7)) : idx;
+            mword |= (uint32_t)code << (4 * k);
+        }
+    } else {
+        float um[8];
+        uniforms8((uint64_t)e0, sc.step, T.tensor_id, 0u, sc.key0, sc.key1, um);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float x = fminf(fmaxf(m1[k] * inv_m, -1.0f), 1.0f);
+            const BucketEntry& e = bucket_of<MCB>(lds.enc_m, x);
+            const bool gt = x > e.thr;
+            const int idx = e.base + (gt ? 1 : 0);
+            const float Lidx = gt ? e.lv1 : e.lv0;
+            // the lower level is idx or idx - 1; an exact hit or the top level stays
+            const bool below = x < Lidx;
+            const int lo = below ? (idx > 0 ? idx - 1 : 0) : idx;
+            const int hi = lo + 1 < NM ? lo + 1 : NM - 1;
+            const float Llo = lds.lev_m[lo], Lhi = lds.lev_m[hi];
+            const bool mv = !(below && idx == 0) && !(x == Lidx) && lo != NM - 1;
+            const int fin = lo + ((mv && um[k] * (Lhi - Llo) < (x - Llo)) ? 1 : 0);
+            const int code = MCB == Q4_CB_SDYN4 ? (fin < 7 ? 15 - fin : (fin == 7 ? 0 : fin - 7)) : fin;
+            mword |= (uint32_t)code << (4 * k);
+        }
+    }
+    if (FULL || nv == 8) {
+        *reinterpret_cast<gptr<uint32_t>>(mcodes + (e0 >> 1)) = mword;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (2 * j < nv) mcodes[(e0 >> 1) + j] = (uint8_t)(mword >> (8 * j));
+    }
+    if ((FULL || blk_ok) && sub == 0) mscales[blk] = s_m;
+
+    if (!packed_v) return;
+
+    // ---- second moment: max scale, the v rule, EDEN
+    float av = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) av = fmaxf(av, v1[k]);
+    const float s_v = row_max16(av);
+    const float inv_v = s_v > 0.0f ? 1.0f / s_v : 0.0f;
+    // lane `sub` holds sqrt(level_sub * s_v): the square root of the state
+    // each level would store, for the preconditioner-space rules
+    const float root_own = V_UPD ? sqrtf(lb.lev_v * s_v) : 0.0f;
+    float uv[8];
+    if (V_SR) uniforms8((uint64_t)e0, sc.step, T.tensor_id, 1u, sc.key0, sc.key1, uv);
+    uint32_t vword = 0;
+    float xx[8], xq[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float x = fminf(v1[k] * inv_v, 1.0f);
+        const BucketEntry& e = bucket_of<VCB>(lds.enc_v, x);
+        const bool gt = x > e.thr;
+        int idx = e.base + (gt ? 1 : 0);
+        float q = gt ? e.lv1 : e.lv0;  // level(idx)
+        if constexpr (VRULE != Q4_RULE_STATE_RTN) {
+            const float Lidx = q;
+            const bool below = x < Lidx;
+            const int lo = below ? (idx > 0 ? idx - 1 : 0) : idx;
+            const int hi = lo + 1 < NV ? lo + 1 : NV - 1;
+            const bool mv = !(below && idx == 0) && !(x == Lidx) && lo != NV - 1;
+            bool up;
+            if constexpr (VRULE == Q4_RULE_STATE_SR) {
+                const float Llo = lds.lev_v[lo], Lhi = lds.lev_v[hi];
+                up = uv[k] * (Lhi - Llo) < (x - Llo);
+            } else {
+                const float rlo = bperm(root_own, row_base + lo);
+                const float rhi = bperm(root_own, row_base + hi);
+                if constexpr (VRULE == Q4_RULE_UPDATE_SR) {
+                    // P(up) = (r(a_lo) - r(v)) / (r(a_lo) - r(a_hi)), r(a) = 1/(sqrt(a) + eps_sr),
+                    // multiplied out so that nothing cancels next to a_lo = 0
+                    const float num = (sv[k] - rlo) * (rhi + sc.eps_sr);
+                    const float den = (rhi - rlo) * (sv[k] + sc.eps_sr);
+                    up = uv[k] * den < num;
+                } else {
+                    // nearer level in r: r(v) - r(a_hi) < r(a_lo) - r(v)
+                    const float left = (rhi - sv[k]) * (rlo + sc.eps_sr);
+                    const float right = (sv[k] - rlo) * (rhi + sc.eps_sr);
+                    up = left < right;
+                }
+            }
+            idx = lo + ((mv && up) ? 1 : 0);
+            if (sc.eden) q = lds.lev_v[idx];
+        }
+        vword |= (uint32_t)idx << (4 * k);
+        xx[k] = x * x;
+        xq[k] = x * q;
+    }
+    if (FULL || nv == 8) {
+        *reinterpret_cast<gptr<uint32_t>>(vcodes + (e0 >> 1)) = vword;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (2 * j < nv) vcodes[(e0 >> 1) + j] = (uint8_t)(vword >> (8 * j));
+    }
+    float stored = s_v;
+    if (sc.eden) {
+        // EDEN: S = <x,x> / <x,Q(x)> over the block, pairwise tree in index order
+        const float sxx = row_sum16(tree8(xx));
+        const float sxq = row_sum16(tree8(xq));
+        const float S = sxq > 0.0f ? sxx / sxq : 1.0f;
+        stored = s_v * S;
+    }
+    if ((FULL || blk_ok) && sub == 0) vscales[blk] = stored;
 }
 
 template <int MCB, int VCB, int VRULE>
 __global__ __launch_bounds__(256) void k_fused_step(const DevTensor* __restrict__ tab,
                                                      const int64_t* __restrict__ chunk_begin, int n_tensors,
                                                      int64_t total_chunks, StepScalars sc) {
-    __shared__ BookLds books;
-    fill_books<MCB, VCB>(books);
+    __shared__ StepLds<MCB, VCB> lds;
+    {
+        // stage the bucket tables and sorted levels in LDS
+        const BucketEntry* gm = enc_table_global<MCB>();
+        const BucketEntry* gv = enc_table_global<VCB>();
+        for (int i = threadIdx.x; i < Enc<MCB>::SIZE; i += blockDim.x) lds.enc_m[i] = gm[i];
+        for (int i = threadIdx.x; i < Enc<VCB>::SIZE; i += blockDim.x) lds.enc_v[i] = gv[i];
+        if (threadIdx.x < 16) {
+            const int t = threadIdx.x;
+            lds.lev_m[t] = t < Book<MCB>::N ? sorted_level_rt<MCB>(t) : 1.0f;
+            lds.lev_v[t] = t < Book<VCB>::N ? sorted_level_rt<VCB>(t) : 1.0f;
+        }
+    }
+    const int lane = threadIdx.x & 63;
+    const int sub = lane & 15;
+    LaneBooks lb;
+    lb.dec_m = bits2f(c_decode[MCB][sub]);
+    lb.dec_v = bits2f(c_decode[VCB][sub]);
+    lb.lev_v = sub < Book<VCB>::N ? sorted_level_rt<VCB>(sub) : 1.0f;
     __syncthreads();
 
-    constexpr int NM = Book<MCB>::N, NV = Book<VCB>::N;
-    constexpr bool V_SR = VRULE == Q4_RULE_STATE_SR || VRULE == Q4_RULE_UPDATE_SR;
-    constexpr bool V_UPD = VRULE == Q4_RULE_UPDATE_SR || VRULE == Q4_RULE_UPDATE_RTN;
-
-    const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int row = lane >> 4, sub = lane & 15;
-    const int row_base = row << 4;
-
     int t = 0;
     for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks;
          c += (int64_t)gridDim.x * kWavesPerGroup) {
         while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
         const DevTensor T = tab[t];
-        const int64_t n = T.numel;
-        const int64_t blk = (c - T.chunk_begin) * kBlocksPerChunk + row;
-        const int64_t e0 = blk * kBlock + sub * 8;
-        const int64_t rem = n - e0;
-        const int nv = rem >= 8 ? 8 : (rem > 0 ? (int)rem : 0);
-        const bool blk_ok = blk * kBlock < n;
-        const bool packed_v = T.kind == KIND_PACKED;
-
-        Lane8 L;
-        if (nv > 0) {
-            load8(T, e0, nv, packed_v, L);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) { L.p[k] = 0.0f; L.g[k] = 0.0f; }
-            L.mc = 0; L.vc = 0;
-        }
-        const float sm_old = blk_ok ? T.m_scales[blk] : 0.0f;
-        const float sv_old = (blk_ok && packed_v) ? T.v_scales[blk] : 0.0f;
-
-        // factored second moment: v1 = (R_r C_c) / mean(R), row-major [rows, cols]
-        float vf[8];
-        if (!packed_v) {
-            const float inv_mean = *T.inv_meanR;
-            // row of the chunk's first element (wave-uniform), then a 32-bit
-            // division for the lane's offset (cols < 2^31 is validated)
-            const uint32_t cols = (uint32_t)T.cols;
-            const int64_t ce0 = (c - T.chunk_begin) * kChunkElems;
-            const int64_t rb = ce0 / T.cols;
-            const uint32_t off = (uint32_t)(e0 - rb * T.cols);
-            const uint32_t dr = off / cols;
-            uint32_t cc = off - dr * cols;
-            int64_t rr = rb + dr;
-            if (nv == 8 && cc + 8u <= cols && (cc & 3u) == 0u) {
-                const float Rr = T.v_row[rr];
-                const float4 a = *reinterpret_cast<const float4*>(T.v_col + cc);
-                const float4 b = *reinterpret_cast<const float4*>(T.v_col + cc + 4);
-                const float cv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-                for (int k = 0; k < 8; ++k) vf[k] = (Rr * cv[k]) * inv_mean;
-            } else {
-#pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    vf[k] = 0.0f;
-                    if (k < nv) {
-                        vf[k] = (T.v_row[rr] * T.v_col[cc]) * inv_mean;
-                        if (++cc == cols) { cc = 0; ++rr; }
-                    }
-                }
-            }
-        }
-
-        // AdamW on the unquantized moments
-        float m1[8], v1[8], sv[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float g = L.g[k];
-            const float m0 = books.dec_m[(L.mc >> (4 * k)) & 15u] * sm_old;
-            const float mm = sc.beta1 * m0 + sc.omb1 * g;
-            float vv;
-            if (packed_v) {
-                const float v0 = books.dec_v[(L.vc >> (4 * k)) & 15u] * sv_old;
-                vv = sc.beta2 * v0 + sc.omb2 * (g * g);
-            } else {
-                vv = vf[k];
-            }
-            const float s = sqrtf(vv);
-            const float denom = s * sc.rsbc2 + sc.eps;
-            L.p[k] = L.p[k] * sc.decay - sc.step_size * (mm / denom);
-            const bool ok = k < nv;
-            m1[k] = ok ? mm : 0.0f;
-            v1[k] = ok ? vv : 0.0f;
-            sv[k] = s;
-        }
-        if (nv > 0) store_params8(T, e0, nv, L.p);
-
-        // first moment: absmax scale of the block, then RTN or state-space SR
-        float am = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(m1[k]));
-        const float s_m = row_max16(am);
-        const float inv_m = s_m > 0.0f ? 1.0f / s_m : 0.0f;
-        const bool m_sr = sc.m_sr_all || ((T.flags & Q4_TF_LM_HEAD) && sc.lm_head_sr);
-        float um[8];
-        if (m_sr) uniforms8((uint64_t)e0, sc.step, T.tensor_id, 0u, sc.key0, sc.key1, um);
-        uint32_t mword = 0;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float x = fminf(fmaxf(m1[k] * inv_m, -1.0f), 1.0f);
-            int idx = rtn_index<MCB>(x);
-            if (m_sr) {
-                int lo; float Llo, Lhi; bool mv;
-                sr_bracket<NM>(books.lev_m, x, idx, lo, Llo, Lhi, mv);
-                idx = lo + ((mv && um[k] * (Lhi - Llo) < (x - Llo)) ? 1 : 0);
-            }
-            const int code = MCB == Q4_CB_SDYN4 ? (idx < 7 ? 15 - idx : (idx == 7 ? 0 : idx - 7)) : idx;
-            mword |= (uint32_t)code << (4 * k);
-        }
-        if (nv > 0) store_codes8(T.m_codes, e0, nv, mword);
-        if (blk_ok && sub == 0) T.m_scales[blk] = s_m;
-
-        if (!packed_v) continue;
-
-        // second moment: max scale of the block, the v rule, EDEN
-        float av = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) av = fmaxf(av, v1[k]);
-        const float s_v = row_max16(av);
-        const float inv_v = s_v > 0.0f ? 1.0f / s_v : 0.0f;
-        // lane `sub` of the row holds sqrt(level_sub * s_v), the square root
-        // of the state value each level would store
-        const float root_own = V_UPD ? sqrtf(books.lev_v[sub] * s_v) : 0.0f;
-        float uv[8];
-        if (V_SR) uniforms8((uint64_t)e0, sc.step, T.tensor_id, 1u, sc.key0, sc.key1, uv);
-        uint32_t vword = 0;
-        float xx[8], xq[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float x = fminf(v1[k] * inv_v, 1.0f);
-            int idx = rtn_index<VCB>(x);
-            if (VRULE != Q4_RULE_STATE_RTN) {
-                int lo; float Llo, Lhi; bool mv;
-                sr_bracket<NV>(books.lev_v, x, idx, lo, Llo, Lhi, mv);
-                bool up = false;
-                if (VRULE == Q4_RULE_STATE_SR) {
-                    up = uv[k] * (Lhi - Llo) < (x - Llo);
-                } else {
-                    const int hi = lo + 1 < NV ? lo + 1 : NV - 1;
-                    const float rlo = bperm(root_own, row_base + lo);
-                    const float rhi = bperm(root_own, row_base + hi);
-                    if (VRULE == Q4_RULE_UPDATE_SR) {
-                        // P(up) = (r(a_lo) - r(v)) / (r(a_lo) - r(a_hi)), r(a) = 1/(sqrt(a) + eps_sr),
-                        // multiplied out so that nothing cancels next to a_lo = 0
-                        const float num = (sv[k] - rlo) * (rhi + sc.eps_sr);
-                        const float den = (rhi - rlo) * (sv[k] + sc.eps_sr);
-                        up = uv[k] * den < num;
-                    } else {
-                        // nearer level in r: r(v) - r(a_hi) < r(a_lo) - r(v)
-                        const float left = (rhi - sv[k]) * (rlo + sc.eps_sr);
-                        const float right = (sv[k] - rlo) * (rhi + sc.eps_sr);
-                        up = left < right;
-                    }
-                }
-                idx = lo + ((mv && up) ? 1 : 0);
-            }
-            vword |= (uint32_t)idx << (4 * k);
-            xx[k] = x * x;
-            xq[k] = x * books.lev_v[idx];
-        }
-        if (nv > 0) store_codes8(T.v_codes, e0, nv, vword);
-        float stored = s_v;
-        if (sc.eden) {
-            // EDEN: S = <x,x> / <x,Q(x)> over the block, pairwise tree in index order
-            const float sxx = row_sum16(tree8(xx));
-            const float sxq = row_sum16(tree8(xq));
-            const float S = sxq > 0.0f ? sxx / sxq : 1.0f;
-            stored = s_v * S;
-        }
-        if (blk_ok && sub == 0) T.v_scales[blk] = stored;
+        const int64_t lc = c - T.chunk_begin;
+        if ((lc + 1) * kChunkElems <= T.numel)
+            step_chunk<MCB, VCB, VRULE, true>(T, lc, c, sc, lds, lb, lane);
+        else
+            step_chunk<MCB, VCB, VRULE, false>(T, lc, c, sc, lds, lb, lane);
     }
 }
 

@@ -98,9 +98,10 @@ class Q4State:
         flags = hp.pop("flags", 0)
         if key == self._last_key:
             flags |= api.HP_REUSE_TABLE
+        else:
+            self._desc = (api.Q4Tensor * len(self.bufs))(*self.describe(params, grads))
         h = self.hparams(step, flags=flags, **hp)
-        desc = self.describe(params, grads)
-        api.q4adamw_step(self.cfg, h, desc, self.ws, self.ws_bytes, stream)
+        api.q4adamw_step(self.cfg, h, self._desc, self.ws, self.ws_bytes, stream)
         self._last_key = key
 
     def dequant(self, i: int, stream=None):

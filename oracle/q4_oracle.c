@@ -329,10 +329,9 @@ static float or_pairwise(const float* x, int n) {
  * state-space SR (the LM-head rule of [P] Table 2) over the signed map.
  * m1[0..n) are the unquantized values; writes n nibbles starting at
  * nibble index j0 of `codes` and returns the new scale. */
-float or_requant_m_block(int cb, int rule, const float* m1, int n, uint64_t seed, uint64_t step,
-                         uint32_t tensor_id, uint64_t elem0, uint8_t* codes, int64_t j0) {
-    or_levels lv;
-    or_make_levels(cb, &lv);
+static float or_requant_m_levels(const or_levels* lvp, int rule, const float* m1, int n, uint64_t seed,
+                                uint64_t step, uint32_t tensor_id, uint64_t elem0, uint8_t* codes, int64_t j0) {
+    const or_levels lv = *lvp;
     float s = 0.0f;
     for (int k = 0; k < n; ++k) { float a = fabsf(m1[k]); if (a > s) s = a; }
     float inv = s > 0.0f ? 1.0f / s : 0.0f;
@@ -350,10 +349,10 @@ float or_requant_m_block(int cb, int rule, const float* m1, int n, uint64_t seed
 /* Second moment of one block: max scale, normalization, the v rule (State
  * or Update, RTN or SR, [P] Table 1), then optionally the EDEN rescale of
  * the quantized block ([P] abstract, ZE-EDEN), folded into the scale. */
-float or_requant_v_block(int cb, int rule, int eden, const float* v1, int n, float eps_sr, uint64_t seed,
-                         uint64_t step, uint32_t tensor_id, uint64_t elem0, uint8_t* codes, int64_t j0) {
-    or_levels lv;
-    or_make_levels(cb, &lv);
+static float or_requant_v_levels(const or_levels* lvp, int rule, int eden, const float* v1, int n, float eps_sr,
+                                uint64_t seed, uint64_t step, uint32_t tensor_id, uint64_t elem0, uint8_t* codes,
+                                int64_t j0) {
+    const or_levels lv = *lvp;
     float s = 0.0f;
     for (int k = 0; k < n; ++k) if (v1[k] > s) s = v1[k];
     float inv = s > 0.0f ? 1.0f / s : 0.0f;
@@ -375,6 +374,22 @@ float or_requant_v_block(int cb, int rule, int eden, const float* v1, int n, flo
     float sxq = or_pairwise(xq, OR_BLOCK);
     float S = sxq > 0.0f ? sxx / sxq : 1.0f;
     return s * S;
+}
+
+/* Block quantizers with the codebook named by id (the tables are built on
+ * each call; the step builds them once per window). */
+float or_requant_m_block(int cb, int rule, const float* m1, int n, uint64_t seed, uint64_t step,
+                         uint32_t tensor_id, uint64_t elem0, uint8_t* codes, int64_t j0) {
+    or_levels lv;
+    or_make_levels(cb, &lv);
+    return or_requant_m_levels(&lv, rule, m1, n, seed, step, tensor_id, elem0, codes, j0);
+}
+
+float or_requant_v_block(int cb, int rule, int eden, const float* v1, int n, float eps_sr, uint64_t seed,
+                         uint64_t step, uint32_t tensor_id, uint64_t elem0, uint8_t* codes, int64_t j0) {
+    or_levels lv;
+    or_make_levels(cb, &lv);
+    return or_requant_v_levels(&lv, rule, eden, v1, n, eps_sr, seed, step, tensor_id, elem0, codes, j0);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -455,6 +470,9 @@ int or_step_window(const or_config* cfg, const or_hparams* hp, const or_window* 
     float Lm[16], Lv[16];
     or_codebook(cfg->m_cb, Lm);
     or_codebook(cfg->v_cb, Lv);
+    or_levels lvm, lvv;
+    or_make_levels(cfg->m_cb, &lvm);
+    or_make_levels(cfg->v_cb, &lvv);
     int m_rule = cfg->m_rule;
     if ((w->flags & OR_TF_LM_HEAD) && hp->lm_head_sr) m_rule = OR_STATE_SR;
 
@@ -492,11 +510,11 @@ int or_step_window(const or_config* cfg, const or_hparams* hp, const or_window* 
             continue;
         }
         uint64_t elem0 = (uint64_t)(w->base + off);
-        w->m_scales[blk] = or_requant_m_block(cfg->m_cb, m_rule, m1, n, hp->seed, hp->step, w->tensor_id,
-                                              elem0, w->m_codes, off);
+        w->m_scales[blk] = or_requant_m_levels(&lvm, m_rule, m1, n, hp->seed, hp->step, w->tensor_id, elem0,
+                                               w->m_codes, off);
         if (!factored)
-            w->v_scales[blk] = or_requant_v_block(cfg->v_cb, cfg->v_rule, cfg->eden, v1, n, hp->eps_sr, hp->seed,
-                                                  hp->step, w->tensor_id, elem0, w->v_codes, off);
+            w->v_scales[blk] = or_requant_v_levels(&lvv, cfg->v_rule, cfg->eden, v1, n, hp->eps_sr, hp->seed,
+                                                   hp->step, w->tensor_id, elem0, w->v_codes, off);
     }
     return 0;
 }
