@@ -26,6 +26,7 @@
 // square root, in the order stated for each operation, so that every code
 // decision is reproducible bit for bit on any IEEE implementation.
 
+#include <atomic>
 #include <utility>
 
 #include "q4_internal.h"
@@ -112,14 +113,19 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
 // 32x32->64 multiplies with the published multipliers, the key bumped by the
-// published Weyl constants between rounds.
+// published Weyl constants between rounds.  On gfx950 each product is one
+// v_mad_u64_u32 and each three-way XOR one v_bitop3_b32 (truth table 0x96).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
 __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
-        const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-        const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
-        c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+        c = make_uint4(xor3((uint32_t)(p1 >> 32), c.y, k0), (uint32_t)p1, xor3((uint32_t)(p0 >> 32), c.w, k1),
+                       (uint32_t)p0);
     }
     return c;
 }
@@ -170,6 +176,21 @@ __device__ __forceinline__ float bperm(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(lane << 2, __float_as_int(v)));
 }
 
+// IEEE (correctly rounded) square root of x from the hardware one, which is
+// faithful: of s - 1ulp, s and s + 1ulp the signs of the exact residuals
+// x - t s (one FMA each) pick the right one (Tuckerman's rounding test).
+// Valid while the residuals cannot underflow, x >= 2^-96, and for x = 0.
+__device__ __forceinline__ float sqrt_rn_normal(float x) {
+    const float s = __builtin_amdgcn_sqrtf(x);
+    const float sd = __uint_as_float(__float_as_uint(s) - 1u);
+    const float su = __uint_as_float(__float_as_uint(s) + 1u);
+    const float rd = __builtin_fmaf(-sd, s, x);
+    const float ru = __builtin_fmaf(-su, s, x);
+    float r = rd <= 0.0f ? sd : s;
+    r = ru > 0.0f ? su : r;
+    return r;
+}
+
 // ---------------------------------------------------------------------------
 // Global-memory views
 // ---------------------------------------------------------------------------
@@ -191,15 +212,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // The RTN index of x is the number of FP32 midpoints strictly below x.
 // Buckets split |x| by its binary exponent and MB leading mantissa bits;
 // every bucket holds at most one midpoint (checked at compile time), so one
-// table entry {thr, base, level(base), level(base+1)} gives the exact count:
-// index = base + (x > thr).  A bucket of a negative x covers (-hi, -lo], one
+// 8-byte table entry {thr, base} gives the exact count: base + (x > thr).  A bucket of a negative x covers (-hi, -lo], one
 // of a positive x [lo, hi); magnitudes below 2^(EMIN-127) share bucket 0.
 
-struct alignas(16) BucketEntry {
+struct alignas(8) BucketEntry {
     float thr;     // the one midpoint inside the bucket, or 3 (never exceeded)
     int32_t base;  // midpoints below every x of the bucket
-    float lv0;     // level(base)
-    float lv1;     // level(min(base + 1, N - 1))
 };
 
 __host__ __device__ constexpr uint32_t f2bits(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -250,8 +268,6 @@ template <int CB> struct EncTable {
                 BucketEntry& d = e[s * E::PAD + b];
                 d.thr = thr;
                 d.base = base;
-                d.lv0 = Book<CB>::level(base);
-                d.lv1 = Book<CB>::level(base + 1 < E::N ? base + 1 : E::N - 1);
             }
         }
     }
@@ -260,6 +276,41 @@ template <int CB> struct EncTable {
 static_assert(EncTable<Q4_CB_NF4>().ok && EncTable<Q4_CB_SDYN4>().ok && EncTable<Q4_CB_DYN4>().ok &&
                   EncTable<Q4_CB_DYN4_NZ>().ok && EncTable<Q4_CB_LIN4_NZ>().ok,
               "a bucket holds two midpoints: use more mantissa bits");
+
+// Floor buckets of an unsigned map whose first level is 0: the index of the
+// largest level <= x.  Each bucket holds at most one level, so one entry
+// {thr, lo} gives it: lo + (x >= thr).  Every level below the bucket lies
+// below every x of the bucket, so x sits exactly on a level iff x == thr.
+struct alignas(8) FloorEntry {
+    float thr;      // the one level inside the bucket, or 3 (never reached)
+    int32_t lo;     // index of the largest level below the bucket (-1 below 0)
+};
+
+template <int CB> struct FloorTable {
+    FloorEntry e[Enc<CB>::NPOS];
+    bool ok;
+    constexpr FloorTable() : e(), ok(true) {
+        using E = Enc<CB>;
+        if (Book<CB>::level(0) != 0.0f) ok = false;
+        for (int b = 0; b < E::NPOS; ++b) {
+            const float lo = b == 0 ? 0.0f : bits2f((uint32_t)((E::EMIN << E::MB) + b) << (23 - E::MB));
+            const float hi = bits2f((uint32_t)((E::EMIN << E::MB) + b + 1) << (23 - E::MB));
+            int below = 0, inside = 0;
+            float thr = 3.0f;
+            for (int k = 0; k < E::N; ++k) {
+                const float L = Book<CB>::level(k);
+                if (L < lo) ++below;
+                else if (L < hi) { ++inside; thr = L; }
+            }
+            if (inside > 1) ok = false;
+            FloorEntry& d = e[b];
+            d.thr = thr;
+            d.lo = below - 1;
+        }
+    }
+};
+static_assert(FloorTable<Q4_CB_DYN4>().ok, "floor buckets of Dyn4 must hold one level each");
+__constant__ FloorTable<Q4_CB_DYN4> c_floor_dyn4 = FloorTable<Q4_CB_DYN4>();
 
 __constant__ EncTable<Q4_CB_NF4> c_enc_nf4 = EncTable<Q4_CB_NF4>();
 __constant__ EncTable<Q4_CB_SDYN4> c_enc_sdyn4 = EncTable<Q4_CB_SDYN4>();
@@ -275,10 +326,9 @@ template <int CB> __device__ __forceinline__ const BucketEntry* enc_table_global
     else return c_enc_lin4nz.e;
 }
 
-// The bucket entry of x (LDS table).  NaN or |x| > 1 land in the last
-// bucket, so the index never leaves the table.
-template <int CB>
-__device__ __forceinline__ const BucketEntry& bucket_of(const BucketEntry* tab, float x) {
+// Bucket index of x.  NaN or |x| > 1 land in the last bucket, so the
+// index never leaves the table.
+template <int CB> __device__ __forceinline__ uint32_t bucket_index(float x) {
     using E = Enc<CB>;
     const uint32_t u = __float_as_uint(x);
     uint32_t raw = __builtin_amdgcn_ubfe(u, 23 - E::MB, 8 + E::MB);
@@ -286,7 +336,11 @@ __device__ __forceinline__ const BucketEntry& bucket_of(const BucketEntry* tab, 
     raw = raw > (uint32_t)(127 << E::MB) ? (uint32_t)(127 << E::MB) : raw;
     uint32_t idx = raw - (uint32_t)(E::EMIN << E::MB);
     if constexpr (E::SIGNED) idx += (u >> 31) * (uint32_t)E::PAD;
-    return tab[idx];
+    return idx;
+}
+template <int CB>
+__device__ __forceinline__ const BucketEntry& bucket_of(const BucketEntry* tab, float x) {
+    return tab[bucket_index<CB>(x)];
 }
 
 // ---------------------------------------------------------------------------
@@ -296,6 +350,7 @@ __device__ __forceinline__ const BucketEntry& bucket_of(const BucketEntry* tab, 
 template <int MCB, int VCB> struct StepLds {
     BucketEntry enc_m[Enc<MCB>::SIZE];
     BucketEntry enc_v[Enc<VCB>::SIZE];
+    FloorEntry floor_v[VCB == Q4_CB_DYN4 ? Enc<VCB>::NPOS : 1];
     float lev_m[16], lev_v[16];  // sorted levels (rare SR paths)
 };
 
@@ -305,7 +360,7 @@ struct LaneBooks {
     float dec_m, dec_v, lev_v;
 };
 
-template <int MCB, int VCB, int VRULE, bool FULL>
+template <int MCB, int VCB, int VRULE, bool FULL, bool PACKED>
 __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc, const int64_t chunk,
                                            const StepScalars& sc, const StepLds<MCB, VCB>& lds,
                                            const LaneBooks& lb, const int lane) {
@@ -323,7 +378,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
         nv = rem >= 8 ? 8 : (rem > 0 ? (int)rem : 0);
         blk_ok = blk * kBlock < n;
     }
-    const bool packed_v = T.kind == KIND_PACKED;
+    constexpr bool packed_v = PACKED;  // packed v; else the factored estimate
     const gptr<float> param = G(T.param);
     const gptr<const uint16_t> grad = G(T.grad);
     const gptr<uint8_t> mcodes = G(T.m_codes);
@@ -368,7 +423,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
 
     // ---- factored second moment: v1 = (R_r C_c) / mean(R) over [rows, cols]
     float vf[8];
-    if (!packed_v) {
+    if constexpr (!packed_v) {
         const float inv_mean = *T.inv_meanR;
         const gptr<const float> R = G((const float*)T.v_row);
         const gptr<const float> Cv = G((const float*)T.v_col);
@@ -405,25 +460,44 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     for (int k = 0; k < 8; ++k) {
         const float gk = g[k];
         const float m0 = bperm(dm_own, row_base + (int)((mc >> (4 * k)) & 15u));
-        const float mm = sc.beta1 * m0 + sc.omb1 * gk;
-        float vv;
-        if (packed_v) {
+        m1[k] = sc.beta1 * m0 + sc.omb1 * gk;
+        if constexpr (packed_v) {
             const float v0 = bperm(dv_own, row_base + (int)((vc >> (4 * k)) & 15u));
-            vv = sc.beta2 * v0 + sc.omb2 * (gk * gk);
+            v1[k] = sc.beta2 * v0 + sc.omb2 * (gk * gk);
         } else {
-            vv = vf[k];
+            v1[k] = vf[k];
         }
-        const float s = sqrtf(vv);
-        const float denom = s * sc.rsbc2 + sc.eps;
-        p[k] = p[k] * sc.decay - sc.step_size * (mm / denom);
-        if (FULL) {
-            m1[k] = mm;
-            v1[k] = vv;
+    }
+    // The preconditioner-space rules decide codes from sqrt(v1), so there it
+    // is the IEEE square root (the short form unless some element of the
+    // wave is below 2^-96); elsewhere it only scales the weight update and
+    // the hardware square root (1 ulp) serves.
+    if (V_UPD) {
+        bool tiny = false;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) tiny |= v1[k] > 0.0f && v1[k] < 0x1p-96f;
+        if (__builtin_amdgcn_ballot_w64(tiny) != 0) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) sv[k] = sqrtf(v1[k]);
         } else {
-            m1[k] = k < nv ? mm : 0.0f;
-            v1[k] = k < nv ? vv : 0.0f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) sv[k] = sqrt_rn_normal(v1[k]);
         }
-        sv[k] = s;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sv[k] = __builtin_amdgcn_sqrtf(v1[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        // the quotient m1 / denom uses the hardware reciprocal (1 ulp): it
+        // moves the weight by far less than one part in 10^6 and no code
+        // depends on it
+        const float denom = sv[k] * sc.rsbc2 + sc.eps;
+        p[k] = p[k] * sc.decay - sc.step_size * (m1[k] * __builtin_amdgcn_rcpf(denom));
+        if (!FULL && k >= nv) {
+            m1[k] = 0.0f;
+            v1[k] = 0.0f;
+        }
     }
     if (FULL || nv == 8) {
         *reinterpret_cast<gptr<f32x4>>(param + e0) = f32x4{p[0], p[1], p[2], p[3]};
@@ -460,7 +534,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
             const BucketEntry& e = bucket_of<MCB>(lds.enc_m, x);
             const bool gt = x > e.thr;
             const int idx = e.base + (gt ? 1 : 0);
-            const float Lidx = gt ? e.lv1 : e.lv0;
+            const float Lidx = lds.lev_m[idx];
             // the lower level is idx or idx - 1; an exact hit or the top level stays
             const bool below = x < Lidx;
             const int lo = below ? (idx > 0 ? idx - 1 : 0) : idx;
@@ -481,7 +555,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     }
     if ((FULL || blk_ok) && sub == 0) mscales[blk] = s_m;
 
-    if (!packed_v) return;
+    if constexpr (!packed_v) return;
 
     // ---- second moment: max scale, the v rule, EDEN
     float av = 0.0f;
@@ -496,13 +570,41 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     if (V_SR) uniforms8((uint64_t)e0, sc.step, T.tensor_id, 1u, sc.key0, sc.key1, uv);
     uint32_t vword = 0;
     float xx[8], xq[8];
+    if (VRULE == Q4_RULE_UPDATE_SR && VCB == Q4_CB_DYN4 && !sc.eden) {
+        // ZIP-SR.  Per-row tables, lane k: root_k, root_(k+1) + eps_sr and
+        // root_(k+1) - root_k (the same FP32 operations the rule forms per
+        // element, done once per level).
+        const float root_next = bperm(root_own, lane + 1);
+        const float rnext_eps = root_next + sc.eps_sr;
+        const float rdiff = root_next - root_own;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float x = fminf(v1[k] * inv_v, 1.0f);
+            // lower level: the floor bucket gives it directly; an exact level
+            // hit needs no draw (the top level 1 can only be hit exactly)
+            const FloorEntry& f = lds.floor_v[bucket_index<VCB>(x)];
+            const bool ge = x >= f.thr;
+            const int lo = f.lo + (ge ? 1 : 0);
+            const bool hit = x == f.thr;
+            const int src = row_base + lo;
+            const float rlo = bperm(root_own, src);
+            const float rhe = bperm(rnext_eps, src);
+            const float rdf = bperm(rdiff, src);
+            // P(up) = (r(a_lo) - r(v)) / (r(a_lo) - r(a_hi)), r(a) = 1/(sqrt(a) + eps_sr),
+            // multiplied out so that nothing cancels next to a_lo = 0
+            const float num = (sv[k] - rlo) * rhe;
+            const float den = rdf * (sv[k] + sc.eps_sr);
+            const bool up = !hit && (uv[k] * den < num);
+            vword |= (uint32_t)(lo + (up ? 1 : 0)) << (4 * k);
+        }
+    } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const float x = fminf(v1[k] * inv_v, 1.0f);
         const BucketEntry& e = bucket_of<VCB>(lds.enc_v, x);
         const bool gt = x > e.thr;
         int idx = e.base + (gt ? 1 : 0);
-        float q = gt ? e.lv1 : e.lv0;  // level(idx)
+        float q = lds.lev_v[idx];  // level(idx)
         if constexpr (VRULE != Q4_RULE_STATE_RTN) {
             const float Lidx = q;
             const bool below = x < Lidx;
@@ -517,8 +619,6 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
                 const float rlo = bperm(root_own, row_base + lo);
                 const float rhi = bperm(root_own, row_base + hi);
                 if constexpr (VRULE == Q4_RULE_UPDATE_SR) {
-                    // P(up) = (r(a_lo) - r(v)) / (r(a_lo) - r(a_hi)), r(a) = 1/(sqrt(a) + eps_sr),
-                    // multiplied out so that nothing cancels next to a_lo = 0
                     const float num = (sv[k] - rlo) * (rhi + sc.eps_sr);
                     const float den = (rhi - rlo) * (sv[k] + sc.eps_sr);
                     up = uv[k] * den < num;
@@ -535,6 +635,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
         vword |= (uint32_t)idx << (4 * k);
         xx[k] = x * x;
         xq[k] = x * q;
+    }
     }
     if (FULL || nv == 8) {
         *reinterpret_cast<gptr<uint32_t>>(vcodes + (e0 >> 1)) = vword;
@@ -554,6 +655,16 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     if ((FULL || blk_ok) && sub == 0) vscales[blk] = stored;
 }
 
+// Last tensor whose first chunk is <= c (binary search over the prefix).
+__device__ __forceinline__ int first_tensor(const int64_t* __restrict__ chunk_begin, int n_tensors, int64_t c) {
+    int lo = 0, hi = n_tensors - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (chunk_begin[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
 template <int MCB, int VCB, int VRULE>
 __global__ __launch_bounds__(256) void k_fused_step(const DevTensor* __restrict__ tab,
                                                      const int64_t* __restrict__ chunk_begin, int n_tensors,
@@ -565,6 +676,8 @@ __global__ __launch_bounds__(256) void k_fused_step(const DevTensor* __restrict_
         const BucketEntry* gv = enc_table_global<VCB>();
         for (int i = threadIdx.x; i < Enc<MCB>::SIZE; i += blockDim.x) lds.enc_m[i] = gm[i];
         for (int i = threadIdx.x; i < Enc<VCB>::SIZE; i += blockDim.x) lds.enc_v[i] = gv[i];
+        if constexpr (VCB == Q4_CB_DYN4)
+            for (int i = threadIdx.x; i < Enc<VCB>::NPOS; i += blockDim.x) lds.floor_v[i] = c_floor_dyn4.e[i];
         if (threadIdx.x < 16) {
             const int t = threadIdx.x;
             lds.lev_m[t] = t < Book<MCB>::N ? sorted_level_rt<MCB>(t) : 1.0f;
@@ -580,16 +693,20 @@ __global__ __launch_bounds__(256) void k_fused_step(const DevTensor* __restrict_
     __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int t = 0;
+    int t = first_tensor(chunk_begin, n_tensors, (int64_t)blockIdx.x * kWavesPerGroup + wave);
     for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks;
          c += (int64_t)gridDim.x * kWavesPerGroup) {
         while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
         const DevTensor T = tab[t];
         const int64_t lc = c - T.chunk_begin;
-        if ((lc + 1) * kChunkElems <= T.numel)
-            step_chunk<MCB, VCB, VRULE, true>(T, lc, c, sc, lds, lb, lane);
-        else
-            step_chunk<MCB, VCB, VRULE, false>(T, lc, c, sc, lds, lb, lane);
+        const bool full = (lc + 1) * kChunkElems <= T.numel;
+        if (T.kind == KIND_PACKED) {
+            if (full) step_chunk<MCB, VCB, VRULE, true, true>(T, lc, c, sc, lds, lb, lane);
+            else step_chunk<MCB, VCB, VRULE, false, true>(T, lc, c, sc, lds, lb, lane);
+        } else {
+            if (full) step_chunk<MCB, VCB, VRULE, true, false>(T, lc, c, sc, lds, lb, lane);
+            else step_chunk<MCB, VCB, VRULE, false, false>(T, lc, c, sc, lds, lb, lane);
+        }
     }
 }
 
@@ -602,7 +719,7 @@ __global__ __launch_bounds__(256) void k_fp32_step(const DevTensor* __restrict__
                                                     int64_t total_chunks, StepScalars sc) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    int t = 0;
+    int t = first_tensor(chunk_begin, n_tensors, (int64_t)blockIdx.x * kWavesPerGroup + wave);
     for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks;
          c += (int64_t)gridDim.x * kWavesPerGroup) {
         while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
@@ -820,9 +937,26 @@ __global__ __launch_bounds__(256) void k_dequant(DevTensor T, float* __restrict_
 // Launchers
 // ---------------------------------------------------------------------------
 
-static int step_grid(int64_t total_chunks) {
+// Grid-stride grid sized from the kernel's occupancy and the number of
+// compute units, never more groups than there are chunk groups.
+template <class K> static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache) {
+    static std::atomic<int> cus{0};
+    if (cus.load() == 0) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        const bool ok = hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess;
+        cus.store(ok && prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256);
+    }
+    int per_cu = per_cu_cache.load();
+    if (per_cu == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        per_cu_cache.store(per_cu);
+    }
     const int64_t groups = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
-    const int64_t cap = 256 * 8;  // 8 resident 256-thread groups per CU
+    // four times the resident groups: the queued groups balance the uneven
+    // finishing times of the first wave of groups (measured best on gfx950)
+    const int64_t cap = 4 * (int64_t)per_cu * cus.load();
     return (int)(groups < cap ? (groups > 0 ? groups : 1) : cap);
 }
 
@@ -846,9 +980,10 @@ bool variant_supported(const Variant& v) {
 hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevTensor* d_tab,
                              const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks, hipStream_t stream) {
     if (total_chunks <= 0) return hipSuccess;
-    const int grid = step_grid(total_chunks);
 #define Q4_LAUNCH(A, B, C)                                                                              \
     if (v.mcb == A && v.vcb == B && v.vrule == C) {                                                     \
+        static std::atomic<int> occ{0};                                                                 \
+        const int grid = step_grid(k_fused_step<A, B, C>, total_chunks, occ);                           \
         k_fused_step<A, B, C><<<grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, sc); \
         return hipGetLastError();                                                                       \
     }
@@ -860,7 +995,9 @@ hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevT
 hipError_t launch_fp32_step(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
                             int n_tensors, int64_t total_chunks, hipStream_t stream) {
     if (total_chunks <= 0) return hipSuccess;
-    k_fp32_step<<<step_grid(total_chunks), 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, sc);
+    static std::atomic<int> occ{0};
+    k_fp32_step<<<step_grid(k_fp32_step, total_chunks, occ), 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors,
+                                                                               total_chunks, sc);
     return hipGetLastError();
 }
 
