@@ -161,3 +161,49 @@ def test_gpt_162m_sampled_20_steps():
         _flush(f"gpt-162m {recipe}")
         rep = parity.run(w, recipe, 20, windows=wins, grads_on="cuda", check_every_step=False)
         rep.check()
+
+
+def test_llama_1_1b_sampled_lm_head_phase():
+    """Llama-style 1.1B set, ZIP-SR, 10 steps, the LM-head first moment on
+    NF4-SR in the final 10% (step 10); windows of every tensor."""
+    w = inputs.llama_1_1b()
+    wins = parity.sample_windows(w, n_random=48, seed=1)
+    _flush("llama-1.1b zip_sr")
+    rep = parity.run(w, "zip_sr", 10, windows=wins, grads_on="cuda", lm_head_phase=True, check_every_step=False)
+    rep.check()
+
+
+@pytest.mark.parametrize("recipe", ["ze_eden", "zip_sr"])
+def test_gpt_2_7b_sampled(recipe):
+    """GPT-style 2.7B set (all state resident in HBM), 10 steps, windows."""
+    w = inputs.gpt_2_7b()
+    wins = parity.sample_windows(w, n_random=48, seed=2)
+    _flush(f"gpt-2.7b {recipe}")
+    rep = parity.run(w, recipe, 10, windows=wins, grads_on="cuda", check_every_step=False)
+    rep.check()
+
+
+def test_qwen3_factored_full_rc():
+    """Factored mode on the Qwen3-0.6B-shaped set (4 BF16 microbatches per
+    step): the oracle recomputes every matrix's R and C from the full
+    gradient each step; weights and m codes compared on windows."""
+    w = inputs.qwen3_0_6b_factored()
+    wins = parity.sample_windows(w, n_random=32, seed=3)
+    _flush("qwen3-0.6b factored")
+    rep = parity.run(w, "factored", 10, windows=wins, grads_on="cuda", check_every_step=False)
+    rep.check()
+
+
+def test_tensor_beyond_2_32_elements():
+    """One tensor of 2^32 + 1000 elements (17 GB of FP32 masters): 64-bit
+    element indices, Philox counters past 2^32 / 4, a ragged last block."""
+    n = (1 << 32) + 1000
+    w = inputs.custom([(n,)], grad_kind="masked", seed=27)
+    nb = (n + 127) // 128
+    lo32 = (1 << 32) // 128
+    lo31 = (1 << 31) // 128
+    wins = [(0, 0, 2), (0, lo31 - 2, lo31 + 2), (0, lo32 - 3, lo32 + 3), (0, nb - 3, nb)]
+    _flush("2^32 + 1000 elements zip_sr")
+    rep = parity.run(w, "zip_sr", 2, windows=wins, grads_on="cuda")
+    rep.check()
+    assert rep.codes_differ == 0
