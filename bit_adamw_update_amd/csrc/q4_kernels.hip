@@ -745,13 +745,28 @@ __global__ __launch_bounds__(256) void k_fp32_step(const DevTensor* __restrict__
 // K2 / K3: factored second moment (row and column means of g^2)
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ double shfl_xor_d(double v, int m) { return __shfl_xor(v, m, 64); }
+template <int CTRL> __device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 
-// Sum of one double per lane over the wavefront, butterfly in fixed order.
+// Sum of one double per lane over the wavefront in a fixed order: a DPP
+// tree within each 16-lane row, then the four rows in order (wave-uniform
+// result).
 __device__ __forceinline__ double wave_sum_d(double v) {
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) v = v + shfl_xor_d(v, m);
-    return v;
+    v = v + dpp_d<DPP_QUAD_1032>(v);
+    v = v + dpp_d<DPP_QUAD_2301>(v);
+    v = v + dpp_d<DPP_ROW_HALF_MIRROR>(v);
+    v = v + dpp_d<DPP_ROW_MIRROR>(v);
+    return ((readlane_d(v, 0) + readlane_d(v, 16)) + readlane_d(v, 32)) + readlane_d(v, 48);
 }
 
 // Sum over the 256 threads of a work-group, tree in LDS in fixed order.
@@ -801,30 +816,47 @@ __global__ __launch_bounds__(256) void k_rowcol_partial(const DevMatrix* __restr
     double col[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) col[k] = 0.0;
-    for (int64_t r = r0 + wave; r < r1; r += kWavesPerGroup) {
-        const uint16_t* gp = M.grad + r * M.cols + c0;
-        double d[8];
-        if (vec) {
-            const uint4 q = *reinterpret_cast<const uint4*>(gp);
-            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    // rows r0 + wave, r0 + wave + 4, ...; four rows' loads are issued before
+    // any of them is reduced, so each wave keeps four loads in flight
+    const gptr<const uint16_t> grad = G(M.grad);
+    constexpr int U = 4;
+    for (int64_t rb = r0 + wave; rb < r1; rb += U * kWavesPerGroup) {
+        u32x4 q[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t r = rb + (int64_t)u * kWavesPerGroup;
+            q[u] = u32x4{0u, 0u, 0u, 0u};
+            if (r < r1) {
+                const gptr<const uint16_t> gp = grad + r * M.cols + c0;
+                if (vec) {
+                    q[u] = *reinterpret_cast<const gptr<const u32x4>>(gp);
+                } else {
+                    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        if (k < ncv) w[k >> 1] |= (uint32_t)gp[k] << (16 * (k & 1));
+                    q[u] = u32x4{w[0], w[1], w[2], w[3]};
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t r = rb + (int64_t)u * kWavesPerGroup;
+            if (r >= r1) break;  // wave-uniform
+            const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+            double d[8];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const float a = bf16_to_f32(w[k] & 0xFFFFu), b = bf16_to_f32(w[k] >> 16);
                 d[2 * k] = (double)(a * a);
                 d[2 * k + 1] = (double)(b * b);
             }
-        } else {
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float a = k < ncv ? bf16_to_f32(gp[k]) : 0.0f;
-                d[k] = (double)(a * a);
-            }
+            for (int k = 0; k < 8; ++k) col[k] += d[k];
+            const double rp = ((d[0] + d[1]) + (d[2] + d[3])) + ((d[4] + d[5]) + (d[6] + d[7]));
+            const double rs = wave_sum_d(rp);
+            if (lane == 0) M.part_row[ctile * M.rows + r] = rs;
         }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) col[k] += d[k];
-        const double rp = ((d[0] + d[1]) + (d[2] + d[3])) + ((d[4] + d[5]) + (d[6] + d[7]));
-        const double rs = wave_sum_d(rp);
-        if (lane == 0) M.part_row[ctile * M.rows + r] = rs;
     }
 #pragma unroll
     for (int k = 0; k < 8; ++k) lds[wave][lane * 8 + k] = col[k];
@@ -868,22 +900,39 @@ __global__ __launch_bounds__(256) void k_rowcol_finalize(const DevMatrix* __rest
         const DevMatrix M = mats[mi];
         const int64_t cidx = (cg - M.cgroup_begin) * kGroup + threadIdx.x;
         if (cidx < M.cols) {
-            double cs = 0.0;
-            for (int64_t b = 0; b < M.n_bands; ++b) cs += M.part_col[b * M.cols + cidx];
+            // eight interleaved accumulators (band b into a[b mod 8]) keep
+            // eight loads in flight; combined in a fixed tree
+            double a[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+            int64_t b = 0;
+            for (; b + 8 <= M.n_bands; b += 8) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) a[j] += M.part_col[(b + j) * M.cols + cidx];
+            }
+            for (int j = 0; b < M.n_bands; ++b, ++j) a[j] += M.part_col[b * M.cols + cidx];
+            const double cs = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
             M.C[cidx] = beta2 * M.C[cidx] + omb2 * ((float)cs / (float)M.rows);
         }
     }
 }
 
-// K3b: one work-group per matrix: mean(R) from the group sums in order.
-__global__ __launch_bounds__(64) void k_rowcol_mean(const DevMatrix* __restrict__ mats) {
+// 1 / mean(R) from the per-group sums of R: thread t adds groups t, t+256,
+// ... in order, then a fixed tree over the threads.  The step and the
+// dequantization both use this, so they agree bit for bit.
+__device__ __forceinline__ float inv_mean_of(const double* __restrict__ part, int64_t n_groups, int64_t rows,
+                                             double* lds) {
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < n_groups; i += 256) s += part[i];
+    const double tot = group_sum_d(s, lds);
+    const float meanR = (float)(tot / (double)rows);
+    return meanR > 0.0f ? 1.0f / meanR : 0.0f;
+}
+
+// K3b: one work-group per matrix.
+__global__ __launch_bounds__(256) void k_rowcol_mean(const DevMatrix* __restrict__ mats) {
+    __shared__ double lds[256];
     const DevMatrix M = mats[blockIdx.x];
-    if (threadIdx.x == 0) {
-        double s = 0.0;
-        for (int64_t i = 0; i < M.n_rgroups; ++i) s += M.part_mean[i];
-        const float meanR = (float)(s / (double)M.rows);
-        *M.inv_meanR = meanR > 0.0f ? 1.0f / meanR : 0.0f;
-    }
+    const float inv = inv_mean_of(M.part_mean, M.n_rgroups, M.rows, lds);
+    if (threadIdx.x == 0) *M.inv_meanR = inv;
 }
 
 // Group sums of the stored R (same tree as K3a), for dequantization.
@@ -893,14 +942,11 @@ __global__ __launch_bounds__(256) void k_rsum_groups(const float* __restrict__ R
     const double s = group_sum_d(r < rows ? (double)R[r] : 0.0, lds);
     if (threadIdx.x == 0) part[blockIdx.x] = s;
 }
-__global__ __launch_bounds__(64) void k_rsum_final(const double* __restrict__ part, int64_t n_groups, int64_t rows,
-                                                   float* inv) {
-    if (threadIdx.x == 0) {
-        double s = 0.0;
-        for (int64_t i = 0; i < n_groups; ++i) s += part[i];
-        const float meanR = (float)(s / (double)rows);
-        *inv = meanR > 0.0f ? 1.0f / meanR : 0.0f;
-    }
+__global__ __launch_bounds__(256) void k_rsum_final(const double* __restrict__ part, int64_t n_groups, int64_t rows,
+                                                    float* inv) {
+    __shared__ double lds[256];
+    const float v = inv_mean_of(part, n_groups, rows, lds);
+    if (threadIdx.x == 0) *inv = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -1011,7 +1057,7 @@ hipError_t launch_factored_stats(const DevMatrix* d_mats, int n_mats, int64_t to
                                                                                      beta2, omb2);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_rowcol_mean<<<n_mats, 64, 0, stream>>>(d_mats);
+    k_rowcol_mean<<<n_mats, 256, 0, stream>>>(d_mats);
     return hipGetLastError();
 }
 
@@ -1033,7 +1079,7 @@ hipError_t launch_dequant(int mcb, int vcb, const DevTensor& t, int64_t rows, fl
         k_rsum_groups<<<(unsigned)ng, 256, 0, stream>>>(t.v_row, rows, ws_partials);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        k_rsum_final<<<1, 64, 0, stream>>>(ws_partials, ng, rows, ws_inv);
+        k_rsum_final<<<1, 256, 0, stream>>>(ws_partials, ng, rows, ws_inv);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
