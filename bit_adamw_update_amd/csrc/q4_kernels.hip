@@ -130,18 +130,15 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
     return c;
 }
 
-// The 8 uniforms of a lane whose first element index e0 is a multiple of 8:
-// element i uses word i mod 4 of Philox(ctr = (i/4, step, tensor, stream)),
-// its top 24 bits scaled by 2^-24.
-__device__ __forceinline__ void uniforms8(uint64_t e0, uint32_t step, uint32_t tid, uint32_t stream, uint32_t k0,
-                                          uint32_t k1, float u[8]) {
-    const uint32_t c0 = (uint32_t)(e0 >> 2);
-    const uint4 a = philox4x32_10(make_uint4(c0, step, tid, stream), k0, k1);
-    const uint4 b = philox4x32_10(make_uint4(c0 + 1u, step, tid, stream), k0, k1);
+// Element i draws word i mod 4 of Philox(ctr = (i/4, step, tensor, stream)),
+// its top 24 bits scaled by 2^-24.  uniforms4 gives the 4 uniforms of
+// elements 4c .. 4c+3.
+__device__ __forceinline__ void uniforms4(uint32_t c, uint32_t step, uint32_t tid, uint32_t stream, uint32_t k0,
+                                          uint32_t k1, float u[4]) {
+    const uint4 a = philox4x32_10(make_uint4(c, step, tid, stream), k0, k1);
     const float s = 5.9604644775390625e-8f;  // 2^-24
-    u[0] = (float)(a.x >> 8) * s; u[1] = (float)(a.y >> 8) * s; u[2] = (float)(a.z >> 8) * s;
-    u[3] = (float)(a.w >> 8) * s; u[4] = (float)(b.x >> 8) * s; u[5] = (float)(b.y >> 8) * s;
-    u[6] = (float)(b.z >> 8) * s; u[7] = (float)(b.w >> 8) * s;
+    u[0] = (float)(a.x >> 8) * s; u[1] = (float)(a.y >> 8) * s;
+    u[2] = (float)(a.z >> 8) * s; u[3] = (float)(a.w >> 8) * s;
 }
 
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
@@ -152,12 +149,19 @@ template <int CTRL> __device__ __forceinline__ float dpp(float v) {
 // with the row's pairwise-tree reduction of its 16 lane values.
 constexpr int DPP_QUAD_1032 = 0xB1, DPP_QUAD_2301 = 0x4E, DPP_ROW_HALF_MIRROR = 0x141, DPP_ROW_MIRROR = 0x140;
 
+// Maximum over the 16 lanes of a row of values that are +0 or positive (not
+// NaN): their bit patterns order like the values, so an unsigned maximum,
+// which takes its DPP operand directly, does it.
+template <int CTRL> __device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
 __device__ __forceinline__ float row_max16(float x) {
-    x = fmaxf(x, dpp<DPP_QUAD_1032>(x));
-    x = fmaxf(x, dpp<DPP_QUAD_2301>(x));
-    x = fmaxf(x, dpp<DPP_ROW_HALF_MIRROR>(x));
-    x = fmaxf(x, dpp<DPP_ROW_MIRROR>(x));
-    return x;
+    uint32_t u = __float_as_uint(x);
+    u = max(u, dpp_u<DPP_QUAD_1032>(u));
+    u = max(u, dpp_u<DPP_QUAD_2301>(u));
+    u = max(u, dpp_u<DPP_ROW_HALF_MIRROR>(u));
+    u = max(u, dpp_u<DPP_ROW_MIRROR>(u));
+    return __uint_as_float(u);
 }
 // Sum over the 16 lanes of a row, combining lanes (0,1),(2,3).. then pairs
 // of pairs, then halves: the pairwise tree over the lanes in index order
@@ -174,6 +178,16 @@ __device__ __forceinline__ float tree8(const float* v) {
 }
 __device__ __forceinline__ float bperm(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(lane << 2, __float_as_int(v)));
+}
+// ds_bpermute byte address of lane row + code, code = nibble k of `codes`,
+// rb4 = 4 * row (the row's first lane): the nibble is shifted straight into
+// place (two instructions).
+__device__ __forceinline__ int nibble_addr(uint32_t codes, int k, uint32_t rb4) {
+    const uint32_t c4 = k == 0 ? (codes << 2) : (codes >> (4 * k - 2));
+    return (int)((c4 & 0x3Cu) | rb4);
+}
+__device__ __forceinline__ float bperm_addr(float v, int addr) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
 }
 
 // IEEE (correctly rounded) square root of x from the hardware one, which is
@@ -368,6 +382,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     constexpr bool V_SR = VRULE == Q4_RULE_STATE_SR || VRULE == Q4_RULE_UPDATE_SR;
     constexpr bool V_UPD = VRULE == Q4_RULE_UPDATE_SR || VRULE == Q4_RULE_UPDATE_RTN;
     const int sub = lane & 15, row_base = lane & 48;
+    const uint32_t rb4 = (uint32_t)row_base << 2;
     const int64_t n = T.numel;
     const int64_t blk = lc * kBlocksPerChunk + (lane >> 4);
     const int64_t e0 = blk * kBlock + sub * 8;
@@ -427,10 +442,12 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
         const float inv_mean = *T.inv_meanR;
         const gptr<const float> R = G((const float*)T.v_row);
         const gptr<const float> Cv = G((const float*)T.v_col);
-        // row of the chunk's first element (wave-uniform), then a 32-bit
-        // division for the lane's offset (cols < 2^31 is validated)
+        // row of the chunk's first element (wave-uniform; 32-bit division
+        // while the offset fits), then a 32-bit division for the lane's
+        // offset (cols < 2^31 is validated)
         const uint32_t cols = (uint32_t)T.cols;
-        const int64_t rb = (lc * kChunkElems) / T.cols;
+        const uint64_t first = (uint64_t)lc * kChunkElems;
+        const int64_t rb = (first >> 32) == 0 ? (int64_t)((uint32_t)first / cols) : (int64_t)(first / (uint64_t)T.cols);
         const uint32_t off = (uint32_t)(e0 - rb * T.cols);
         const uint32_t dr = off / cols;
         uint32_t cc = off - dr * cols;
@@ -459,10 +476,10 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const float gk = g[k];
-        const float m0 = bperm(dm_own, row_base + (int)((mc >> (4 * k)) & 15u));
+        const float m0 = bperm_addr(dm_own, nibble_addr(mc, k, rb4));
         m1[k] = sc.beta1 * m0 + sc.omb1 * gk;
         if constexpr (packed_v) {
-            const float v0 = bperm(dv_own, row_base + (int)((vc >> (4 * k)) & 15u));
+            const float v0 = bperm_addr(dv_own, nibble_addr(vc, k, rb4));
             v1[k] = sc.beta2 * v0 + sc.omb2 * (gk * gk);
         } else {
             v1[k] = vf[k];
@@ -473,10 +490,11 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     // wave is below 2^-96); elsewhere it only scales the weight update and
     // the hardware square root (1 ulp) serves.
     if (V_UPD) {
-        bool tiny = false;
+        // some v1 in (0, 2^-96)?  v1 >= +0, and bits - 1 sends +0 to the top
+        uint32_t low = 0xFFFFFFFFu;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) tiny |= v1[k] > 0.0f && v1[k] < 0x1p-96f;
-        if (__builtin_amdgcn_ballot_w64(tiny) != 0) {
+        for (int k = 0; k < 8; ++k) low = min(low, __float_as_uint(v1[k]) - 1u);
+        if (__builtin_amdgcn_ballot_w64(low < 0x0F800000u - 1u) != 0) {
 #pragma unroll
             for (int k = 0; k < 8; ++k) sv[k] = sqrtf(v1[k]);
         } else {
@@ -526,10 +544,10 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
             mword |= (uint32_t)code << (4 * k);
         }
     } else {
-        float um[8];
-        uniforms8((uint64_t)e0, sc.step, T.tensor_id, 0u, sc.key0, sc.key1, um);
+        float um[4];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
+            if ((k & 3) == 0) uniforms4((uint32_t)(e0 >> 2) + (k >> 2), sc.step, T.tensor_id, 0u, sc.key0, sc.key1, um);
             const float x = fminf(fmaxf(m1[k] * inv_m, -1.0f), 1.0f);
             const BucketEntry& e = bucket_of<MCB>(lds.enc_m, x);
             const bool gt = x > e.thr;
@@ -541,7 +559,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
             const int hi = lo + 1 < NM ? lo + 1 : NM - 1;
             const float Llo = lds.lev_m[lo], Lhi = lds.lev_m[hi];
             const bool mv = !(below && idx == 0) && !(x == Lidx) && lo != NM - 1;
-            const int fin = lo + ((mv && um[k] * (Lhi - Llo) < (x - Llo)) ? 1 : 0);
+            const int fin = lo + ((mv && um[k & 3] * (Lhi - Llo) < (x - Llo)) ? 1 : 0);
             const int code = MCB == Q4_CB_SDYN4 ? (fin < 7 ? 15 - fin : (fin == 7 ? 0 : fin - 7)) : fin;
             mword |= (uint32_t)code << (4 * k);
         }
@@ -566,8 +584,12 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     // lane `sub` holds sqrt(level_sub * s_v): the square root of the state
     // each level would store, for the preconditioner-space rules
     const float root_own = V_UPD ? sqrtf(lb.lev_v * s_v) : 0.0f;
-    float uv[8];
-    if (V_SR) uniforms8((uint64_t)e0, sc.step, T.tensor_id, 1u, sc.key0, sc.key1, uv);
+    // uniforms of the v rule, drawn 4 at a time (elements 4h .. 4h+3)
+    float uv[4];
+    auto draw_v = [&](int k) {
+        if (V_SR && (k & 3) == 0)
+            uniforms4((uint32_t)(e0 >> 2) + (k >> 2), sc.step, T.tensor_id, 1u, sc.key0, sc.key1, uv);
+    };
     uint32_t vword = 0;
     float xx[8], xq[8];
     if (VRULE == Q4_RULE_UPDATE_SR && VCB == Q4_CB_DYN4 && !sc.eden) {
@@ -579,6 +601,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
         const float rdiff = root_next - root_own;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
+            draw_v(k);
             const float x = fminf(v1[k] * inv_v, 1.0f);
             // lower level: the floor bucket gives it directly; an exact level
             // hit needs no draw (the top level 1 can only be hit exactly)
@@ -594,12 +617,13 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
             // multiplied out so that nothing cancels next to a_lo = 0
             const float num = (sv[k] - rlo) * rhe;
             const float den = rdf * (sv[k] + sc.eps_sr);
-            const bool up = !hit && (uv[k] * den < num);
+            const bool up = !hit && (uv[k & 3] * den < num);
             vword |= (uint32_t)(lo + (up ? 1 : 0)) << (4 * k);
         }
     } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
+        draw_v(k);
         const float x = fminf(v1[k] * inv_v, 1.0f);
         const BucketEntry& e = bucket_of<VCB>(lds.enc_v, x);
         const bool gt = x > e.thr;
@@ -614,14 +638,14 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
             bool up;
             if constexpr (VRULE == Q4_RULE_STATE_SR) {
                 const float Llo = lds.lev_v[lo], Lhi = lds.lev_v[hi];
-                up = uv[k] * (Lhi - Llo) < (x - Llo);
+                up = uv[k & 3] * (Lhi - Llo) < (x - Llo);
             } else {
                 const float rlo = bperm(root_own, row_base + lo);
                 const float rhi = bperm(root_own, row_base + hi);
                 if constexpr (VRULE == Q4_RULE_UPDATE_SR) {
                     const float num = (sv[k] - rlo) * (rhi + sc.eps_sr);
                     const float den = (rhi - rlo) * (sv[k] + sc.eps_sr);
-                    up = uv[k] * den < num;
+                    up = uv[k & 3] * den < num;
                 } else {
                     // nearer level in r: r(v) - r(a_hi) < r(a_lo) - r(v)
                     const float left = (rhi - sv[k]) * (rlo + sc.eps_sr);
@@ -665,8 +689,17 @@ __device__ __forceinline__ int first_tensor(const int64_t* __restrict__ chunk_be
     return lo;
 }
 
+// Resident wavefronts per SIMD asked of the register allocator (at most 80
+// and 72 VGPRs): the preconditioner-space rules keep more values live than
+// the state-space ones.  Measured on the GPT-2.7B set: ZIP-SR 2% faster than
+// with the allocator's own choice (91 VGPRs, 5 wavefronts).
+template <int VRULE> constexpr int step_waves() {
+    return (VRULE == Q4_RULE_UPDATE_SR || VRULE == Q4_RULE_UPDATE_RTN) ? 6 : 7;
+}
+
 template <int MCB, int VCB, int VRULE>
-__global__ __launch_bounds__(256) void k_fused_step(const DevTensor* __restrict__ tab,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves<VRULE>())))
+void k_fused_step(const DevTensor* __restrict__ tab,
                                                      const int64_t* __restrict__ chunk_begin, int n_tensors,
                                                      int64_t total_chunks, StepScalars sc) {
     __shared__ StepLds<MCB, VCB> lds;
