@@ -21,10 +21,11 @@
 // every tensor: waves walk a grid-stride sequence of tensor-aligned chunks
 // and follow a prefix table of chunk offsets.
 //
-// Arithmetic is FP32, round-to-nearest-even, without contraction (the
-// library is built with -ffp-contract=off) and with IEEE division and
-// square root, in the order stated for each operation, so that every code
-// decision is reproducible bit for bit on any IEEE implementation.
+// Arithmetic is FP32, round-to-nearest-even, with IEEE division and square
+// root, in the order stated for each operation, so that every code decision
+// is reproducible bit for bit on any IEEE implementation.  The compiler
+// contracts nothing (-ffp-contract=off); the fused multiply-adds are written
+// out: the two moment recurrences, the denominator and the weight update.
 
 #include <atomic>
 #include <utility>
@@ -477,10 +478,11 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     for (int k = 0; k < 8; ++k) {
         const float gk = g[k];
         const float m0 = bperm_addr(dm_own, nibble_addr(mc, k, rb4));
-        m1[k] = sc.beta1 * m0 + sc.omb1 * gk;
+        // each recurrence is one fused multiply-add onto the gradient term
+        m1[k] = __builtin_fmaf(sc.beta1, m0, sc.omb1 * gk);
         if constexpr (packed_v) {
             const float v0 = bperm_addr(dv_own, nibble_addr(vc, k, rb4));
-            v1[k] = sc.beta2 * v0 + sc.omb2 * (gk * gk);
+            v1[k] = __builtin_fmaf(sc.beta2, v0, sc.omb2 * (gk * gk));
         } else {
             v1[k] = vf[k];
         }
@@ -510,8 +512,8 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
         // the quotient m1 / denom uses the hardware reciprocal (1 ulp): it
         // moves the weight by far less than one part in 10^6 and no code
         // depends on it
-        const float denom = sv[k] * sc.rsbc2 + sc.eps;
-        p[k] = p[k] * sc.decay - sc.step_size * (m1[k] * __builtin_amdgcn_rcpf(denom));
+        const float denom = __builtin_fmaf(sv[k], sc.rsbc2, sc.eps);
+        p[k] = __builtin_fmaf(-sc.step_size, m1[k] * __builtin_amdgcn_rcpf(denom), p[k] * sc.decay);
         if (!FULL && k >= nv) {
             m1[k] = 0.0f;
             v1[k] = 0.0f;
@@ -763,10 +765,10 @@ __global__ __launch_bounds__(256) void k_fp32_step(const DevTensor* __restrict__
             const int64_t i = e0 + k;
             if (i < T.numel) {
                 const float g = bf16_to_f32(T.grad[i]);
-                const float mm = sc.beta1 * T.m32[i] + sc.omb1 * g;
-                const float vv = sc.beta2 * T.v32[i] + sc.omb2 * (g * g);
-                const float denom = sqrtf(vv) * sc.rsbc2 + sc.eps;
-                T.param[i] = T.param[i] * sc.decay - sc.step_size * (mm / denom);
+                const float mm = __builtin_fmaf(sc.beta1, T.m32[i], sc.omb1 * g);
+                const float vv = __builtin_fmaf(sc.beta2, T.v32[i], sc.omb2 * (g * g));
+                const float denom = __builtin_fmaf(sqrtf(vv), sc.rsbc2, sc.eps);
+                T.param[i] = __builtin_fmaf(-sc.step_size, mm / denom, T.param[i] * sc.decay);
                 T.m32[i] = mm;
                 T.v32[i] = vv;
             }

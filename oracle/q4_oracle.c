@@ -22,12 +22,16 @@
  *        the AdamW description paragraph and the storage paragraph
  *        (1.0625 B/param vs 8 B for two FP32 buffers).
  *
- * Arithmetic: every step is IEEE binary32 with round-to-nearest-even, no
- * contraction (build with -ffp-contract=off), in the order written, because
- * [A] "State representation" fixes the update to block-local FP32 work.
- * Exceptions, each stated where it happens: the bias-correction scalars
- * (binary64, then rounded), the codebook constructions (binary64, then
- * rounded) and the factored row/column sums (binary64 accumulation).
+ * Arithmetic: every step is IEEE binary32 with round-to-nearest-even, in
+ * the order written, because [A] "State representation" fixes the update to
+ * block-local FP32 work.  The compiler contracts nothing (build with
+ * -ffp-contract=off); where a sum of products is one fused multiply-add,
+ * the code calls fmaf: the two moment recurrences, the denominator and the
+ * weight update (the pages fix FP32 work, not the rounding of each product
+ * within it).  Exceptions, each stated where it happens: the
+ * bias-correction scalars (binary64, then rounded), the codebook
+ * constructions (binary64, then rounded) and the factored row/column sums
+ * (binary64 accumulation).
  *
  * Readings where the pages are silent (each one is listed in the design
  * notes of the repository as well):
@@ -492,16 +496,19 @@ int or_step_window(const or_config* cfg, const or_hparams* hp, const or_window* 
                 m0 = Lm[or_get_nibble(w->m_codes, j)] * w->m_scales[blk];
                 if (!factored) v0 = Lv[or_get_nibble(w->v_codes, j)] * w->v_scales[blk];
             }
-            float mm = b1 * m0 + omb1 * g;
+            /* m1 = b1 m0 + (1 - b1) g, v1 = b2 v0 + (1 - b2) g^2, each as one
+             * fused multiply-add onto the rounded gradient term */
+            float mm = fmaf(b1, m0, omb1 * g);
             float vv;
             if (factored) {
                 int64_t r = i / w->cols, c = i % w->cols;
                 vv = (w->R[r] * w->C[c]) * w->inv_meanR;
             } else {
-                vv = b2 * v0 + omb2 * (g * g);
+                vv = fmaf(b2, v0, omb2 * (g * g));
             }
-            float denom = sqrtf(vv) * rsbc2 + eps;
-            w->param[j] = w->param[j] * decay - step_size * (mm / denom);
+            /* w <- w decay - step_size m1 / (sqrt(v1) rsbc2 + eps) */
+            float denom = fmaf(sqrtf(vv), rsbc2, eps);
+            w->param[j] = fmaf(-step_size, mm / denom, w->param[j] * decay);
             m1[k] = mm;
             v1[k] = vv;
         }
