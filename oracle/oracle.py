@@ -53,7 +53,7 @@ def build(force: bool = False) -> str:
 class _Hp(C.Structure):
     _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
                 ("weight_decay", C.c_float), ("eps_sr", C.c_float), ("step", C.c_uint64),
-                ("seed", C.c_uint64), ("lm_head_sr", C.c_uint32)]
+                ("seed", C.c_uint64), ("lm_head_sr", C.c_uint32), ("grad_scale", C.c_float)]
 
 
 class _Cfg(C.Structure):
@@ -102,6 +102,11 @@ def lib():
         L.or_zero_code.argtypes = [i32]
         L.or_zero_code.restype = i32
         L.or_state_bytes.argtypes = [i32, i64, i64, i32, C.POINTER(C.c_uint64)]
+        L.or_accumulate_bf16.argtypes = [vp, vp, i64, i32]
+        L.or_grad_sumsq.argtypes = [vp, i64]
+        L.or_grad_sumsq.restype = C.c_double
+        L.or_clip_factor.argtypes = [C.c_double, C.c_float]
+        L.or_clip_factor.restype = C.c_float
         _lib = L
     return _lib
 
@@ -117,10 +122,12 @@ class HParams:
     step: int = 1
     seed: int = 0
     lm_head_sr: int = 0
+    grad_scale: float = 1.0
 
     def c(self) -> _Hp:
         return _Hp(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay,
-                   self.eps if self.eps_sr is None else self.eps_sr, self.step, self.seed, self.lm_head_sr)
+                   self.eps if self.eps_sr is None else self.eps_sr, self.step, self.seed, self.lm_head_sr,
+                   self.grad_scale)
 
 
 @dataclass
@@ -253,6 +260,23 @@ def dequant_window(cfg: Config, *, numel: int, base: int, length: int, m_codes, 
     c = cfg.c()
     lib().or_dequant_window(C.byref(c), C.byref(w), _fp(m), _fp(v))
     return m, v
+
+
+def accumulate_bf16(acc: np.ndarray, micro: np.ndarray, first: bool) -> None:
+    """acc <- micro (first) or bf16(f32(acc) + f32(micro)), in place (uint16 BF16 bits)."""
+    assert acc.dtype == np.uint16 and micro.dtype == np.uint16 and acc.size == micro.size
+    lib().or_accumulate_bf16(_p(acc), _p(micro), acc.size, int(bool(first)))
+
+
+def grad_sumsq(g: np.ndarray) -> float:
+    """Binary64 sum of the FP32 squares of a BF16 gradient, in index order."""
+    assert g.dtype == np.uint16
+    return float(lib().or_grad_sumsq(_p(g), g.size))
+
+
+def clip_factor(sq: float, max_norm: float) -> float:
+    """min(1, max_norm / (sqrt(sq) + 1e-6)) rounded to FP32; 1.0 when max_norm <= 0."""
+    return float(lib().or_clip_factor(float(sq), float(max_norm)))
 
 
 def state_bytes(recipe: int, numel: int, rows: int, is_matrix: bool) -> tuple[int, int, int]:

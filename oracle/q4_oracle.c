@@ -212,6 +212,7 @@ typedef struct {
     float lr, beta1, beta2, eps, weight_decay, eps_sr;
     uint64_t step, seed;
     uint32_t lm_head_sr;
+    float grad_scale; /* clip factor applied to every gradient element (1: no clipping) */
 } or_hparams;
 
 typedef struct { float decay, step_size, rsbc2, omb1, omb2; } or_scalars;
@@ -411,11 +412,16 @@ static float or_bf16_to_f32(uint16_t b) {
     return f;
 }
 
+/* With gradient clipping (grad_scale s != 1) the statistics are those of the
+ * clipped gradient, formed as s^2 times the binary64 sums of the squares of
+ * the unclipped BF16 gradient (s^2 exact in binary64), so that they can be
+ * gathered before s is known. */
 void or_factored_update(const or_hparams* hp, int64_t rows, int64_t cols, const uint16_t* grad,
                         float* R, float* C, float* inv_meanR) {
     float sc[5];
     or_host_scalars(hp, sc);
     float omb2 = sc[4];
+    const double s2 = (double)hp->grad_scale * (double)hp->grad_scale;
     double* cs = (double*)calloc((size_t)cols, sizeof(double));
     for (int64_t r = 0; r < rows; ++r) {
         double rs = 0.0;
@@ -425,14 +431,63 @@ void or_factored_update(const or_hparams* hp, int64_t rows, int64_t cols, const 
             rs += (double)g2;
             cs[c] += (double)g2;
         }
-        R[r] = hp->beta2 * R[r] + omb2 * ((float)rs / (float)cols);
+        R[r] = hp->beta2 * R[r] + omb2 * ((float)(rs * s2) / (float)cols);
     }
-    for (int64_t c = 0; c < cols; ++c) C[c] = hp->beta2 * C[c] + omb2 * ((float)cs[c] / (float)rows);
+    for (int64_t c = 0; c < cols; ++c) C[c] = hp->beta2 * C[c] + omb2 * ((float)(cs[c] * s2) / (float)rows);
     free(cs);
     double sum = 0.0;
     for (int64_t r = 0; r < rows; ++r) sum += (double)R[r];
     float meanR = (float)(sum / (double)rows);
     *inv_meanR = meanR > 0.0f ? 1.0f / meanR : 0.0f;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The step before: BF16 gradient accumulation, norm and clip factor        */
+/* ------------------------------------------------------------------------ */
+/* [A] "State representation": microbatches stream into BF16 gradient
+ * shards (no FP32 main gradient), and the gradient norm and clipping work
+ * on those BF16 shards. */
+
+/* FP32 -> BF16, round to nearest, ties to even (NaN kept quiet). */
+static uint16_t or_f32_to_bf16(float f) {
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+/* acc <- micro on the first microbatch; otherwise acc <- bf16(f32(acc) +
+ * f32(micro)): one FP32 addition (exact for most BF16 pairs), then one
+ * rounding to BF16. */
+void or_accumulate_bf16(uint16_t* acc, const uint16_t* micro, int64_t n, int first) {
+    for (int64_t i = 0; i < n; ++i) {
+        if (first) acc[i] = micro[i];
+        else acc[i] = or_f32_to_bf16(or_bf16_to_f32(acc[i]) + or_bf16_to_f32(micro[i]));
+    }
+}
+
+/* Sum of squares of a BF16 gradient: each square formed in FP32 (exact for
+ * BF16 inputs short of overflow and underflow), summed in binary64 in index
+ * order.  The global squared norm is the binary64 sum of these over the
+ * tensors in order; the pages fix no summation order, so another order
+ * gives the same value up to binary64 rounding. */
+double or_grad_sumsq(const uint16_t* g, int64_t n) {
+    double s = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        float x = or_bf16_to_f32(g[i]);
+        s += (double)(x * x);
+    }
+    return s;
+}
+
+/* Clip factor from the global squared norm, as torch.nn.utils.clip_grad_norm_
+ * forms it: min(1, max_norm / (sqrt(sq) + 1e-6)) in binary64, rounded to
+ * FP32; 1 when max_norm <= 0 (clipping off). */
+float or_clip_factor(double sq, float max_norm) {
+    if (!(max_norm > 0.0f)) return 1.0f;
+    double c = (double)max_norm / (sqrt(sq) + 1e-6);
+    return c < 1.0 ? (float)c : 1.0f;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -487,7 +542,8 @@ int or_step_window(const or_config* cfg, const or_hparams* hp, const or_window* 
         for (int k = 0; k < n; ++k) {
             int64_t j = off + k;            /* index within the window */
             int64_t i = w->base + j;        /* index within the tensor */
-            float g = or_bf16_to_f32(w->grad[j]);
+            /* the clipped gradient: one FP32 product (exact when s = 1) */
+            float g = or_bf16_to_f32(w->grad[j]) * hp->grad_scale;
             float m0, v0 = 0.0f;
             if (fp32) {
                 m0 = w->m32[j];

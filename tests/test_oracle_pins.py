@@ -503,3 +503,131 @@ def test_lm_head_sr_only_in_final_phase():
     assert np.array_equal(out[(0, 0)], out[(0, 1)]) and np.array_equal(out[(0, 0)], out[(O.TF_LM_HEAD, 0)])
     assert not np.array_equal(out[(0, 0)], out[(O.TF_LM_HEAD, 1)])
     assert inputs.lm_head_sr_on(10, 10) == 1 and inputs.lm_head_sr_on(9, 10) == 0
+
+
+# ---------------------------------------------------------------------------
+# The step before: BF16 accumulation, gradient norm, clipping
+# ---------------------------------------------------------------------------
+
+def _bf16_bits(x):
+    import torch
+    return x.to(torch.bfloat16).view(torch.uint16).numpy().copy()
+
+
+def test_accumulate_bf16_matches_torch_round_to_nearest_even():
+    """acc <- bf16(f32(acc) + f32(micro)) over four microbatches equals
+    torch's own FP32 addition and BF16 conversion (round to nearest even),
+    on random gradients and on crafted halfway cases."""
+    import torch
+    g = torch.Generator().manual_seed(11)
+    n = 200_000
+    micro = [torch.randn(n, generator=g) * torch.exp(torch.randn(n, generator=g) * 3) for _ in range(4)]
+    acc = np.zeros(n, np.uint16)
+    ref = None
+    for k, m in enumerate(micro):
+        mb = _bf16_bits(m)
+        O.accumulate_bf16(acc, mb, first=(k == 0))
+        mt = torch.from_numpy(mb.view(np.int16)).view(torch.bfloat16)
+        ref = mt.clone() if k == 0 else (ref.float() + mt.float()).to(torch.bfloat16)
+        assert np.array_equal(acc, ref.view(torch.uint16).numpy())
+    # halfway cases: 1 + 2^-8 rounds to 1, (1 + 2^-7) + 2^-8 rounds up to 1 + 2^-6
+    a = np.array([0x3F80, 0x3F81, 0xBF80, 0x3F80], np.uint16)
+    b = np.array([0x3B80, 0x3B80, 0xBB80, 0x0000], np.uint16)   # 2^-8, 2^-8, -2^-8, +0
+    O.accumulate_bf16(a, b, first=False)
+    ta = torch.tensor([1.0, 1.0078125, -1.0, 1.0]).to(torch.bfloat16)
+    tb = torch.tensor([2 ** -8, 2 ** -8, -2 ** -8, 0.0]).to(torch.bfloat16)
+    assert np.array_equal(a, (ta.float() + tb.float()).to(torch.bfloat16).view(torch.uint16).numpy())
+    assert a[0] == 0x3F80 and a[1] == 0x3F82
+
+
+@pytest.mark.parametrize("max_norm", [0.05, 1e9])
+def test_grad_norm_and_clip_factor_match_torch(max_norm):
+    """The global norm (binary64 sum of squares) and the clip factor equal
+    torch.nn.utils.clip_grad_norm_ on float64 copies of the same BF16
+    gradients: the norm to 1e-12, the factor to the FP32 rounding of
+    torch's."""
+    import torch
+    g = torch.Generator().manual_seed(12)
+    shapes = [(1000,), (64, 37), (5,)]
+    grads = [_bf16_bits(torch.randn(*s, generator=g) * 1e-3) .reshape(-1) for s in shapes]
+    sq = sum(O.grad_sumsq(x) for x in grads)
+    ps = []
+    for x in grads:
+        p = torch.nn.Parameter(torch.zeros(x.size, dtype=torch.float64))
+        p.grad = torch.from_numpy((x.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+        ps.append(p)
+    before = [p.grad.clone() for p in ps]
+    total = float(torch.nn.utils.clip_grad_norm_(ps, max_norm))
+    assert abs(np.sqrt(sq) - total) <= 1e-12 * total
+    coef = float((ps[0].grad[before[0] != 0] / before[0][before[0] != 0]).mean())
+    c = O.clip_factor(sq, max_norm)
+    assert c == float(np.float32(coef)) or abs(c - coef) <= 2 ** -23 * coef
+    if max_norm > total:
+        assert c == 1.0
+    else:
+        assert c < 1.0
+    assert O.clip_factor(sq, 0.0) == 1.0
+
+
+def test_power_of_two_clip_scales_moments_exactly():
+    """A clip factor of 1/2 halves g exactly, so from the zero state the
+    first ZE-EDEN step writes the same codes, m scales exactly halved and v
+    scales exactly quartered, and the factored row/column statistics come
+    out exactly a quarter of the unclipped ones."""
+    import torch
+    g = torch.Generator().manual_seed(13)
+    n = 4096
+    grad = _bf16_bits(torch.randn(n, generator=g) * 1e-3)
+    outs = []
+    for s in (1.0, 0.5):
+        st = O.TensorState(O.Config.of(O.ZE_EDEN), (n,), 5)
+        p = np.zeros(n, np.float32)
+        st.step(O.HParams(step=1, grad_scale=s), p, grad)
+        outs.append(st)
+    a, b = outs
+    assert np.array_equal(a.m_codes, b.m_codes) and np.array_equal(a.v_codes, b.v_codes)
+    assert np.array_equal(a.m_scales * np.float32(0.5), b.m_scales)
+    assert np.array_equal(a.v_scales * np.float32(0.25), b.v_scales)
+    rows, cols = 32, 128
+    gm = grad[: rows * cols]
+    res = []
+    for s in (1.0, 0.5):
+        R = np.zeros(rows, np.float32)
+        Cc = np.zeros(cols, np.float32)
+        O.factored_update(O.HParams(step=1, grad_scale=s), rows, cols, gm, R, Cc)
+        res.append((R, Cc))
+    assert np.array_equal(res[0][0] * np.float32(0.25), res[1][0])
+    assert np.array_equal(res[0][1] * np.float32(0.25), res[1][1])
+
+
+def test_fp32_recipe_with_clipping_matches_torch():
+    """FP32 recipe with clipping against torch: clip_grad_norm_ on float64
+    gradients, then AdamW, 5 steps."""
+    import torch
+    from bit_adamw_update_amd import inputs
+    w = inputs.custom([(1000,), (37, 29)], grad_kind="masked", seed=14)
+    steps, max_norm = 5, 1e-3
+    params, grads = _workload_host(w, steps)
+    cfg = O.Config.of(O.FP32)
+    states = [O.TensorState(cfg, t.shape, t.tensor_id) for t in w.tensors]
+    p_or = [p.copy() for p in params]
+    tp = [torch.nn.Parameter(torch.from_numpy(p.astype(np.float64))) for p in params]
+    f = {k: float(np.float32(v)) for k, v in w.hp.items()}
+    opt = torch.optim.AdamW(tp, lr=f["lr"], betas=(f["beta1"], f["beta2"]), eps=f["eps"],
+                            weight_decay=f["weight_decay"], foreach=False)
+    clipped = 0
+    for t in range(1, steps + 1):
+        sq = sum(O.grad_sumsq(x) for x in grads[t - 1])
+        c = O.clip_factor(sq, max_norm)
+        clipped += c < 1.0
+        hp = O.HParams(step=t, grad_scale=c, **w.hp)
+        for i, st in enumerate(states):
+            st.step(hp, p_or[i], grads[t - 1][i])
+            tp[i].grad = torch.from_numpy((grads[t - 1][i].astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+        torch.nn.utils.clip_grad_norm_(tp, max_norm)
+        opt.step()
+    assert clipped == steps
+    for i in range(len(states)):
+        ref = tp[i].detach().numpy()
+        scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref ** 2)))
+        assert (np.abs(p_or[i] - ref) / scale).max() < 2e-6
