@@ -509,7 +509,7 @@ def test_lm_head_sr_only_in_final_phase():
 # The step before: BF16 accumulation, gradient norm, clipping
 # ---------------------------------------------------------------------------
 
-def _bf16_bits(x):
+def _torch_bf16_bits(x):
     import torch
     return x.to(torch.bfloat16).view(torch.uint16).numpy().copy()
 
@@ -525,7 +525,7 @@ def test_accumulate_bf16_matches_torch_round_to_nearest_even():
     acc = np.zeros(n, np.uint16)
     ref = None
     for k, m in enumerate(micro):
-        mb = _bf16_bits(m)
+        mb = _torch_bf16_bits(m)
         O.accumulate_bf16(acc, mb, first=(k == 0))
         mt = torch.from_numpy(mb.view(np.int16)).view(torch.bfloat16)
         ref = mt.clone() if k == 0 else (ref.float() + mt.float()).to(torch.bfloat16)
@@ -549,7 +549,7 @@ def test_grad_norm_and_clip_factor_match_torch(max_norm):
     import torch
     g = torch.Generator().manual_seed(12)
     shapes = [(1000,), (64, 37), (5,)]
-    grads = [_bf16_bits(torch.randn(*s, generator=g) * 1e-3) .reshape(-1) for s in shapes]
+    grads = [_torch_bf16_bits(torch.randn(*s, generator=g) * 1e-3) .reshape(-1) for s in shapes]
     sq = sum(O.grad_sumsq(x) for x in grads)
     ps = []
     for x in grads:
@@ -577,7 +577,7 @@ def test_power_of_two_clip_scales_moments_exactly():
     import torch
     g = torch.Generator().manual_seed(13)
     n = 4096
-    grad = _bf16_bits(torch.randn(n, generator=g) * 1e-3)
+    grad = _torch_bf16_bits(torch.randn(n, generator=g) * 1e-3)
     outs = []
     for s in (1.0, 0.5):
         st = O.TensorState(O.Config.of(O.ZE_EDEN), (n,), 5)
