@@ -14,9 +14,10 @@ from .build import LIB_PATH
 RECIPE_ZIP_SR, RECIPE_ZE_EDEN, RECIPE_FACTORED, RECIPE_FP32, RECIPE_CUSTOM = range(5)
 CB_NF4, CB_SDYN4, CB_DYN4, CB_DYN4_NZ, CB_LIN4_NZ = range(5)
 RULE_STATE_RTN, RULE_STATE_SR, RULE_UPDATE_RTN, RULE_UPDATE_SR = range(4)
-HP_REUSE_TABLE, HP_CHECK_POINTERS = 1, 2
+HP_REUSE_TABLE, HP_CHECK_POINTERS, HP_GRAD_STATS = 1, 2, 4
+ACC_FIRST, ACC_LAST, ACC_REUSE_TABLE = 1, 2, 4
 TF_LM_HEAD = 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 MAX_NDIM = 8
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_INVALID_ARG", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGNMENT", 4: "Q4_ERR_CONFLICT",
@@ -32,7 +33,8 @@ class Q4Config(C.Structure):
 class Q4HParams(C.Structure):
     _fields_ = [("lr", C.c_float), ("beta1", C.c_float), ("beta2", C.c_float), ("eps", C.c_float),
                 ("weight_decay", C.c_float), ("eps_sr", C.c_float), ("step", C.c_uint64), ("seed", C.c_uint64),
-                ("lm_head_sr", C.c_uint32), ("flags", C.c_uint32)]
+                ("lm_head_sr", C.c_uint32), ("flags", C.c_uint32), ("max_grad_norm", C.c_float),
+                ("reserved", C.c_uint32)]
 
 
 class Q4Tensor(C.Structure):
@@ -81,6 +83,12 @@ _SIGNATURES = {
                       C.c_size_t, C.c_void_p], C.c_int),
     "q4adamw_dequant_state": ([C.POINTER(Q4Config), C.POINTER(Q4Tensor), C.c_void_p, C.c_void_p, C.c_void_p,
                                C.c_size_t, C.c_void_p], C.c_int),
+    "q4adamw_flat_offsets": ([C.POINTER(Q4Tensor), C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_int64)], C.c_int),
+    "q4adamw_accumulate": ([C.POINTER(Q4Config), C.POINTER(Q4Tensor), C.c_int32, C.c_void_p, C.c_int32, C.c_void_p,
+                           C.c_size_t, C.c_void_p], C.c_int),
+    "q4adamw_grad_stats": ([C.POINTER(Q4Config), C.POINTER(Q4Tensor), C.c_int32, C.c_void_p, C.c_size_t,
+                           C.c_void_p], C.c_int),
+    "q4adamw_grad_norm": ([C.c_void_p, C.c_size_t, C.POINTER(C.c_double), C.c_void_p], C.c_int),
 }
 
 
@@ -211,3 +219,35 @@ def q4adamw_dequant_state(cfg: Q4Config, tensor: Q4Tensor, m_out, v_out, ws=None
         ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load_library().q4adamw_dequant_state(C.byref(cfg), C.byref(tensor), _ptr(m_out), _ptr(v_out), _ptr(ws),
                                                 ws_bytes, _stream(stream)))
+
+
+def q4adamw_flat_offsets(tensors) -> tuple[list, int]:
+    arr, n = _tensors(tensors)
+    offs = (C.c_int64 * n)()
+    total = C.c_int64()
+    _check(load_library().q4adamw_flat_offsets(arr, n, offs, C.byref(total)))
+    return list(offs), total.value
+
+
+def q4adamw_accumulate(cfg: Q4Config, tensors, micro, flags: int, ws, ws_bytes: int | None = None,
+                       stream=None) -> None:
+    arr, n = _tensors(tensors)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(load_library().q4adamw_accumulate(C.byref(cfg), arr, n, _ptr(micro), flags, _ptr(ws), ws_bytes,
+                                             _stream(stream)))
+
+
+def q4adamw_grad_stats(cfg: Q4Config, tensors, ws, ws_bytes: int | None = None, stream=None) -> None:
+    arr, n = _tensors(tensors)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(load_library().q4adamw_grad_stats(C.byref(cfg), arr, n, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def q4adamw_grad_norm(ws, ws_bytes: int | None = None, stream=None) -> float:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    out = C.c_double()
+    _check(load_library().q4adamw_grad_norm(_ptr(ws), ws_bytes, C.byref(out), _stream(stream)))
+    return out.value

@@ -98,6 +98,8 @@ q4_status check_hp(const q4_hparams* hp) {
         return fail(Q4_ERR_INVALID_ARG, "beta1 and beta2 must lie in [0, 1)");
     if (!(hp->eps > 0.0f)) return fail(Q4_ERR_INVALID_ARG, "eps must be > 0");
     if (hp->step == 0) return fail(Q4_ERR_INVALID_ARG, "step is 1-based (got 0)");
+    if (!finite(hp->max_grad_norm) || hp->max_grad_norm < 0.0f)
+        return fail(Q4_ERR_INVALID_ARG, "max_grad_norm must be finite and >= 0");
     return ok();
 }
 
@@ -216,8 +218,12 @@ q4_status check_all_pointers(const q4_tensor* t, int32_t n) {
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace layout of a step.
+// Workspace bytes 0..255: the gradient statistics' sum of squares (binary64,
+// offset 0) and the clip factor (FP32, offset 8).
+constexpr size_t kOffSq = 0, kOffClip = 8;
+
 struct Plan {
-    size_t off_tab, off_chunks, off_mats, off_inv, off_prow, off_pcol, off_pmean, total;
+    size_t off_tab, off_chunks, off_mats, off_inv, off_prow, off_pcol, off_pmean, off_sqpart, total;
     int64_t total_chunks = 0;
     int n_mats = 0;
     int64_t total_tiles = 0, total_rgroups = 0, total_cgroups = 0;
@@ -262,6 +268,7 @@ void plan_layout(const Resolved& r, const q4_tensor* t, int32_t n, Plan& P, uint
             m.n_ctiles = (m.cols + kTileCols - 1) / kTileCols;
             m.n_bands = (m.rows + kBandRows - 1) / kBandRows;
             m.tile_begin = P.total_tiles;
+            m.flat_off = d.chunk_begin * kChunkElems;
             P.total_tiles += m.n_ctiles * m.n_bands;
             m.n_rgroups = (m.rows + kGroup - 1) / kGroup;
             m.rgroup_begin = P.total_rgroups;
@@ -290,6 +297,7 @@ void plan_layout(const Resolved& r, const q4_tensor* t, int32_t n, Plan& P, uint
     P.off_prow = o;      o = round256(o + sizeof(double) * prow);
     P.off_pcol = o;      o = round256(o + sizeof(double) * pcol);
     P.off_pmean = o;     o = round256(o + sizeof(double) * pmean);
+    P.off_sqpart = o;    o = round256(o + sizeof(double) * (size_t)(kAccGroups + P.total_tiles));
     P.total = o;
     if (ws) {  // resolve offsets into device addresses
         for (DevMatrix& m : P.mats) {
@@ -326,6 +334,39 @@ int zero_code(int cb) {
 
 q4_status hip_fail(hipError_t e, const char* what) {
     return fail(Q4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Tensor table, chunk prefix and matrix table form one contiguous upload.
+// From pageable host memory HIP performs the copy synchronously, so the
+// temporary source may go away on return; the cost (a host wait for the
+// stream) is why callers that pass the same tensor list again set
+// Q4_HP_REUSE_TABLE / Q4_ACC_REUSE_TABLE.
+q4_status upload_tables(const Plan& P, int32_t n, uint8_t* wsb, hipStream_t st) {
+    const size_t upload = P.off_inv - P.off_tab;
+    std::vector<uint8_t> host(upload, 0);
+    std::memcpy(host.data(), P.tab.data(), sizeof(DevTensor) * n);
+    std::memcpy(host.data() + (P.off_chunks - P.off_tab), P.chunks.data(), sizeof(int64_t) * (n + 1));
+    if (!P.mats.empty())
+        std::memcpy(host.data() + (P.off_mats - P.off_tab), P.mats.data(), sizeof(DevMatrix) * P.mats.size());
+    const hipError_t e = hipMemcpyAsync(wsb + P.off_tab, host.data(), upload, hipMemcpyHostToDevice, st);
+    if (e != hipSuccess) return hip_fail(e, "tensor table upload");
+    return Q4_OK;
+}
+
+// Common checks and layout of the calls that take a workspace.
+q4_status prepare(const q4_config* cfg, const q4_tensor* t, int32_t n, bool need_param, void* ws, size_t ws_bytes,
+                  Resolved& r, Plan& P) {
+    q4_status s = resolve(cfg, &r);
+    if (s != Q4_OK) return s;
+    if ((s = check_tensors(r, t, n, need_param)) != Q4_OK) return s;
+    int dev = 0;
+    if ((s = check_device(&dev)) != Q4_OK) return s;
+    if (!ws) return fail(Q4_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned16(ws)) return fail(Q4_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+    plan_layout(r, t, n, P, reinterpret_cast<uint8_t*>(ws));
+    if (ws_bytes < P.total)
+        return fail(Q4_ERR_WORKSPACE, "workspace has %zu bytes, the call needs %zu", ws_bytes, P.total);
+    return Q4_OK;
 }
 
 }  // namespace
@@ -529,21 +570,7 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
 
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
-    if (!(hp->flags & Q4_HP_REUSE_TABLE)) {
-        // Tensor table, chunk prefix and matrix table form one contiguous
-        // upload.  From pageable host memory HIP performs the copy
-        // synchronously, so the temporary source may go away on return; the
-        // cost (a host wait for the stream) is why callers that step the same
-        // tensor list again pass Q4_HP_REUSE_TABLE.
-        const size_t upload = P.off_inv - P.off_tab;
-        std::vector<uint8_t> host(upload, 0);
-        std::memcpy(host.data(), P.tab.data(), sizeof(DevTensor) * n);
-        std::memcpy(host.data() + (P.off_chunks - P.off_tab), P.chunks.data(), sizeof(int64_t) * (n + 1));
-        if (!P.mats.empty())
-            std::memcpy(host.data() + (P.off_mats - P.off_tab), P.mats.data(), sizeof(DevMatrix) * P.mats.size());
-        e = hipMemcpyAsync(wsb + P.off_tab, host.data(), upload, hipMemcpyHostToDevice, st);
-        if (e != hipSuccess) return hip_fail(e, "tensor table upload");
-    }
+    if (!(hp->flags & Q4_HP_REUSE_TABLE) && (s = upload_tables(P, n, wsb, st)) != Q4_OK) return s;
     float hs[5];
     scalars_of(hp, hs);
     StepScalars sc{};
@@ -562,17 +589,36 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
     sc.lm_head_sr = hp->lm_head_sr ? 1u : 0u;
     sc.m_sr_all = (uint32_t)r.m_sr_all;
     sc.eden = (uint32_t)r.eden;
+    sc.clip = nullptr;
 
     const DevTensor* d_tab = reinterpret_cast<const DevTensor*>(wsb + P.off_tab);
     const int64_t* d_chunks = reinterpret_cast<const int64_t*>(wsb + P.off_chunks);
+    const DevMatrix* d_mats = reinterpret_cast<const DevMatrix*>(wsb + P.off_mats);
+    bool stats_ready = (hp->flags & Q4_HP_GRAD_STATS) != 0;
+    if (hp->max_grad_norm > 0.0f) {
+        double* sq = reinterpret_cast<double*>(wsb + kOffSq);
+        float* clip = reinterpret_cast<float*>(wsb + kOffClip);
+        if (!stats_ready) {
+            // one read of the gradients: their norm and, for factored
+            // matrices, the row/column partials the step needs anyway
+            e = launch_grad_pass(GRAD_STATS_ONLY, true, P.n_mats > 0, d_tab, d_chunks, n, P.total_chunks, d_mats,
+                                 P.n_mats, P.total_tiles, nullptr, reinterpret_cast<double*>(wsb + P.off_sqpart), sq,
+                                 st);
+            if (e != hipSuccess) return hip_fail(e, "gradient statistics launch");
+            stats_ready = true;
+        }
+        e = launch_clip_factor(sq, hp->max_grad_norm, clip, st);
+        if (e != hipSuccess) return hip_fail(e, "clip factor launch");
+        sc.clip = clip;
+    }
     if (r.recipe == Q4_RECIPE_FP32) {
         e = launch_fp32_step(sc, d_tab, d_chunks, n, P.total_chunks, st);
         if (e != hipSuccess) return hip_fail(e, "fp32 step launch");
         return ok();
     }
     if (P.n_mats > 0) {
-        e = launch_factored_stats(reinterpret_cast<const DevMatrix*>(wsb + P.off_mats), P.n_mats, P.total_tiles,
-                                  P.total_rgroups, P.total_cgroups, sc.beta2, sc.omb2, st);
+        e = launch_factored_stats(d_mats, P.n_mats, P.total_tiles, P.total_rgroups, P.total_cgroups, sc.beta2, sc.omb2,
+                                  sc.clip, stats_ready, st);
         if (e != hipSuccess) return hip_fail(e, "factored statistics launch");
     }
     e = launch_fused_step(r.var, sc, d_tab, d_chunks, n, P.total_chunks, st);
@@ -619,6 +665,75 @@ q4_status q4adamw_dequant_state(const q4_config* cfg, const q4_tensor* t, float*
                                   need ? reinterpret_cast<double*>(wsb + 256) : nullptr,
                                   need ? reinterpret_cast<float*>(wsb) : nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "dequant launch");
+    return ok();
+}
+
+q4_status q4adamw_flat_offsets(const q4_tensor* t, int32_t n, int64_t* offsets, int64_t* total) {
+    if (!t || !offsets || !total) return fail(Q4_ERR_INVALID_ARG, "tensor list, offsets or total is NULL");
+    if (n <= 0) return fail(Q4_ERR_SHAPE, "n_tensors must be >= 1 (got %d)", n);
+    int64_t o = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (t[i].numel < 0 || t[i].numel >= kMaxNumel) return fail(Q4_ERR_SHAPE, "tensor %d: bad numel", i);
+        offsets[i] = o;
+        o += (t[i].numel + kChunkElems - 1) / kChunkElems * kChunkElems;
+    }
+    *total = o;
+    return ok();
+}
+
+q4_status q4adamw_accumulate(const q4_config* cfg, const q4_tensor* t, int32_t n, const uint16_t* micro,
+                             int32_t flags, void* ws, size_t ws_bytes, void* stream) {
+    if (!micro) return fail(Q4_ERR_INVALID_ARG, "micro is NULL");
+    if (!aligned16(micro)) return fail(Q4_ERR_ALIGNMENT, "micro is not 16-byte aligned");
+    if (flags & ~(Q4_ACC_FIRST | Q4_ACC_LAST | Q4_ACC_REUSE_TABLE))
+        return fail(Q4_ERR_INVALID_ARG, "unknown accumulate flags 0x%x", flags);
+    Resolved r;
+    Plan P;
+    q4_status s = prepare(cfg, t, n, true, ws, ws_bytes, r, P);
+    if (s != Q4_OK) return s;
+    uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (!(flags & Q4_ACC_REUSE_TABLE) && (s = upload_tables(P, n, wsb, st)) != Q4_OK) return s;
+    const int mode = (flags & Q4_ACC_FIRST) ? GRAD_FIRST : GRAD_ADD;
+    const hipError_t e = launch_grad_pass(mode, (flags & Q4_ACC_LAST) != 0, P.n_mats > 0,
+                                          reinterpret_cast<const DevTensor*>(wsb + P.off_tab),
+                                          reinterpret_cast<const int64_t*>(wsb + P.off_chunks), n, P.total_chunks,
+                                          reinterpret_cast<const DevMatrix*>(wsb + P.off_mats), P.n_mats,
+                                          P.total_tiles, micro, reinterpret_cast<double*>(wsb + P.off_sqpart),
+                                          reinterpret_cast<double*>(wsb + kOffSq), st);
+    if (e != hipSuccess) return hip_fail(e, "accumulate launch");
+    return ok();
+}
+
+q4_status q4adamw_grad_stats(const q4_config* cfg, const q4_tensor* t, int32_t n, void* ws, size_t ws_bytes,
+                             void* stream) {
+    Resolved r;
+    Plan P;
+    q4_status s = prepare(cfg, t, n, true, ws, ws_bytes, r, P);
+    if (s != Q4_OK) return s;
+    uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if ((s = upload_tables(P, n, wsb, st)) != Q4_OK) return s;
+    const hipError_t e = launch_grad_pass(GRAD_STATS_ONLY, true, P.n_mats > 0,
+                                          reinterpret_cast<const DevTensor*>(wsb + P.off_tab),
+                                          reinterpret_cast<const int64_t*>(wsb + P.off_chunks), n, P.total_chunks,
+                                          reinterpret_cast<const DevMatrix*>(wsb + P.off_mats), P.n_mats,
+                                          P.total_tiles, nullptr, reinterpret_cast<double*>(wsb + P.off_sqpart),
+                                          reinterpret_cast<double*>(wsb + kOffSq), st);
+    if (e != hipSuccess) return hip_fail(e, "gradient statistics launch");
+    return ok();
+}
+
+q4_status q4adamw_grad_norm(const void* ws, size_t ws_bytes, double* norm, void* stream) {
+    if (!ws || !norm) return fail(Q4_ERR_INVALID_ARG, "workspace or norm is NULL");
+    if (ws_bytes < 256) return fail(Q4_ERR_WORKSPACE, "workspace has %zu bytes", ws_bytes);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    double sq = 0.0;
+    hipError_t e = hipMemcpyAsync(&sq, reinterpret_cast<const uint8_t*>(ws) + kOffSq, sizeof(double),
+                                  hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "gradient norm copy");
+    *norm = std::sqrt(sq);
     return ok();
 }
 

@@ -16,6 +16,11 @@ constexpr int kWavesPerGroup = 4;      // 256-thread work-groups
 constexpr int kBandRows = 256;         // rows per band of the row/column partial kernel
 constexpr int kTileCols = 512;         // columns per tile (64 lanes x 8 BF16)
 constexpr int kGroup = 256;            // rows (columns) per finalize work-group
+constexpr int kAccGroups = 2048;       // work-groups of the chunk-order accumulation pass (at most)
+
+// Gradient pass modes: read the gradient for its statistics only, copy the
+// microbatch into it, or add the microbatch to it.
+enum GradMode : int { GRAD_STATS_ONLY = 0, GRAD_FIRST = 1, GRAD_ADD = 2 };
 
 enum Kind : int32_t { KIND_PACKED = 0, KIND_FACTORED = 1, KIND_FP32 = 2 };
 
@@ -56,7 +61,8 @@ struct alignas(16) DevMatrix {
     int64_t n_ctiles, n_bands;
     int64_t rgroup_begin, n_rgroups;
     int64_t cgroup_begin, n_cgroups;
-    int64_t pad[3];
+    int64_t flat_off;    // element offset of this matrix in a flat microbatch gradient buffer
+    int64_t pad[2];
 };
 static_assert(sizeof(DevMatrix) == 160, "DevMatrix layout");
 
@@ -68,6 +74,7 @@ struct StepScalars {
     uint32_t lm_head_sr;  // final-phase flag
     uint32_t m_sr_all;    // every tensor rounds m by SR
     uint32_t eden;        // EDEN rescale of packed v
+    const float* clip;    // device: gradient clip factor, or NULL (no clipping)
 };
 
 // Kernel variants that exist (m codebook, v codebook, v rule).
@@ -78,8 +85,20 @@ hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevT
                              hipStream_t stream);
 hipError_t launch_fp32_step(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
                             int n_tensors, int64_t total_chunks, hipStream_t stream);
+// K2 (skipped when the partials are already in the workspace), K3a, K3b.
 hipError_t launch_factored_stats(const DevMatrix* d_mats, int n_mats, int64_t total_tiles, int64_t total_rgroups,
-                                 int64_t total_cgroups, float beta2, float omb2, hipStream_t stream);
+                                 int64_t total_cgroups, float beta2, float omb2, const float* clip, bool partials_ready,
+                                 hipStream_t stream);
+// One pass over the gradients: mode GradMode; with `last` it also leaves the
+// factored row/column partials of matrices (when `tiles_for_matrices`) and
+// the binary64 sums of squares in sq_part (kAccGroups + total_tiles slots),
+// then their total in *sq.
+hipError_t launch_grad_pass(int mode, bool last, bool tiles_for_matrices, const DevTensor* d_tab,
+                            const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks, const DevMatrix* d_mats,
+                            int n_mats, int64_t total_tiles, const uint16_t* micro, double* sq_part, double* sq,
+                            hipStream_t stream);
+// *clip = min(1, max_norm / (sqrt(*sq) + 1e-6)) rounded to FP32.
+hipError_t launch_clip_factor(const double* sq, float max_norm, float* clip, hipStream_t stream);
 hipError_t launch_fill(void* p, size_t bytes, uint8_t value, hipStream_t stream);
 hipError_t launch_dequant(int mcb, int vcb, const DevTensor& t, int64_t rows, float* m_out, float* v_out,
                           double* ws_partials, float* ws_inv, hipStream_t stream);

@@ -430,6 +430,12 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
             }
         }
     }
+    if (sc.clip) {
+        // the clipped gradient (one FP32 product per element)
+        const float gs = *sc.clip;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) g[k] *= gs;
+    }
     const float sm_old = (FULL || blk_ok) ? mscales[blk] : 0.0f;
     const float sv_old = ((FULL || blk_ok) && packed_v) ? vscales[blk] : 0.0f;
     // lane `sub` of the row holds level(sub) * old scale: decoding is one
@@ -569,6 +575,8 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     if (FULL || nv == 8) {
         *reinterpret_cast<gptr<uint32_t>>(mcodes + (e0 >> 1)) = mword;
     } else {
+        // nibbles past the end of the tensor stay 0
+        mword &= (1u << (4 * nv)) - 1u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (2 * j < nv) mcodes[(e0 >> 1) + j] = (uint8_t)(mword >> (8 * j));
@@ -666,6 +674,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     if (FULL || nv == 8) {
         *reinterpret_cast<gptr<uint32_t>>(vcodes + (e0 >> 1)) = vword;
     } else {
+        vword &= (1u << (4 * nv)) - 1u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             if (2 * j < nv) vcodes[(e0 >> 1) + j] = (uint8_t)(vword >> (8 * j));
@@ -760,11 +769,12 @@ __global__ __launch_bounds__(256) void k_fp32_step(const DevTensor* __restrict__
         while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
         const DevTensor T = tab[t];
         const int64_t e0 = (c - T.chunk_begin) * kChunkElems + lane * 8;
+        const float gs = sc.clip ? *sc.clip : 1.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int64_t i = e0 + k;
             if (i < T.numel) {
-                const float g = bf16_to_f32(T.grad[i]);
+                const float g = bf16_to_f32(T.grad[i]) * gs;
                 const float mm = __builtin_fmaf(sc.beta1, T.m32[i], sc.omb1 * g);
                 const float vv = __builtin_fmaf(sc.beta2, T.v32[i], sc.omb2 * (g * g));
                 const float denom = __builtin_fmaf(sqrtf(vv), sc.rsbc2, sc.eps);
@@ -834,7 +844,34 @@ __device__ __forceinline__ int find_matrix(const DevMatrix* mats, int n, int64_t
 // w, w+4, ... of the band.  Column partials stay in registers (binary64)
 // and are combined across the 4 waves in LDS; each row's partial over the
 // tile is a wavefront butterfly.  No atomics: the order is fixed.
-__global__ __launch_bounds__(256) void k_rowcol_partial(const DevMatrix* __restrict__ mats, int n_mats) {
+// FP32 -> BF16 bits, round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x0040u;
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+// Two BF16 values packed in a word: acc <- micro (FIRST), bf16(acc + micro)
+// (ADD) or acc (statistics only).
+template <int MODE> __device__ __forceinline__ uint32_t grad_pair(uint32_t acc, uint32_t micro) {
+    if constexpr (MODE == GRAD_STATS_ONLY) return acc;
+    if constexpr (MODE == GRAD_FIRST) return micro;
+    const uint32_t lo = f32_to_bf16_rne(bf16_to_f32(acc & 0xFFFFu) + bf16_to_f32(micro & 0xFFFFu));
+    const uint32_t hi = f32_to_bf16_rne(bf16_to_f32(acc >> 16) + bf16_to_f32(micro >> 16));
+    return lo | (hi << 16);
+}
+
+// K2 (MODE = GRAD_STATS_ONLY), or the last microbatch's accumulation pass
+// for the factored matrices (FIRST / ADD): a band of 256 rows x a tile of 512
+// columns per work-group; wave w takes rows w, w+4, ... of the band.  Column
+// partials stay in registers (binary64) and are combined across the 4 waves
+// in LDS; each row's partial over the tile is a wavefront butterfly.  No
+// atomics: the order is fixed.  With sq_part the work-group also leaves the
+// binary64 sum of its squares (its rows' partials, wave by wave) at
+// sq_part[tile].
+template <int MODE>
+__global__ __launch_bounds__(256) void k_rowcol_partial(const DevMatrix* __restrict__ mats, int n_mats,
+                                                         const uint16_t* __restrict__ micro,
+                                                         double* __restrict__ sq_part) {
     __shared__ double lds[kWavesPerGroup][kTileCols];
     const int64_t tile = blockIdx.x;
     const int mi = find_matrix(mats, n_mats, tile, 0);
@@ -851,26 +888,36 @@ __global__ __launch_bounds__(256) void k_rowcol_partial(const DevMatrix* __restr
     double col[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) col[k] = 0.0;
+    double sq_wave = 0.0;
     // rows r0 + wave, r0 + wave + 4, ...; four rows' loads are issued before
     // any of them is reduced, so each wave keeps four loads in flight
-    const gptr<const uint16_t> grad = G(M.grad);
+    const gptr<uint16_t> grad = G(const_cast<uint16_t*>(M.grad));
+    const gptr<const uint16_t> mic = G(micro + (MODE == GRAD_STATS_ONLY ? 0 : M.flat_off));
     constexpr int U = 4;
     for (int64_t rb = r0 + wave; rb < r1; rb += U * kWavesPerGroup) {
-        u32x4 q[U];
+        u32x4 q[U], mq[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t r = rb + (int64_t)u * kWavesPerGroup;
             q[u] = u32x4{0u, 0u, 0u, 0u};
+            mq[u] = u32x4{0u, 0u, 0u, 0u};
             if (r < r1) {
-                const gptr<const uint16_t> gp = grad + r * M.cols + c0;
+                const int64_t off = r * M.cols + c0;
                 if (vec) {
-                    q[u] = *reinterpret_cast<const gptr<const u32x4>>(gp);
+                    if constexpr (MODE != GRAD_FIRST) q[u] = *reinterpret_cast<const gptr<const u32x4>>(grad + off);
+                    if constexpr (MODE != GRAD_STATS_ONLY) mq[u] = *reinterpret_cast<const gptr<const u32x4>>(mic + off);
                 } else {
-                    uint32_t w[4] = {0u, 0u, 0u, 0u};
+                    uint32_t w[4] = {0u, 0u, 0u, 0u}, mw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-                    for (int k = 0; k < 8; ++k)
-                        if (k < ncv) w[k >> 1] |= (uint32_t)gp[k] << (16 * (k & 1));
+                    for (int k = 0; k < 8; ++k) {
+                        if (k < ncv) {
+                            if constexpr (MODE != GRAD_FIRST) w[k >> 1] |= (uint32_t)grad[off + k] << (16 * (k & 1));
+                            if constexpr (MODE != GRAD_STATS_ONLY)
+                                mw[k >> 1] |= (uint32_t)mic[off + k] << (16 * (k & 1));
+                        }
+                    }
                     q[u] = u32x4{w[0], w[1], w[2], w[3]};
+                    mq[u] = u32x4{mw[0], mw[1], mw[2], mw[3]};
                 }
             }
         }
@@ -878,7 +925,20 @@ __global__ __launch_bounds__(256) void k_rowcol_partial(const DevMatrix* __restr
         for (int u = 0; u < U; ++u) {
             const int64_t r = rb + (int64_t)u * kWavesPerGroup;
             if (r >= r1) break;  // wave-uniform
-            const uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+            uint32_t w[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+            if constexpr (MODE != GRAD_STATS_ONLY) {
+                const uint32_t mw[4] = {mq[u].x, mq[u].y, mq[u].z, mq[u].w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k) w[k] = grad_pair<MODE>(w[k], mw[k]);
+                const int64_t off = r * M.cols + c0;
+                if (vec) {
+                    *reinterpret_cast<gptr<u32x4>>(grad + off) = u32x4{w[0], w[1], w[2], w[3]};
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        if (k < ncv) grad[off + k] = (uint16_t)(w[k >> 1] >> (16 * (k & 1)));
+                }
+            }
             double d[8];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -891,6 +951,7 @@ __global__ __launch_bounds__(256) void k_rowcol_partial(const DevMatrix* __restr
             const double rp = ((d[0] + d[1]) + (d[2] + d[3])) + ((d[4] + d[5]) + (d[6] + d[7]));
             const double rs = wave_sum_d(rp);
             if (lane == 0) M.part_row[ctile * M.rows + r] = rs;
+            sq_wave += rs;
         }
     }
 #pragma unroll
@@ -905,15 +966,112 @@ __global__ __launch_bounds__(256) void k_rowcol_partial(const DevMatrix* __restr
             }
         }
     }
+    if (sq_part) {
+        __syncthreads();
+        if (lane == 0) lds[0][wave] = sq_wave;
+        __syncthreads();
+        if (threadIdx.x == 0) sq_part[tile] = ((lds[0][0] + lds[0][1]) + lds[0][2]) + lds[0][3];
+    }
+}
+
+// The accumulation / statistics pass in chunk order over every tensor (but
+// the factored matrices when skip_factored: the tile kernel above takes
+// them), grid-stride over tensor-aligned chunks of 512 elements, lane l on
+// elements 8l .. 8l+7.  micro holds the microbatch gradients flat: tensor i
+// at element 512 * chunk_begin(i).  With LAST each lane keeps a binary64 sum
+// of its squares over its chunks; the work-group leaves the sum of its four
+// waves at sq_part[blockIdx.x].
+template <int MODE, bool LAST>
+__global__ __launch_bounds__(256) void k_grad_chunks(const DevTensor* __restrict__ tab,
+                                                      const int64_t* __restrict__ chunk_begin, int n_tensors,
+                                                      int64_t total_chunks, int skip_factored,
+                                                      const uint16_t* __restrict__ micro,
+                                                      double* __restrict__ sq_part) {
+    __shared__ double lds[kWavesPerGroup];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    double sq = 0.0;
+    int t = first_tensor(chunk_begin, n_tensors, (int64_t)blockIdx.x * kWavesPerGroup + wave);
+    for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks;
+         c += (int64_t)gridDim.x * kWavesPerGroup) {
+        while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
+        const DevTensor T = tab[t];
+        if (skip_factored && T.kind == KIND_FACTORED) continue;
+        const int64_t lc = c - T.chunk_begin;
+        const int64_t e0 = lc * kChunkElems + lane * 8;
+        const int64_t rem = T.numel - e0;
+        const int nv = rem >= 8 ? 8 : (rem > 0 ? (int)rem : 0);
+        const gptr<uint16_t> gp = G(const_cast<uint16_t*>(T.grad)) + e0;
+        const gptr<const uint16_t> mp = G(micro + (MODE == GRAD_STATS_ONLY ? 0 : T.chunk_begin * kChunkElems)) + e0;
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if (nv == 8) {
+            u32x4 q = u32x4{0u, 0u, 0u, 0u}, m = u32x4{0u, 0u, 0u, 0u};
+            if constexpr (MODE != GRAD_FIRST) q = *reinterpret_cast<const gptr<const u32x4>>(gp);
+            if constexpr (MODE != GRAD_STATS_ONLY) m = *reinterpret_cast<const gptr<const u32x4>>(mp);
+            w[0] = grad_pair<MODE>(q.x, m.x);
+            w[1] = grad_pair<MODE>(q.y, m.y);
+            w[2] = grad_pair<MODE>(q.z, m.z);
+            w[3] = grad_pair<MODE>(q.w, m.w);
+            if constexpr (MODE != GRAD_STATS_ONLY) *reinterpret_cast<gptr<u32x4>>(gp) = u32x4{w[0], w[1], w[2], w[3]};
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                if (k < nv) {
+                    const uint32_t x = MODE != GRAD_FIRST ? (uint32_t)gp[k] : 0u;
+                    const uint32_t y = MODE != GRAD_STATS_ONLY ? (uint32_t)mp[k] : 0u;
+                    const uint32_t o = grad_pair<MODE>(x, y) & 0xFFFFu;
+                    if constexpr (MODE != GRAD_STATS_ONLY) gp[k] = (uint16_t)o;
+                    w[k >> 1] |= o << (16 * (k & 1));
+                }
+            }
+        }
+        if constexpr (LAST) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float x = bf16_to_f32(w[k] & 0xFFFFu), y = bf16_to_f32(w[k] >> 16);
+                sq += (double)(x * x);
+                sq += (double)(y * y);
+            }
+        }
+    }
+    if constexpr (LAST) {
+        const double wsum = wave_sum_d(sq);
+        if (lane == 0) lds[wave] = wsum;
+        __syncthreads();
+        if (threadIdx.x == 0) sq_part[blockIdx.x] = ((lds[0] + lds[1]) + lds[2]) + lds[3];
+    }
+}
+
+// Total of the partial sums of squares: thread t adds slots t, t+256, ... in
+// order, then a fixed tree over the threads.
+__global__ __launch_bounds__(256) void k_sq_total(const double* __restrict__ part, int64_t n,
+                                                   double* __restrict__ out) {
+    __shared__ double lds[256];
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < n; i += 256) s += part[i];
+    const double tot = group_sum_d(s, lds);
+    if (threadIdx.x == 0) *out = tot;
+}
+
+// Clip factor as torch.nn.utils.clip_grad_norm_ forms it, in binary64 (IEEE
+// square root and division), rounded to FP32.
+__global__ void k_clip_factor(const double* __restrict__ sq, float max_norm, float* __restrict__ clip) {
+    if (threadIdx.x == 0) {
+        const double c = (double)max_norm / (sqrt(*sq) + 1e-6);
+        *clip = c < 1.0 ? (float)c : 1.0f;
+    }
 }
 
 // K3a: finalize rows (first total_rgroups groups) and columns (the rest).
 // R_r <- b2 R_r + (1-b2) (row sum / cols), C_c likewise with rows; each row
 // group also leaves the binary64 sum of its updated R for the mean.
 __global__ __launch_bounds__(256) void k_rowcol_finalize(const DevMatrix* __restrict__ mats, int n_mats,
-                                                          int64_t total_rgroups, float beta2, float omb2) {
+                                                          int64_t total_rgroups, float beta2, float omb2,
+                                                          const float* __restrict__ clip) {
     __shared__ double lds[256];
     const int64_t g = blockIdx.x;
+    // clipped gradient: its sums of squares are s^2 times the gathered ones
+    const double s2 = clip ? (double)*clip * (double)*clip : 1.0;
     if (g < total_rgroups) {
         const int mi = find_matrix(mats, n_mats, g, 1);
         const DevMatrix M = mats[mi];
@@ -923,7 +1081,7 @@ __global__ __launch_bounds__(256) void k_rowcol_finalize(const DevMatrix* __rest
         if (r < M.rows) {
             double rs = 0.0;
             for (int64_t ct = 0; ct < M.n_ctiles; ++ct) rs += M.part_row[ct * M.rows + r];
-            const float Rn = beta2 * M.R[r] + omb2 * ((float)rs / (float)M.cols);
+            const float Rn = beta2 * M.R[r] + omb2 * ((float)(rs * s2) / (float)M.cols);
             M.R[r] = Rn;
             mine = (double)Rn;
         }
@@ -945,7 +1103,7 @@ __global__ __launch_bounds__(256) void k_rowcol_finalize(const DevMatrix* __rest
             }
             for (int j = 0; b < M.n_bands; ++b, ++j) a[j] += M.part_col[b * M.cols + cidx];
             const double cs = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
-            M.C[cidx] = beta2 * M.C[cidx] + omb2 * ((float)cs / (float)M.rows);
+            M.C[cidx] = beta2 * M.C[cidx] + omb2 * ((float)(cs * s2) / (float)M.rows);
         }
     }
 }
@@ -1083,16 +1241,78 @@ hipError_t launch_fp32_step(const StepScalars& sc, const DevTensor* d_tab, const
 }
 
 hipError_t launch_factored_stats(const DevMatrix* d_mats, int n_mats, int64_t total_tiles, int64_t total_rgroups,
-                                 int64_t total_cgroups, float beta2, float omb2, hipStream_t stream) {
+                                 int64_t total_cgroups, float beta2, float omb2, const float* clip, bool partials_ready,
+                                 hipStream_t stream) {
     if (n_mats <= 0) return hipSuccess;
-    k_rowcol_partial<<<(unsigned)total_tiles, 256, 0, stream>>>(d_mats, n_mats);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if (!partials_ready) {
+        k_rowcol_partial<GRAD_STATS_ONLY><<<(unsigned)total_tiles, 256, 0, stream>>>(d_mats, n_mats, nullptr, nullptr);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     k_rowcol_finalize<<<(unsigned)(total_rgroups + total_cgroups), 256, 0, stream>>>(d_mats, n_mats, total_rgroups,
-                                                                                     beta2, omb2);
+                                                                                     beta2, omb2, clip);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_rowcol_mean<<<n_mats, 256, 0, stream>>>(d_mats);
+    return hipGetLastError();
+}
+
+template <int MODE>
+static void launch_grad_mode(bool last, int64_t groups, const DevTensor* d_tab, const int64_t* d_chunk_begin,
+                             int n_tensors, int64_t total_chunks, int skip_factored, const uint16_t* micro,
+                             double* sq_part, hipStream_t stream) {
+    if (last)
+        k_grad_chunks<MODE, true><<<(unsigned)groups, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks,
+                                                                        skip_factored, micro, sq_part);
+    else
+        k_grad_chunks<MODE, false><<<(unsigned)groups, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors,
+                                                                         total_chunks, skip_factored, micro, sq_part);
+}
+
+hipError_t launch_grad_pass(int mode, bool last, bool tiles_for_matrices, const DevTensor* d_tab,
+                            const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks, const DevMatrix* d_mats,
+                            int n_mats, int64_t total_tiles, const uint16_t* micro, double* sq_part, double* sq,
+                            hipStream_t stream) {
+    const bool tiles = last && tiles_for_matrices && n_mats > 0;
+    int64_t groups = 0;
+    if (total_chunks > 0) {
+        groups = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
+        if (groups > kAccGroups) groups = kAccGroups;
+        if (mode == GRAD_STATS_ONLY)
+            launch_grad_mode<GRAD_STATS_ONLY>(last, groups, d_tab, d_chunk_begin, n_tensors, total_chunks, tiles, micro,
+                                              sq_part, stream);
+        else if (mode == GRAD_FIRST)
+            launch_grad_mode<GRAD_FIRST>(last, groups, d_tab, d_chunk_begin, n_tensors, total_chunks, tiles, micro,
+                                         sq_part, stream);
+        else
+            launch_grad_mode<GRAD_ADD>(last, groups, d_tab, d_chunk_begin, n_tensors, total_chunks, tiles, micro,
+                                       sq_part, stream);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (tiles) {
+        double* tile_sq = sq_part + groups;
+        if (mode == GRAD_STATS_ONLY)
+            k_rowcol_partial<GRAD_STATS_ONLY><<<(unsigned)total_tiles, 256, 0, stream>>>(d_mats, n_mats, micro,
+                                                                                          tile_sq);
+        else if (mode == GRAD_FIRST)
+            k_rowcol_partial<GRAD_FIRST><<<(unsigned)total_tiles, 256, 0, stream>>>(d_mats, n_mats, micro, tile_sq);
+        else
+            k_rowcol_partial<GRAD_ADD><<<(unsigned)total_tiles, 256, 0, stream>>>(d_mats, n_mats, micro, tile_sq);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (last) {
+        // slots 0 .. groups-1 from the chunk pass, then one per tile
+        k_sq_total<<<1, 256, 0, stream>>>(sq_part, groups + (tiles ? total_tiles : 0), sq);
+        return hipGetLastError();
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_clip_factor(const double* sq, float max_norm, float* clip, hipStream_t stream) {
+    k_clip_factor<<<1, 64, 0, stream>>>(sq, max_norm, clip);
     return hipGetLastError();
 }
 

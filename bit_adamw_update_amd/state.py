@@ -85,24 +85,59 @@ class Q4State:
         return out
 
     def hparams(self, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, eps_sr=0.0, seed=0,
-                lm_head_sr=0, flags=0) -> api.Q4HParams:
-        return api.Q4HParams(lr, beta1, beta2, eps, weight_decay, eps_sr, step, seed, lm_head_sr, flags)
+                lm_head_sr=0, flags=0, max_grad_norm=0.0) -> api.Q4HParams:
+        return api.Q4HParams(lr, beta1, beta2, eps, weight_decay, eps_sr, step, seed, lm_head_sr, flags,
+                             max_grad_norm, 0)
 
-    def step(self, params, grads, step: int, stream=None, **hp) -> None:
+    def _table(self, params, grads) -> bool:
+        """The C tensor list for these buffers; True when the workspace
+        already holds it (the previous call passed the same pointers)."""
         for p, g, b in zip(params, grads, self.bufs):
             if p.dtype != torch.float32 or g.dtype != torch.bfloat16 or p.numel() != b.numel or g.numel() != b.numel:
                 raise ValueError("params must be float32 and grads bfloat16, matching the state's shapes")
             if not (p.is_contiguous() and g.is_contiguous()):
                 raise ValueError("params and grads must be contiguous")
         key = (tuple(p.data_ptr() for p in params), tuple(g.data_ptr() for g in grads), self.ws.data_ptr())
-        flags = hp.pop("flags", 0)
-        if key == self._last_key:
-            flags |= api.HP_REUSE_TABLE
-        else:
+        same = key == self._last_key
+        if not same:
             self._desc = (api.Q4Tensor * len(self.bufs))(*self.describe(params, grads))
+        self._last_key = key
+        return same
+
+    def step(self, params, grads, step: int, stream=None, grad_stats: bool = False, **hp) -> None:
+        """One q4adamw_step.  grad_stats: the workspace holds the statistics
+        of these gradients from accumulate(..., last=True) or grad_stats()."""
+        flags = hp.pop("flags", 0)
+        if self._table(params, grads):
+            flags |= api.HP_REUSE_TABLE
+        if grad_stats:
+            flags |= api.HP_GRAD_STATS
         h = self.hparams(step, flags=flags, **hp)
         api.q4adamw_step(self.cfg, h, self._desc, self.ws, self.ws_bytes, stream)
-        self._last_key = key
+
+    def flat_offsets(self) -> tuple[list, int]:
+        """Element offsets of each tensor in a flat microbatch gradient buffer, and its length."""
+        return api.q4adamw_flat_offsets(self.describe(None, None))
+
+    def accumulate(self, params, grads, micro, first: bool, last: bool, stream=None) -> None:
+        """grads <- micro (first) or bf16(grads + micro), from the flat BF16
+        microbatch buffer `micro`; with last, also the statistics."""
+        if micro.dtype != torch.bfloat16 or not micro.is_contiguous():
+            raise ValueError("micro must be a contiguous bfloat16 buffer")
+        _, total = self.flat_offsets()
+        if micro.numel() < total:
+            raise ValueError(f"micro holds {micro.numel()} elements, the flat layout needs {total}")
+        flags = (api.ACC_FIRST if first else 0) | (api.ACC_LAST if last else 0)
+        if self._table(params, grads):
+            flags |= api.ACC_REUSE_TABLE
+        api.q4adamw_accumulate(self.cfg, self._desc, micro, flags, self.ws, self.ws_bytes, stream)
+
+    def grad_stats(self, params, grads, stream=None) -> None:
+        self._table(params, grads)
+        api.q4adamw_grad_stats(self.cfg, self._desc, self.ws, self.ws_bytes, stream)
+
+    def grad_norm(self, stream=None) -> float:
+        return api.q4adamw_grad_norm(self.ws, self.ws_bytes, stream)
 
     def dequant(self, i: int, stream=None):
         b = self.bufs[i]

@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define Q4ADAMW_ABI_VERSION 1u
+#define Q4ADAMW_ABI_VERSION 2u
 #define Q4ADAMW_LAYOUT_VERSION 1u
 #define Q4ADAMW_BLOCK 128
 #define Q4ADAMW_MAX_NDIM 8
@@ -112,11 +112,18 @@ typedef struct {
     uint64_t seed;       /* Philox key */
     uint32_t lm_head_sr; /* 1 during the final-10% phase: tensors flagged Q4_TF_LM_HEAD round m by SR */
     uint32_t flags;      /* Q4_HP_* */
+    float max_grad_norm; /* > 0: clip the gradients to this global L2 norm (see q4adamw_step); 0: off */
+    uint32_t reserved;   /* 0 */
 } q4_hparams;
 
 #define Q4_HP_REUSE_TABLE 1u      /* the workspace already holds this exact tensor list from the previous
-                                     q4adamw_step with the same configuration: skip its upload */
+                                     q4adamw_step or q4adamw_accumulate with the same configuration: skip
+                                     its upload */
 #define Q4_HP_CHECK_POINTERS 2u   /* also check that every pointer lives on the current device */
+#define Q4_HP_GRAD_STATS 4u       /* the workspace holds the statistics of exactly these gradients, left by
+                                     q4adamw_accumulate (Q4_ACC_LAST) or q4adamw_grad_stats with this
+                                     tensor list and configuration: the step uses them and does not read the
+                                     gradients a second time */
 
 #define Q4_TF_LM_HEAD 1u          /* tensor is the LM head (its m switches to SR when lm_head_sr = 1) */
 
@@ -209,12 +216,18 @@ q4_status q4adamw_init_state(const q4_config* cfg, const q4_tensor* t, int32_t n
 
 /* One fused AdamW step over all tensors ([N] AdamW paragraph; [A] "State
  * representation"; [P] Table 1, Table 2).  Per 128-element block: decode m
- * and v, form m1 = b1 m0 + (1-b1) g and v1 = b2 v0 + (1-b2) g^2 (or the
- * factored estimate (R_r C_c)/mean(R) for matrices of the factored recipe,
- * after R and C take their own EMA of this step's row/column means of g^2),
- * update the weight p <- p decay - step_size m1 / (sqrt(v1) rsbc2 + eps)
- * from the unquantized m1, v1, then requantize: absmax scales, the m rule
- * (RTN, or SR for the LM head in the final phase), the v rule, EDEN.
+ * and v, form m1 = b1 m0 + (1-b1) g and v1 = b2 v0 + (1-b2) g^2 (each one
+ * fused multiply-add onto the rounded gradient term; or the factored
+ * estimate (R_r C_c)/mean(R) for matrices of the factored recipe, after R
+ * and C take their own EMA of this step's row/column means of g^2), update
+ * the weight p <- p decay - step_size m1 / (sqrt(v1) rsbc2 + eps) from the
+ * unquantized m1, v1, then requantize: absmax scales, the m rule (RTN, or
+ * SR for the LM head in the final phase), the v rule, EDEN.
+ * Clipping (hp->max_grad_norm > 0): s = min(1, max_grad_norm / (norm +
+ * 1e-6)) in binary64, rounded to FP32, from the global norm of the
+ * gradients (the statistics in ws with Q4_HP_GRAD_STATS, else gathered
+ * first by one read of the gradients); every gradient element is multiplied
+ * by s before use and the factored row/column sums of g^2 by s^2.
  * Stochastic rounding draws Philox4x32-10 with counter (i/4, step,
  * tensor_id, stream 0 for m / 1 for v), key (seed), word i mod 4.
  * `ws` (device, ws_bytes >= q4adamw_workspace_bytes) holds the tensor table
@@ -222,6 +235,44 @@ q4_status q4adamw_init_state(const q4_config* cfg, const q4_tensor* t, int32_t n
  * overlaps on the device. */
 q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tensor* t, int32_t n_tensors,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* ---- the step before: gradient accumulation, norm, clipping ------------
+ * [A] "State representation": microbatches stream into BF16 gradient shards
+ * (no FP32 main gradient), and the gradient norm and clipping work on those
+ * BF16 shards.  A microbatch's gradients arrive as one flat device buffer
+ * of BF16 values in which tensor i starts at element offsets[i] =
+ * 512 * sum_{j<i} ceil(numel_j / 512) (q4adamw_flat_offsets); the elements
+ * between tensors are not read. */
+
+#define Q4_ACC_FIRST 1        /* first microbatch: grad <- micro (instead of adding) */
+#define Q4_ACC_LAST 2         /* last microbatch: also leave the gradients' statistics in ws */
+#define Q4_ACC_REUSE_TABLE 4  /* as Q4_HP_REUSE_TABLE */
+
+/* offsets[i] (host, n_tensors entries) and *total (elements of the flat
+ * buffer) of the flat microbatch layout above. */
+q4_status q4adamw_flat_offsets(const q4_tensor* t, int32_t n_tensors, int64_t* offsets, int64_t* total);
+
+/* Accumulate one microbatch into the BF16 gradient buffers t[i].grad
+ * (device, written in place although q4_tensor declares them const): per
+ * element g <- bf16(f32(g) + f32(micro)), rounded to nearest even, or
+ * g <- micro with Q4_ACC_FIRST.  With Q4_ACC_LAST the same pass leaves in
+ * `ws` the statistics of the accumulated gradients: their binary64 sum of
+ * squares over all tensors and, for the matrices of the factored recipe,
+ * the per-row and per-column partial sums of g^2 that q4adamw_step would
+ * otherwise gather with a second read of the gradients.  `micro` (device):
+ * the flat microbatch buffer.  `ws`: as for q4adamw_step, the same buffer
+ * the step will get. */
+q4_status q4adamw_accumulate(const q4_config* cfg, const q4_tensor* t, int32_t n_tensors, const uint16_t* micro,
+                             int32_t flags, void* ws, size_t ws_bytes, void* stream);
+
+/* The statistics of Q4_ACC_LAST for gradients accumulated elsewhere (one
+ * read of every gradient). */
+q4_status q4adamw_grad_stats(const q4_config* cfg, const q4_tensor* t, int32_t n_tensors, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* The global L2 norm sqrt(sum of squares) from the statistics in ws:
+ * waits for `stream`, then stores it to *norm (host). */
+q4_status q4adamw_grad_norm(const void* ws, size_t ws_bytes, double* norm, void* stream);
 
 /* Decode one tensor's state to FP32 (device m_out, v_out of numel floats,
  * 16-byte aligned): m = L_m[code] s_m; v = L_v[code] s_v, or

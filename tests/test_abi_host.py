@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings():
-    assert q4.q4adamw_abi_version() == 1
+    assert q4.q4adamw_abi_version() == 2 == q4.api.ABI_VERSION
     assert q4.q4adamw_status_string(0) == "ok"
     assert "workspace" in q4.q4adamw_status_string(7)
 
@@ -61,7 +61,7 @@ def test_default_configs_follow_table2():
         q4.CB_NF4, q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 1)
     f = q4.q4adamw_default_config(q4.RECIPE_FACTORED)
     assert (f.v_codebook, f.v_rule, f.eden) == (q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, 0)
-    assert f.block == 128 and f.abi_version == 1
+    assert f.block == 128 and f.abi_version == 2
 
 
 @pytest.mark.parametrize("step", [1, 2, 10, 1000, 123456789])
@@ -97,7 +97,7 @@ def fake_tensor(shape, tid=0, base=0x10000, fp32=False, factored=False):
 
 def hp(**kw):
     d = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, eps_sr=0.0, step=1, seed=0,
-             lm_head_sr=0, flags=0)
+             lm_head_sr=0, flags=0, max_grad_norm=0.0, reserved=0)
     d.update(kw)
     return q4.Q4HParams(*[d[k] for k, _ in q4.Q4HParams._fields_])
 
@@ -122,6 +122,9 @@ def test_validation_errors():
     assert status_of(V, cfg, hp(beta2=-0.1), [good]) == 1
     assert status_of(V, cfg, hp(eps=0.0), [good]) == 1
     assert status_of(V, cfg, hp(lr=float("nan")), [good]) == 1
+    assert status_of(V, cfg, hp(max_grad_norm=-1.0), [good]) == 1
+    assert status_of(V, cfg, hp(max_grad_norm=float("inf")), [good]) == 1
+    q4.q4adamw_validate(cfg, hp(max_grad_norm=1.0), [good])
     bad = fake_tensor((100, 7)); bad.numel = 701
     assert status_of(V, cfg, hp(), [bad]) == 2
     bad = fake_tensor((100, 7)); bad.ndim = 9
@@ -213,3 +216,11 @@ def test_product_path_has_no_oracle_dependency():
             api.load_library(os.path.join(ROOT, "does_not_exist.so"))
         finally:
             api._lib = api._lib_saved
+
+
+def test_flat_offsets_of_the_microbatch_layout():
+    """Tensor i starts at 512 * sum_{j<i} ceil(numel_j / 512)."""
+    ts = [fake_tensor((1000,)), fake_tensor((3, 5)), fake_tensor((512,)), fake_tensor((7, 129))]
+    offs, total = q4.q4adamw_flat_offsets(ts)
+    assert offs == [0, 1024, 1536, 2048]
+    assert total == 2048 + 1024
