@@ -111,6 +111,51 @@ def time_workload(workload, recipe: str, steps: int, warmup: int, lm_head_phase:
     return out
 
 
+def time_step_before(workload, recipe: str, steps: int, warmup: int, max_grad_norm: float = 0.0):
+    """The step before on the same tensors: one accumulation pass of a BF16
+    microbatch with the statistics (q4adamw_accumulate, Q4_ACC_LAST), then
+    the step that reuses them (Q4_HP_GRAD_STATS; clipping when
+    max_grad_norm > 0).  Returns the average duration of each, in ms."""
+    import torch
+
+    import bit_adamw_update_amd as q4
+
+    dev = torch.device("cuda")
+    params = [p.reshape(-1) for p in workload.init_params(dev)]
+    consts = workload._tensor_consts(dev)
+    grads = [g.reshape(-1).contiguous() for g in workload.grads(1, dev, consts)]
+    state = q4.Q4State(recipe, workload.tensors, device=dev)
+    _, total = state.flat_offsets()
+    micro = torch.empty(total, dtype=torch.bfloat16, device=dev)
+    off = 0
+    for g in workload.grads(2, dev, consts):
+        n = g.numel()
+        micro[off:off + n].copy_(g.reshape(-1))
+        off += (n + 511) // 512 * 512
+    del consts
+    hp = dict(workload.hp)
+    stream = torch.cuda.current_stream()
+    step = 0
+    for _ in range(warmup):
+        state.accumulate(params, grads, micro, first=False, last=True)
+        step += 1
+        state.step(params, grads, step, grad_stats=True, max_grad_norm=max_grad_norm, **hp)
+    torch.cuda.synchronize()
+    acc_ms, step_ms = [], []
+    for _ in range(steps):
+        a0, a1, s1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        a0.record(stream)
+        state.accumulate(params, grads, micro, first=False, last=True)
+        a1.record(stream)
+        step += 1
+        state.step(params, grads, step, grad_stats=True, max_grad_norm=max_grad_norm, **hp)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        acc_ms.append(a0.elapsed_time(a1))
+        step_ms.append(a1.elapsed_time(s1))
+    return sum(acc_ms) / len(acc_ms), sum(step_ms) / len(step_ms)
+
+
 def copy_ceiling_gbs(nbytes: int = 4 << 30) -> float:
     """A plain device copy of the same order of bytes: the practical ceiling."""
     import torch
@@ -255,6 +300,21 @@ def main():
                 "alg_bytes_per_param": (b2 + extra) / w2.numel}
             log(f"{wname}/{rec}: {variants[f'{wname}/{rec}']}")
             del v
+            torch.cuda.empty_cache()
+        # the step before ([A] "State representation"): accumulation pass with
+        # statistics, then the step that reuses them (no second gradient read)
+        for wname, rec, clip in (("qwen3-0.6b-factored", "factored", 0.0), ("gpt-2.7b", "zip_sr", 1.0)):
+            w2 = inputs.WORKLOADS[wname]()
+            acc_ms, st_ms = time_step_before(w2, rec, args.steps, args.warmup, max_grad_norm=clip)
+            b2 = alg_bytes(w2, rec)
+            acc_bytes = 6 * w2.numel   # read the BF16 gradient and the microbatch, write the gradient
+            key = f"{wname}/{rec}+accumulated-stats" + ("+clip" if clip else "")
+            variants[key] = {
+                "params": w2.numel, "step_launch_ms": st_ms, "step_alg_gbs": b2 / (st_ms * 1e-3) / 1e9,
+                "step_frac_of_peak": b2 / (st_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "step_alg_bytes_per_param": b2 / w2.numel,
+                "accumulate_ms": acc_ms, "accumulate_gbs": acc_bytes / (acc_ms * 1e-3) / 1e9,
+                "max_grad_norm": clip}
+            log(f"{key}: {variants[key]}")
             torch.cuda.empty_cache()
         result["variants"] = variants
 

@@ -218,9 +218,6 @@ q4_status check_all_pointers(const q4_tensor* t, int32_t n) {
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Workspace layout of a step.
-// Workspace bytes 0..255: the gradient statistics' sum of squares (binary64,
-// offset 0) and the clip factor (FP32, offset 8).
-constexpr size_t kOffSq = 0, kOffClip = 8;
 
 struct Plan {
     size_t off_tab, off_chunks, off_mats, off_inv, off_prow, off_pcol, off_pmean, off_sqpart, total;
@@ -289,7 +286,7 @@ void plan_layout(const Resolved& r, const q4_tensor* t, int32_t n, Plan& P, uint
     }
     P.chunks[n] = P.total_chunks;
     P.n_mats = (int)P.mats.size();
-    size_t o = 256;
+    size_t o = kWsOffTable;
     P.off_tab = o;       o = round256(o + sizeof(DevTensor) * n);
     P.off_chunks = o;    o = round256(o + sizeof(int64_t) * (n + 1));
     P.off_mats = o;      o = round256(o + sizeof(DevMatrix) * P.mats.size());
@@ -586,18 +583,16 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
     sc.step = (uint32_t)hp->step;
     sc.key0 = (uint32_t)hp->seed;
     sc.key1 = (uint32_t)(hp->seed >> 32);
-    sc.lm_head_sr = hp->lm_head_sr ? 1u : 0u;
-    sc.m_sr_all = (uint32_t)r.m_sr_all;
-    sc.eden = (uint32_t)r.eden;
-    sc.clip = nullptr;
+    sc.flags = (hp->lm_head_sr ? SF_LM_HEAD_SR : 0u) | (r.m_sr_all ? SF_M_SR_ALL : 0u) | (r.eden ? SF_EDEN : 0u);
+    const float* clip = nullptr;
 
     const DevTensor* d_tab = reinterpret_cast<const DevTensor*>(wsb + P.off_tab);
     const int64_t* d_chunks = reinterpret_cast<const int64_t*>(wsb + P.off_chunks);
     const DevMatrix* d_mats = reinterpret_cast<const DevMatrix*>(wsb + P.off_mats);
     bool stats_ready = (hp->flags & Q4_HP_GRAD_STATS) != 0;
     if (hp->max_grad_norm > 0.0f) {
-        double* sq = reinterpret_cast<double*>(wsb + kOffSq);
-        float* clip = reinterpret_cast<float*>(wsb + kOffClip);
+        double* sq = reinterpret_cast<double*>(wsb + kWsOffSq);
+        float* clipw = reinterpret_cast<float*>(wsb + kWsOffClip);
         if (!stats_ready) {
             // one read of the gradients: their norm and, for factored
             // matrices, the row/column partials the step needs anyway
@@ -607,9 +602,10 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
             if (e != hipSuccess) return hip_fail(e, "gradient statistics launch");
             stats_ready = true;
         }
-        e = launch_clip_factor(sq, hp->max_grad_norm, clip, st);
+        e = launch_clip_factor(sq, hp->max_grad_norm, clipw, st);
         if (e != hipSuccess) return hip_fail(e, "clip factor launch");
-        sc.clip = clip;
+        sc.flags |= SF_CLIP;
+        clip = clipw;
     }
     if (r.recipe == Q4_RECIPE_FP32) {
         e = launch_fp32_step(sc, d_tab, d_chunks, n, P.total_chunks, st);
@@ -618,7 +614,7 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
     }
     if (P.n_mats > 0) {
         e = launch_factored_stats(d_mats, P.n_mats, P.total_tiles, P.total_rgroups, P.total_cgroups, sc.beta2, sc.omb2,
-                                  sc.clip, stats_ready, st);
+                                  clip, stats_ready, st);
         if (e != hipSuccess) return hip_fail(e, "factored statistics launch");
     }
     e = launch_fused_step(r.var, sc, d_tab, d_chunks, n, P.total_chunks, st);
@@ -700,7 +696,7 @@ q4_status q4adamw_accumulate(const q4_config* cfg, const q4_tensor* t, int32_t n
                                           reinterpret_cast<const int64_t*>(wsb + P.off_chunks), n, P.total_chunks,
                                           reinterpret_cast<const DevMatrix*>(wsb + P.off_mats), P.n_mats,
                                           P.total_tiles, micro, reinterpret_cast<double*>(wsb + P.off_sqpart),
-                                          reinterpret_cast<double*>(wsb + kOffSq), st);
+                                          reinterpret_cast<double*>(wsb + kWsOffSq), st);
     if (e != hipSuccess) return hip_fail(e, "accumulate launch");
     return ok();
 }
@@ -719,7 +715,7 @@ q4_status q4adamw_grad_stats(const q4_config* cfg, const q4_tensor* t, int32_t n
                                           reinterpret_cast<const int64_t*>(wsb + P.off_chunks), n, P.total_chunks,
                                           reinterpret_cast<const DevMatrix*>(wsb + P.off_mats), P.n_mats,
                                           P.total_tiles, nullptr, reinterpret_cast<double*>(wsb + P.off_sqpart),
-                                          reinterpret_cast<double*>(wsb + kOffSq), st);
+                                          reinterpret_cast<double*>(wsb + kWsOffSq), st);
     if (e != hipSuccess) return hip_fail(e, "gradient statistics launch");
     return ok();
 }
@@ -729,7 +725,7 @@ q4_status q4adamw_grad_norm(const void* ws, size_t ws_bytes, double* norm, void*
     if (ws_bytes < 256) return fail(Q4_ERR_WORKSPACE, "workspace has %zu bytes", ws_bytes);
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     double sq = 0.0;
-    hipError_t e = hipMemcpyAsync(&sq, reinterpret_cast<const uint8_t*>(ws) + kOffSq, sizeof(double),
+    hipError_t e = hipMemcpyAsync(&sq, reinterpret_cast<const uint8_t*>(ws) + kWsOffSq, sizeof(double),
                                   hipMemcpyDeviceToHost, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);
     if (e != hipSuccess) return hip_fail(e, "gradient norm copy");

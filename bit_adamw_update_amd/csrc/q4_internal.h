@@ -71,11 +71,23 @@ struct StepScalars {
     float beta1, beta2, omb1, omb2, eps, eps_sr, decay, step_size, rsbc2;
     uint32_t step;        // low 32 bits of the step count (Philox counter word)
     uint32_t key0, key1;  // Philox key (seed)
-    uint32_t lm_head_sr;  // final-phase flag
-    uint32_t m_sr_all;    // every tensor rounds m by SR
-    uint32_t eden;        // EDEN rescale of packed v
-    const float* clip;    // device: gradient clip factor, or NULL (no clipping)
+    uint32_t flags;       // SF_*
 };
+enum StepFlags : uint32_t {
+    SF_LM_HEAD_SR = 1u,  // final phase: LM-head tensors round m by SR
+    SF_M_SR_ALL = 2u,    // every tensor rounds m by SR
+    SF_EDEN = 4u,        // EDEN rescale of packed v
+    SF_CLIP = 8u,        // scale the gradients by the clip factor in the workspace
+};
+
+// Workspace layout shared by host and kernels: the first 256 bytes hold the
+// gradient statistics' sum of squares (binary64, offset 0) and the clip
+// factor (FP32, offset 8); the tensor table starts at byte 256, so a kernel
+// that has the table finds the clip factor 248 bytes before it.
+constexpr size_t kWsOffSq = 0, kWsOffClip = 8, kWsOffTable = 256;
+__host__ __device__ inline const float* clip_of_table(const DevTensor* tab) {
+    return reinterpret_cast<const float*>(reinterpret_cast<const char*>(tab) - kWsOffTable + kWsOffClip);
+}
 
 // Kernel variants that exist (m codebook, v codebook, v rule).
 struct Variant { int mcb, vcb, vrule; };

@@ -375,10 +375,10 @@ struct LaneBooks {
     float dec_m, dec_v, lev_v;
 };
 
-template <int MCB, int VCB, int VRULE, bool FULL, bool PACKED>
+template <int MCB, int VCB, int VRULE, bool FULL, bool PACKED, bool CLIP>
 __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc, const int64_t chunk,
                                            const StepScalars& sc, const StepLds<MCB, VCB>& lds,
-                                           const LaneBooks& lb, const int lane) {
+                                           const LaneBooks& lb, const int lane, const float gs) {
     constexpr int NM = Book<MCB>::N, NV = Book<VCB>::N;
     constexpr bool V_SR = VRULE == Q4_RULE_STATE_SR || VRULE == Q4_RULE_UPDATE_SR;
     constexpr bool V_UPD = VRULE == Q4_RULE_UPDATE_SR || VRULE == Q4_RULE_UPDATE_RTN;
@@ -430,9 +430,8 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
             }
         }
     }
-    if (sc.clip) {
+    if constexpr (CLIP) {
         // the clipped gradient (one FP32 product per element)
-        const float gs = *sc.clip;
 #pragma unroll
         for (int k = 0; k < 8; ++k) g[k] *= gs;
     }
@@ -540,7 +539,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(m1[k]));
     const float s_m = row_max16(am);
     const float inv_m = s_m > 0.0f ? 1.0f / s_m : 0.0f;
-    const bool m_sr = sc.m_sr_all || ((T.flags & Q4_TF_LM_HEAD) && sc.lm_head_sr);
+    const bool m_sr = (sc.flags & SF_M_SR_ALL) || ((T.flags & Q4_TF_LM_HEAD) && (sc.flags & SF_LM_HEAD_SR));
     uint32_t mword = 0;
     if (!m_sr) {
 #pragma unroll
@@ -602,7 +601,8 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     };
     uint32_t vword = 0;
     float xx[8], xq[8];
-    if (VRULE == Q4_RULE_UPDATE_SR && VCB == Q4_CB_DYN4 && !sc.eden) {
+    const bool eden = (sc.flags & SF_EDEN) != 0;
+    if (VRULE == Q4_RULE_UPDATE_SR && VCB == Q4_CB_DYN4 && !eden) {
         // ZIP-SR.  Per-row tables, lane k: root_k, root_(k+1) + eps_sr and
         // root_(k+1) - root_k (the same FP32 operations the rule forms per
         // element, done once per level).
@@ -664,7 +664,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
                 }
             }
             idx = lo + ((mv && up) ? 1 : 0);
-            if (sc.eden) q = lds.lev_v[idx];
+            if (eden) q = lds.lev_v[idx];
         }
         vword |= (uint32_t)idx << (4 * k);
         xx[k] = x * x;
@@ -680,7 +680,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
             if (2 * j < nv) vcodes[(e0 >> 1) + j] = (uint8_t)(vword >> (8 * j));
     }
     float stored = s_v;
-    if (sc.eden) {
+    if (eden) {
         // EDEN: S = <x,x> / <x,Q(x)> over the block, pairwise tree in index order
         const float sxx = row_sum16(tree8(xx));
         const float sxq = row_sum16(tree8(xq));
@@ -708,7 +708,7 @@ template <int VRULE> constexpr int step_waves() {
     return (VRULE == Q4_RULE_UPDATE_SR || VRULE == Q4_RULE_UPDATE_RTN) ? 6 : 7;
 }
 
-template <int MCB, int VCB, int VRULE>
+template <int MCB, int VCB, int VRULE, bool CLIP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves<VRULE>())))
 void k_fused_step(const DevTensor* __restrict__ tab,
                                                      const int64_t* __restrict__ chunk_begin, int n_tensors,
@@ -737,6 +737,9 @@ void k_fused_step(const DevTensor* __restrict__ tab,
     __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // clipping is a separate instantiation: the unclipped kernel carries no
+    // trace of it (its live values are what limits occupancy)
+    const float gs = CLIP ? *clip_of_table(tab) : 1.0f;
     int t = first_tensor(chunk_begin, n_tensors, (int64_t)blockIdx.x * kWavesPerGroup + wave);
     for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks;
          c += (int64_t)gridDim.x * kWavesPerGroup) {
@@ -745,11 +748,11 @@ void k_fused_step(const DevTensor* __restrict__ tab,
         const int64_t lc = c - T.chunk_begin;
         const bool full = (lc + 1) * kChunkElems <= T.numel;
         if (T.kind == KIND_PACKED) {
-            if (full) step_chunk<MCB, VCB, VRULE, true, true>(T, lc, c, sc, lds, lb, lane);
-            else step_chunk<MCB, VCB, VRULE, false, true>(T, lc, c, sc, lds, lb, lane);
+            if (full) step_chunk<MCB, VCB, VRULE, true, true, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
+            else step_chunk<MCB, VCB, VRULE, false, true, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
         } else {
-            if (full) step_chunk<MCB, VCB, VRULE, true, false>(T, lc, c, sc, lds, lb, lane);
-            else step_chunk<MCB, VCB, VRULE, false, false>(T, lc, c, sc, lds, lb, lane);
+            if (full) step_chunk<MCB, VCB, VRULE, true, false, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
+            else step_chunk<MCB, VCB, VRULE, false, false, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
         }
     }
 }
@@ -769,7 +772,7 @@ __global__ __launch_bounds__(256) void k_fp32_step(const DevTensor* __restrict__
         while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
         const DevTensor T = tab[t];
         const int64_t e0 = (c - T.chunk_begin) * kChunkElems + lane * 8;
-        const float gs = sc.clip ? *sc.clip : 1.0f;
+        const float gs = (sc.flags & SF_CLIP) ? *clip_of_table(tab) : 1.0f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int64_t i = e0 + k;
@@ -1219,12 +1222,20 @@ bool variant_supported(const Variant& v) {
 hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevTensor* d_tab,
                              const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks, hipStream_t stream) {
     if (total_chunks <= 0) return hipSuccess;
-#define Q4_LAUNCH(A, B, C)                                                                              \
-    if (v.mcb == A && v.vcb == B && v.vrule == C) {                                                     \
-        static std::atomic<int> occ{0};                                                                 \
-        const int grid = step_grid(k_fused_step<A, B, C>, total_chunks, occ);                           \
-        k_fused_step<A, B, C><<<grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, sc); \
-        return hipGetLastError();                                                                       \
+#define Q4_LAUNCH(A, B, C)                                                                                   \
+    if (v.mcb == A && v.vcb == B && v.vrule == C) {                                                          \
+        if (sc.flags & SF_CLIP) {                                                                            \
+            static std::atomic<int> occ{0};                                                                  \
+            const int grid = step_grid(k_fused_step<A, B, C, true>, total_chunks, occ);                      \
+            k_fused_step<A, B, C, true><<<grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, \
+                                                                  sc);                                       \
+        } else {                                                                                             \
+            static std::atomic<int> occ{0};                                                                  \
+            const int grid = step_grid(k_fused_step<A, B, C, false>, total_chunks, occ);                     \
+            k_fused_step<A, B, C, false><<<grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors,          \
+                                                                   total_chunks, sc);                        \
+        }                                                                                                    \
+        return hipGetLastError();                                                                            \
     }
     Q4_VARIANTS(Q4_LAUNCH)
 #undef Q4_LAUNCH
