@@ -102,6 +102,12 @@ def lib():
         L.or_zero_code.argtypes = [i32]
         L.or_zero_code.restype = i32
         L.or_state_bytes.argtypes = [i32, i64, i64, i32, C.POINTER(C.c_uint64)]
+        L.or_codebook8.argtypes = [i32, fp]
+        L.or_sorted_levels8.argtypes = [i32, fp, C.POINTER(C.c_int), fp]
+        L.or_sorted_levels8.restype = i32
+        L.or_step8_window.argtypes = [C.POINTER(_Hp), C.POINTER(_Win)]
+        L.or_step8_window.restype = i32
+        L.or_dequant8_window.argtypes = [C.POINTER(_Win), fp, fp]
         L.or_accumulate_bf16.argtypes = [vp, vp, i64, i32]
         L.or_grad_sumsq.argtypes = [vp, i64]
         L.or_grad_sumsq.restype = C.c_double
@@ -338,3 +344,68 @@ class TensorState:
         return dequant_window(self.cfg, numel=self.numel, base=0, length=self.numel, m_codes=self.m_codes,
                               m_scales=self.m_scales, v_codes=self.v_codes, v_scales=self.v_scales,
                               cols=self.cols, R=self.R, Cc=self.Cc, inv_meanR=self.inv_meanR)
+
+
+# ---------------------------------------------------------------------------
+# 8-bit blockwise AdamW
+# ---------------------------------------------------------------------------
+
+CB8_SDYN8, CB8_DYN8 = 0, 1
+
+
+def codebook8(cb8: int) -> np.ndarray:
+    """Code-indexed 256-entry table: SDyn8 (m) or Dyn8 (v)."""
+    out = np.zeros(256, np.float32)
+    lib().or_codebook8(cb8, _fp(out))
+    return out
+
+
+def sorted_levels8(cb8: int):
+    L = np.zeros(256, np.float32)
+    code = (C.c_int * 256)()
+    mid = np.zeros(255, np.float32)
+    n = lib().or_sorted_levels8(cb8, _fp(L), code, _fp(mid))
+    return L[:n].copy(), np.array(code[:n]), mid[: n - 1].copy()
+
+
+class TensorState8:
+    """Host copy of one tensor's 8-bit state (one byte per code), zero state:
+    codes 0 (both maps decode code 0 to 0), scales +0."""
+
+    def __init__(self, shape, tensor_id: int, flags: int = 0):
+        self.shape = tuple(int(s) for s in shape)
+        self.numel = int(np.prod(self.shape))
+        self.tensor_id = tensor_id
+        self.flags = flags
+        nb = (self.numel + BLOCK - 1) // BLOCK
+        self.m_codes = np.zeros(self.numel, np.uint8)
+        self.v_codes = np.zeros(self.numel, np.uint8)
+        self.m_scales = np.zeros(nb, np.float32)
+        self.v_scales = np.zeros(nb, np.float32)
+
+    def step(self, hp: HParams, param: np.ndarray, grad: np.ndarray, base: int = 0, length: int | None = None):
+        """Step elements [base, base + length) (base a multiple of 128; the
+        arrays passed are the whole tensor's)."""
+        length = self.numel - base if length is None else length
+        b0 = base // BLOCK
+        nb = (length + BLOCK - 1) // BLOCK
+        p = param[base: base + length]
+        g = np.ascontiguousarray(grad[base: base + length])
+        mc = self.m_codes[base: base + length]
+        vc = self.v_codes[base: base + length]
+        ms = self.m_scales[b0: b0 + nb]
+        vs = self.v_scales[b0: b0 + nb]
+        assert p.flags.c_contiguous and mc.flags.c_contiguous
+        w = _Win(self.tensor_id, self.flags, self.numel, 0, base, length, _p(p), _p(g), _p(mc), _p(ms), _p(vc),
+                 _p(vs), None, None, 0.0, None, None)
+        h = hp.c()
+        if lib().or_step8_window(C.byref(h), C.byref(w)) != 0:
+            raise ValueError("oracle: window base must be a multiple of 128")
+
+    def dequant(self):
+        w = _Win(0, 0, self.numel, 0, 0, self.numel, None, None, _p(self.m_codes), _p(self.m_scales),
+                 _p(self.v_codes), _p(self.v_scales), None, None, 0.0, None, None)
+        m = np.zeros(self.numel, np.float32)
+        v = np.zeros(self.numel, np.float32)
+        lib().or_dequant8_window(C.byref(w), _fp(m), _fp(v))
+        return m, v

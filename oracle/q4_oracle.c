@@ -623,3 +623,124 @@ void or_state_bytes(int recipe, int64_t numel, int64_t rows, int is_matrix, uint
     } else { q = 2 * codes; meta = 2 * 4 * nb; }
     out[0] = q; out[1] = meta; out[2] = q + meta;
 }
+
+/* ------------------------------------------------------------------------ */
+/* 8-bit blockwise AdamW ([A] names an 8-bit blockwise AdamW, without        */
+/* factorization, beside the 4-bit optimizer; the two are mutually           */
+/* exclusive)                                                                */
+/* ------------------------------------------------------------------------ */
+/* Readings (the pages give no maps for it): the 8-bit members of the
+ * dynamic-exponent family above, one byte per code.
+ *   SDyn8 (m): bit 7 the sign, bits 0..6 the 7-bit dynamic magnitude; the
+ *              code 0x80 ("-0") decodes to +0 and is never written.
+ *   Dyn8  (v): the 8-bit dynamic map, zero-inclusive.
+ * 128-element blocks, absmax scales (FP32), round to nearest level (ties to
+ * the lower level) in normalized units, the AdamW arithmetic of the 4-bit
+ * step.  Codes: byte i holds element i. */
+enum { OR_CB8_SDYN8 = 0, OR_CB8_DYN8 = 1 };
+
+void or_codebook8(int cb8, float out[256]) {
+    for (int c = 0; c < 256; ++c) {
+        if (cb8 == OR_CB8_DYN8) {
+            out[c] = (float)or_dyn_magnitude(c, 8, 0);
+        } else {
+            float mag = (float)or_dyn_magnitude(c & 127, 7, 0);
+            out[c] = (c & 128) ? -mag : mag;
+        }
+    }
+    if (cb8 == OR_CB8_SDYN8) out[128] = 0.0f;
+}
+
+typedef struct { int n; float L[256]; int code[256]; float mid[255]; } or_levels8;
+
+static void or_make_levels8(int cb8, or_levels8* lv) {
+    float dec[256];
+    or_codebook8(cb8, dec);
+    int n = 0;
+    for (int c = 0; c < 256; ++c) {
+        if (cb8 == OR_CB8_SDYN8 && c == 128) continue;
+        lv->L[n] = dec[c]; lv->code[n] = c; ++n;
+    }
+    for (int i = 1; i < n; ++i)
+        for (int j = i; j > 0 && lv->L[j - 1] > lv->L[j]; --j) {
+            float t = lv->L[j]; lv->L[j] = lv->L[j - 1]; lv->L[j - 1] = t;
+            int tc = lv->code[j]; lv->code[j] = lv->code[j - 1]; lv->code[j - 1] = tc;
+        }
+    lv->n = n;
+    for (int k = 0; k + 1 < n; ++k) lv->mid[k] = (lv->L[k] + lv->L[k + 1]) * 0.5f;
+}
+
+int or_sorted_levels8(int cb8, float L[256], int code[256], float mid[255]) {
+    or_levels8 lv;
+    or_make_levels8(cb8, &lv);
+    memcpy(L, lv.L, sizeof(lv.L));
+    memcpy(code, lv.code, sizeof(lv.code));
+    memcpy(mid, lv.mid, sizeof(lv.mid));
+    return lv.n;
+}
+
+/* Nearest level: the number of midpoints strictly below x (a midpoint goes
+ * to the lower level), found by scanning. */
+static int or_rtn8(const or_levels8* lv, float x) {
+    int idx = 0;
+    while (idx + 1 < lv->n && lv->mid[idx] < x) ++idx;
+    return lv->code[idx];
+}
+
+/* One step over a window of an 8-bit tensor (same window conventions as
+ * or_window; m_codes / v_codes hold one byte per element). */
+int or_step8_window(const or_hparams* hp, const or_window* w) {
+    if (w->base % OR_BLOCK != 0) return -1;
+    float sc[5];
+    or_host_scalars(hp, sc);
+    const float decay = sc[0], step_size = sc[1], rsbc2 = sc[2], omb1 = sc[3], omb2 = sc[4];
+    float Lm[256], Lv[256];
+    or_codebook8(OR_CB8_SDYN8, Lm);
+    or_codebook8(OR_CB8_DYN8, Lv);
+    or_levels8 lvm, lvv;
+    or_make_levels8(OR_CB8_SDYN8, &lvm);
+    or_make_levels8(OR_CB8_DYN8, &lvv);
+    float m1[OR_BLOCK], v1[OR_BLOCK];
+    for (int64_t off = 0; off < w->len; off += OR_BLOCK) {
+        int n = (int)((w->len - off) < OR_BLOCK ? (w->len - off) : OR_BLOCK);
+        int64_t blk = off / OR_BLOCK;
+        for (int k = 0; k < n; ++k) {
+            int64_t j = off + k;
+            float g = or_bf16_to_f32(w->grad[j]) * hp->grad_scale;
+            float m0 = Lm[w->m_codes[j]] * w->m_scales[blk];
+            float v0 = Lv[w->v_codes[j]] * w->v_scales[blk];
+            float mm = fmaf(hp->beta1, m0, omb1 * g);
+            float vv = fmaf(hp->beta2, v0, omb2 * (g * g));
+            float denom = fmaf(sqrtf(vv), rsbc2, hp->eps);
+            w->param[j] = fmaf(-step_size, mm / denom, w->param[j] * decay);
+            m1[k] = mm;
+            v1[k] = vv;
+        }
+        float sm = 0.0f, sv = 0.0f;
+        for (int k = 0; k < n; ++k) {
+            float a = fabsf(m1[k]);
+            if (a > sm) sm = a;
+            if (v1[k] > sv) sv = v1[k];
+        }
+        float im = sm > 0.0f ? 1.0f / sm : 0.0f, iv = sv > 0.0f ? 1.0f / sv : 0.0f;
+        for (int k = 0; k < n; ++k) {
+            float xm = fminf(fmaxf(m1[k] * im, -1.0f), 1.0f);
+            float xv = fminf(v1[k] * iv, 1.0f);
+            w->m_codes[off + k] = (uint8_t)or_rtn8(&lvm, xm);
+            w->v_codes[off + k] = (uint8_t)or_rtn8(&lvv, xv);
+        }
+        w->m_scales[blk] = sm;
+        w->v_scales[blk] = sv;
+    }
+    return 0;
+}
+
+void or_dequant8_window(const or_window* w, float* m_out, float* v_out) {
+    float Lm[256], Lv[256];
+    or_codebook8(OR_CB8_SDYN8, Lm);
+    or_codebook8(OR_CB8_DYN8, Lv);
+    for (int64_t j = 0; j < w->len; ++j) {
+        m_out[j] = Lm[w->m_codes[j]] * w->m_scales[j / OR_BLOCK];
+        v_out[j] = Lv[w->v_codes[j]] * w->v_scales[j / OR_BLOCK];
+    }
+}

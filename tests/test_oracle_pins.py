@@ -631,3 +631,70 @@ def test_fp32_recipe_with_clipping_matches_torch():
         ref = tp[i].detach().numpy()
         scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref ** 2)))
         assert (np.abs(p_or[i] - ref) / scale).max() < 2e-6
+
+
+# ---------------------------------------------------------------------------
+# 8-bit blockwise AdamW
+# ---------------------------------------------------------------------------
+
+def _dyn_exact(code, bits):
+    from fractions import Fraction
+    if code == 0:
+        return Fraction(0)
+    E = bits - code.bit_length()
+    F = bits - 1 - E
+    f = code & ((1 << F) - 1)
+    return Fraction(1, 10 ** E) * (Fraction(1, 10) + Fraction(9, 10) * Fraction(f + 1, 1 << F))
+
+
+def test_8bit_maps_follow_the_dynamic_exponent_construction():
+    """Dyn8 and SDyn8 equal the construction evaluated in exact rational
+    arithmetic and rounded to FP32, code by code; Dyn8 is sorted by code with
+    2^(7-E) levels in decade E; SDyn8 is the sign-magnitude mirror of the
+    7-bit map with -0 decoding to +0."""
+    d8 = O.codebook8(O.CB8_DYN8)
+    s8 = O.codebook8(O.CB8_SDYN8)
+    for c in range(256):
+        assert d8[c] == np.float32(float(_dyn_exact(c, 8)))
+        mag = np.float32(float(_dyn_exact(c & 127, 7)))
+        assert s8[c] == (-mag if c & 128 and c != 128 else mag)
+    assert np.all(np.diff(d8) > 0) and d8[0] == 0 and d8[255] == 1
+    for E in range(8):
+        lo, hi = 10.0 ** (-E - 1), 10.0 ** (-E)
+        assert int(((d8 > lo * (1 + 1e-6)) & (d8 <= hi * (1 + 1e-6))).sum()) == 2 ** (7 - E)
+    L, code, mid = O.sorted_levels8(O.CB8_SDYN8)
+    assert len(L) == 255 and 128 not in code and np.array_equal(L, -L[::-1])
+    assert np.all(L[:-1] < mid) and np.all(mid < L[1:])
+
+
+def test_8bit_first_step_rounds_to_the_nearest_level_and_matches_fp32():
+    """From the zero state the decoded moments are 0, so the weights equal
+    the FP32 recipe's bit for bit; the stored m and v codes are the nearest
+    levels (ties to the lower one) of m1 / s_m and v1 / s_v, by brute force."""
+    import torch
+    g = torch.Generator().manual_seed(15)
+    n = 3 * 128 + 57
+    grad = (torch.randn(n, generator=g) * 1e-3).to(torch.bfloat16).view(torch.uint16).numpy().copy()
+    param = (torch.randn(n, generator=g) * 0.02).numpy()
+    hp = O.HParams(step=1)
+    st8 = O.TensorState8((n,), 3)
+    p8 = param.copy()
+    st8.step(hp, p8, grad)
+    st32 = O.TensorState(O.Config.of(O.FP32), (n,), 3)
+    p32 = param.copy()
+    st32.step(hp, p32, grad)
+    assert np.array_equal(p8.view(np.uint32), p32.view(np.uint32))
+    for vals, codes, scales, cb, signed in ((st32.m32, st8.m_codes, st8.m_scales, O.CB8_SDYN8, True),
+                                            (st32.v32, st8.v_codes, st8.v_scales, O.CB8_DYN8, False)):
+        table = O.codebook8(cb)
+        L, lcode, _ = O.sorted_levels8(cb)
+        for b in range(len(scales)):
+            blk = vals[b * 128: (b + 1) * 128]
+            s = np.float32(np.abs(blk).max())
+            assert scales[b] == s
+            inv = np.float32(1) / s
+            x = np.clip(blk * inv, -1, 1) if signed else np.minimum(blk * inv, 1)
+            d = np.abs(x[:, None].astype(np.float64) - L[None, :].astype(np.float64))
+            best = lcode[np.argmin(d, axis=1)]     # argmin takes the first (lower) level on a tie
+            assert np.array_equal(codes[b * 128: b * 128 + blk.size], best)
+            assert np.all(np.abs(table[codes[b * 128: b * 128 + blk.size]] - x) <= np.diff(L).max() / 2 + 1e-7)
