@@ -14,8 +14,8 @@ from .api import (  # noqa: F401
     q4adamw_validate, q4adamw_workspace_bytes, q4adamw_state_bytes, q4adamw_make_header,
     q4adamw_check_header, q4adamw_host_scalars, q4adamw_codebook, q4adamw_init_state, q4adamw_step,
     q4adamw_dequant_state, q4adamw_flat_offsets, q4adamw_accumulate, q4adamw_grad_stats, q4adamw_grad_norm,
-    RECIPE_ZIP_SR, RECIPE_ZE_EDEN, RECIPE_FACTORED, RECIPE_FP32, RECIPE_CUSTOM,
-    CB_NF4, CB_SDYN4, CB_DYN4, CB_DYN4_NZ, CB_LIN4_NZ,
+    RECIPE_ZIP_SR, RECIPE_ZE_EDEN, RECIPE_FACTORED, RECIPE_FP32, RECIPE_CUSTOM, RECIPE_BLOCK8,
+    CB_NF4, CB_SDYN4, CB_DYN4, CB_DYN4_NZ, CB_LIN4_NZ, CB_SDYN8, CB_DYN8,
     RULE_STATE_RTN, RULE_STATE_SR, RULE_UPDATE_RTN, RULE_UPDATE_SR,
     HP_REUSE_TABLE, HP_CHECK_POINTERS, HP_GRAD_STATS, ACC_FIRST, ACC_LAST, ACC_REUSE_TABLE, TF_LM_HEAD,
 )

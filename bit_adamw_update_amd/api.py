@@ -11,8 +11,8 @@ import os
 
 from .build import LIB_PATH
 
-RECIPE_ZIP_SR, RECIPE_ZE_EDEN, RECIPE_FACTORED, RECIPE_FP32, RECIPE_CUSTOM = range(5)
-CB_NF4, CB_SDYN4, CB_DYN4, CB_DYN4_NZ, CB_LIN4_NZ = range(5)
+RECIPE_ZIP_SR, RECIPE_ZE_EDEN, RECIPE_FACTORED, RECIPE_FP32, RECIPE_CUSTOM, RECIPE_BLOCK8 = range(6)
+CB_NF4, CB_SDYN4, CB_DYN4, CB_DYN4_NZ, CB_LIN4_NZ, CB_SDYN8, CB_DYN8 = range(7)
 RULE_STATE_RTN, RULE_STATE_SR, RULE_UPDATE_RTN, RULE_UPDATE_SR = range(4)
 HP_REUSE_TABLE, HP_CHECK_POINTERS, HP_GRAD_STATS = 1, 2, 4
 ACC_FIRST, ACC_LAST, ACC_REUSE_TABLE = 1, 2, 4
@@ -196,7 +196,7 @@ def q4adamw_host_scalars(hp: Q4HParams):
 
 
 def q4adamw_codebook(cb: int):
-    out = (C.c_float * 16)()
+    out = (C.c_float * (256 if cb in (CB_SDYN8, CB_DYN8) else 16))()
     _check(load_library().q4adamw_codebook(cb, out))
     return list(out)
 

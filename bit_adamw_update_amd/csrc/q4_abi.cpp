@@ -52,15 +52,25 @@ q4_status resolve(const q4_config* cfg, Resolved* r) {
     if (cfg->abi_version != Q4ADAMW_ABI_VERSION)
         return fail(Q4_ERR_INVALID_ARG, "config abi_version %u != %u", cfg->abi_version, Q4ADAMW_ABI_VERSION);
     if (cfg->block != Q4ADAMW_BLOCK) return fail(Q4_ERR_INVALID_ARG, "block must be 128 (got %d)", cfg->block);
-    if (cfg->recipe < Q4_RECIPE_ZIP_SR || cfg->recipe > Q4_RECIPE_CUSTOM)
+    if (cfg->recipe < Q4_RECIPE_ZIP_SR || cfg->recipe > Q4_RECIPE_BLOCK8)
         return fail(Q4_ERR_INVALID_ARG, "unknown recipe %d", cfg->recipe);
     if (cfg->recipe == Q4_RECIPE_FP32) {
         *r = Resolved{Q4_RECIPE_FP32, Variant{Q4_CB_NF4, Q4_CB_DYN4, Q4_RULE_STATE_RTN}, 0, 0};
         return ok();
     }
-    if (cfg->m_codebook < 0 || cfg->m_codebook > Q4_CB_LIN4_NZ || cfg->v_codebook < 0 ||
-        cfg->v_codebook > Q4_CB_LIN4_NZ)
+    if (cfg->recipe == Q4_RECIPE_BLOCK8) {
+        // the 8-bit optimizer has one configuration; 4-bit and 8-bit options
+        // do not mix ([A] "Requirements and errors")
+        if (cfg->m_codebook != Q4_CB_SDYN8 || cfg->v_codebook != Q4_CB_DYN8 || cfg->m_rule != Q4_RULE_STATE_RTN ||
+            cfg->v_rule != Q4_RULE_STATE_RTN || cfg->eden != 0)
+            return fail(Q4_ERR_CONFLICT, "the 8-bit recipe takes SDyn8 m, Dyn8 v, State-RTN and no EDEN");
+        *r = Resolved{Q4_RECIPE_BLOCK8, Variant{Q4_CB_SDYN8, Q4_CB_DYN8, Q4_RULE_STATE_RTN}, 0, 0};
+        return ok();
+    }
+    if (cfg->m_codebook < 0 || cfg->m_codebook > Q4_CB_DYN8 || cfg->v_codebook < 0 || cfg->v_codebook > Q4_CB_DYN8)
         return fail(Q4_ERR_INVALID_ARG, "unknown codebook");
+    if (cfg->m_codebook >= Q4_CB_SDYN8 || cfg->v_codebook >= Q4_CB_SDYN8)
+        return fail(Q4_ERR_CONFLICT, "8-bit codebooks belong to Q4_RECIPE_BLOCK8 only");
     if (cfg->m_rule < 0 || cfg->m_rule > Q4_RULE_UPDATE_SR || cfg->v_rule < 0 || cfg->v_rule > Q4_RULE_UPDATE_SR)
         return fail(Q4_ERR_INVALID_ARG, "unknown rounding rule");
     if (cfg->eden != 0 && cfg->eden != 1) return fail(Q4_ERR_INVALID_ARG, "eden must be 0 or 1");
@@ -105,6 +115,7 @@ q4_status check_hp(const q4_hparams* hp) {
 
 int kind_of(const Resolved& r, const q4_tensor& t) {
     if (r.recipe == Q4_RECIPE_FP32) return KIND_FP32;
+    if (r.recipe == Q4_RECIPE_BLOCK8) return KIND_BYTE8;
     if (r.recipe == Q4_RECIPE_FACTORED && t.ndim >= 2) return KIND_FACTORED;
     return KIND_PACKED;
 }
@@ -321,10 +332,12 @@ void scalars_of(const q4_hparams* hp, float out[5]) {
     out[4] = 1.0f - hp->beta2;
 }
 
+int codebook_size(int cb) { return cb >= Q4_CB_SDYN8 ? 256 : 16; }
+
 int zero_code(int cb) {
-    float L[16];
+    float L[256];
     codebook_table(cb, L);
-    for (int c = 0; c < 16; ++c)
+    for (int c = 0; c < codebook_size(cb); ++c)
         if (L[c] == 0.0f) return c;
     return 0;  // zero-excluding maps: the floor code, decoded with scale 0
 }
@@ -403,6 +416,8 @@ q4_status q4adamw_default_config(int32_t recipe, q4_config* cfg) {
     case Q4_RECIPE_FACTORED: c.v_codebook = Q4_CB_DYN4_NZ; c.v_rule = Q4_RULE_STATE_RTN; c.eden = 0; break;
     case Q4_RECIPE_FP32: c.v_codebook = Q4_CB_DYN4; c.v_rule = Q4_RULE_STATE_RTN; c.eden = 0; break;
     case Q4_RECIPE_CUSTOM: c.v_codebook = Q4_CB_DYN4; c.v_rule = Q4_RULE_UPDATE_SR; c.eden = 0; break;
+    case Q4_RECIPE_BLOCK8:
+        c.m_codebook = Q4_CB_SDYN8; c.v_codebook = Q4_CB_DYN8; c.v_rule = Q4_RULE_STATE_RTN; c.eden = 0; break;
     default: return fail(Q4_ERR_INVALID_ARG, "unknown recipe %d", recipe);
     }
     *cfg = c;
@@ -444,6 +459,9 @@ q4_status q4adamw_state_bytes(const q4_config* cfg, const q4_tensor* t, int32_t 
         const int kind = kind_of(r, x);
         if (kind == KIND_FP32) {
             q += 8 * numel;
+        } else if (kind == KIND_BYTE8) {
+            q += 2 * numel;
+            meta += 8 * nb;
         } else if (kind == KIND_FACTORED && numel > 0) {
             q += codes;
             meta += 4 * nb + 4 * (uint64_t)x.shape[0] + 4 * (numel / (uint64_t)x.shape[0]);
@@ -502,9 +520,9 @@ q4_status q4adamw_host_scalars(const q4_hparams* hp, float out[5]) {
     return ok();
 }
 
-q4_status q4adamw_codebook(int32_t cb, float out[16]) {
+q4_status q4adamw_codebook(int32_t cb, float* out) {
     if (!out) return fail(Q4_ERR_INVALID_ARG, "out is NULL");
-    if (cb < 0 || cb > Q4_CB_LIN4_NZ) return fail(Q4_ERR_INVALID_ARG, "unknown codebook %d", cb);
+    if (cb < 0 || cb > Q4_CB_DYN8) return fail(Q4_ERR_INVALID_ARG, "unknown codebook %d", cb);
     codebook_table(cb, out);
     return ok();
 }
@@ -529,6 +547,11 @@ q4_status q4adamw_init_state(const q4_config* cfg, const q4_tensor* t, int32_t n
         if (kind == KIND_FP32) {
             fill(x.m_fp32, 4 * numel, 0);
             fill(x.v_fp32, 4 * numel, 0);
+        } else if (kind == KIND_BYTE8) {
+            fill(x.m_codes, numel, zm);
+            fill(x.v_codes, numel, zv);
+            fill(x.m_scales, 4 * nb, 0);
+            fill(x.v_scales, 4 * nb, 0);
         } else {
             fill(x.m_codes, codes, (uint8_t)(zm | (zm << 4)));
             if (numel & 1) fill(x.m_codes + codes - 1, 1, zm);
@@ -610,6 +633,11 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
     if (r.recipe == Q4_RECIPE_FP32) {
         e = launch_fp32_step(sc, d_tab, d_chunks, n, P.total_chunks, st);
         if (e != hipSuccess) return hip_fail(e, "fp32 step launch");
+        return ok();
+    }
+    if (r.recipe == Q4_RECIPE_BLOCK8) {
+        e = launch_block8_step(sc, d_tab, d_chunks, n, P.total_chunks, st);
+        if (e != hipSuccess) return hip_fail(e, "8-bit step launch");
         return ok();
     }
     if (P.n_mats > 0) {

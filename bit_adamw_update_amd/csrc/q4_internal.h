@@ -22,7 +22,7 @@ constexpr int kAccGroups = 2048;       // work-groups of the chunk-order accumul
 // microbatch into it, or add the microbatch to it.
 enum GradMode : int { GRAD_STATS_ONLY = 0, GRAD_FIRST = 1, GRAD_ADD = 2 };
 
-enum Kind : int32_t { KIND_PACKED = 0, KIND_FACTORED = 1, KIND_FP32 = 2 };
+enum Kind : int32_t { KIND_PACKED = 0, KIND_FACTORED = 1, KIND_FP32 = 2, KIND_BYTE8 = 3 };
 
 // One tensor as the step kernel sees it (128 bytes, read with scalar loads).
 struct alignas(16) DevTensor {
@@ -97,6 +97,8 @@ hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevT
                              hipStream_t stream);
 hipError_t launch_fp32_step(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
                             int n_tensors, int64_t total_chunks, hipStream_t stream);
+hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
+                              int n_tensors, int64_t total_chunks, hipStream_t stream);
 // K2 (skipped when the partials are already in the workspace), K3a, K3b.
 hipError_t launch_factored_stats(const DevMatrix* d_mats, int n_mats, int64_t total_tiles, int64_t total_rgroups,
                                  int64_t total_cgroups, float beta2, float omb2, const float* clip, bool partials_ready,
@@ -115,6 +117,6 @@ hipError_t launch_fill(void* p, size_t bytes, uint8_t value, hipStream_t stream)
 hipError_t launch_dequant(int mcb, int vcb, const DevTensor& t, int64_t rows, float* m_out, float* v_out,
                           double* ws_partials, float* ws_inv, hipStream_t stream);
 bool variant_supported(const Variant& v);
-void codebook_table(int cb, float out[16]);
+void codebook_table(int cb, float* out);  // 16 entries, 256 for the 8-bit maps
 
 }  // namespace q4

@@ -90,9 +90,14 @@ template <int CB> __device__ __forceinline__ float sorted_level_rt(int k) {
     return bits2f(c_decode[CB][Book<CB>::code_of(k)]);
 }
 
-void codebook_table(int cb, float out[16]) {
+void codebook_table(int cb, float* out) {
     static const uint32_t host[5][16] = {Q4_CB_BITS_NF4, Q4_CB_BITS_SDYN4, Q4_CB_BITS_DYN4, Q4_CB_BITS_DYN4_NZ,
                                          Q4_CB_BITS_LIN4_NZ};
+    static const uint32_t host8[2][256] = {Q4_CB8_BITS_SDYN8, Q4_CB8_BITS_DYN8};
+    if (cb >= Q4_CB_SDYN8) {
+        for (int i = 0; i < 256; ++i) out[i] = bits2f(host8[cb - Q4_CB_SDYN8][i]);
+        return;
+    }
     for (int i = 0; i < 16; ++i) out[i] = bits2f(host[cb][i]);
 }
 
@@ -219,6 +224,7 @@ template <class T> __device__ __forceinline__ gptr<const T> G(const T* p) { retu
 // clang vector types copy in any address space (HIP's float4 does not)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // ---------------------------------------------------------------------------
 // Round-to-nearest by bucket table
@@ -790,6 +796,185 @@ __global__ __launch_bounds__(256) void k_fp32_step(const DevTensor* __restrict__
 }
 
 // ---------------------------------------------------------------------------
+// K1 of the 8-bit recipe: SDyn8 m, Dyn8 v, one byte per code
+// ---------------------------------------------------------------------------
+//
+// Same lane layout as K1 (8 consecutive elements per lane, a 128-block per
+// 16-lane row).  A code is one byte, so a lane's 8 codes of a moment are one
+// 8-byte access.  256-entry maps do not fit ds_bpermute's 64 lanes: decoding
+// reads a code-indexed table in LDS, and the nearest level is the number of
+// FP32 midpoints strictly below x, found by an 8-step binary search over the
+// sorted midpoints in LDS (padded with +inf).
+
+__constant__ uint32_t c_cb8[2][256] = {Q4_CB8_BITS_SDYN8, Q4_CB8_BITS_DYN8};
+
+struct Step8Lds {
+    float dec_m[256], dec_v[256];  // code-indexed levels
+    float mid_m[256], mid_v[256];  // ascending FP32 midpoints, +inf padded
+};
+
+// SDyn8 in ascending order: -1 .. -1e-6 are codes 255 .. 129, then 0, then
+// 1 .. 127 (the code 128, "-0", is never written).
+__device__ __forceinline__ uint32_t sdyn8_code(int k) { return k < 127 ? 255u - k : (k == 127 ? 0u : (uint32_t)(k - 127)); }
+
+__device__ __forceinline__ int rtn8(const float* mid, float x) {
+    int idx = 0;
+#pragma unroll
+    for (int s = 128; s > 0; s >>= 1) idx += mid[idx + s - 1] < x ? s : 0;
+    return idx;
+}
+
+template <bool FULL, bool CLIP>
+__device__ __forceinline__ void step8_chunk(const DevTensor& T, const int64_t lc, const StepScalars& sc,
+                                            const Step8Lds& lds, const int lane, const float gs) {
+    const int sub = lane & 15;
+    const int64_t n = T.numel;
+    const int64_t blk = lc * kBlocksPerChunk + (lane >> 4);
+    const int64_t e0 = blk * kBlock + sub * 8;
+    int nv = 8;
+    bool blk_ok = true;
+    if (!FULL) {
+        const int64_t rem = n - e0;
+        nv = rem >= 8 ? 8 : (rem > 0 ? (int)rem : 0);
+        blk_ok = blk * kBlock < n;
+    }
+    const gptr<float> param = G(T.param);
+    const gptr<const uint16_t> grad = G(T.grad);
+    const gptr<uint8_t> mcodes = G(T.m_codes);
+    const gptr<uint8_t> vcodes = G(T.v_codes);
+    const gptr<float> mscales = G(T.m_scales);
+    const gptr<float> vscales = G(T.v_scales);
+
+    float p[8], g[8];
+    uint32_t mc[2] = {0u, 0u}, vc[2] = {0u, 0u};
+    if (FULL || nv == 8) {
+        const f32x4 a = *reinterpret_cast<const gptr<const f32x4>>(param + e0);
+        const f32x4 b = *reinterpret_cast<const gptr<const f32x4>>(param + e0 + 4);
+        p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
+        const u32x4 gq = *reinterpret_cast<const gptr<const u32x4>>(grad + e0);
+        g[0] = bf16_to_f32(gq.x & 0xFFFFu); g[1] = bf16_to_f32(gq.x >> 16);
+        g[2] = bf16_to_f32(gq.y & 0xFFFFu); g[3] = bf16_to_f32(gq.y >> 16);
+        g[4] = bf16_to_f32(gq.z & 0xFFFFu); g[5] = bf16_to_f32(gq.z >> 16);
+        g[6] = bf16_to_f32(gq.w & 0xFFFFu); g[7] = bf16_to_f32(gq.w >> 16);
+        const u32x2 m8 = *reinterpret_cast<const gptr<const u32x2>>(mcodes + e0);
+        const u32x2 v8 = *reinterpret_cast<const gptr<const u32x2>>(vcodes + e0);
+        mc[0] = m8.x; mc[1] = m8.y; vc[0] = v8.x; vc[1] = v8.y;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            p[k] = k < nv ? param[e0 + k] : 0.0f;
+            g[k] = k < nv ? bf16_to_f32(grad[e0 + k]) : 0.0f;
+            if (k < nv) {
+                mc[k >> 2] |= (uint32_t)mcodes[e0 + k] << (8 * (k & 3));
+                vc[k >> 2] |= (uint32_t)vcodes[e0 + k] << (8 * (k & 3));
+            }
+        }
+    }
+    if constexpr (CLIP) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) g[k] *= gs;
+    }
+    const float sm_old = (FULL || blk_ok) ? mscales[blk] : 0.0f;
+    const float sv_old = (FULL || blk_ok) ? vscales[blk] : 0.0f;
+
+    float m1[8], v1[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const uint32_t cm = (mc[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+        const uint32_t cv = (vc[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+        const float m0 = lds.dec_m[cm] * sm_old;
+        const float v0 = lds.dec_v[cv] * sv_old;
+        m1[k] = __builtin_fmaf(sc.beta1, m0, sc.omb1 * g[k]);
+        v1[k] = __builtin_fmaf(sc.beta2, v0, sc.omb2 * (g[k] * g[k]));
+        const float denom = __builtin_fmaf(__builtin_amdgcn_sqrtf(v1[k]), sc.rsbc2, sc.eps);
+        p[k] = __builtin_fmaf(-sc.step_size, m1[k] * __builtin_amdgcn_rcpf(denom), p[k] * sc.decay);
+        if (!FULL && k >= nv) {
+            m1[k] = 0.0f;
+            v1[k] = 0.0f;
+        }
+    }
+    if (FULL || nv == 8) {
+        *reinterpret_cast<gptr<f32x4>>(param + e0) = f32x4{p[0], p[1], p[2], p[3]};
+        *reinterpret_cast<gptr<f32x4>>(param + e0 + 4) = f32x4{p[4], p[5], p[6], p[7]};
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (k < nv) param[e0 + k] = p[k];
+    }
+
+    float am = 0.0f, av = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        am = fmaxf(am, fabsf(m1[k]));
+        av = fmaxf(av, v1[k]);
+    }
+    const float s_m = row_max16(am), s_v = row_max16(av);
+    const float inv_m = s_m > 0.0f ? 1.0f / s_m : 0.0f;
+    const float inv_v = s_v > 0.0f ? 1.0f / s_v : 0.0f;
+    uint32_t mw[2] = {0u, 0u}, vw[2] = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float xm = fminf(fmaxf(m1[k] * inv_m, -1.0f), 1.0f);
+        const float xv = fminf(v1[k] * inv_v, 1.0f);
+        mw[k >> 2] |= sdyn8_code(rtn8(lds.mid_m, xm)) << (8 * (k & 3));
+        vw[k >> 2] |= (uint32_t)rtn8(lds.mid_v, xv) << (8 * (k & 3));
+    }
+    if (FULL || nv == 8) {
+        *reinterpret_cast<gptr<u32x2>>(mcodes + e0) = u32x2{mw[0], mw[1]};
+        *reinterpret_cast<gptr<u32x2>>(vcodes + e0) = u32x2{vw[0], vw[1]};
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            if (k < nv) {
+                mcodes[e0 + k] = (uint8_t)(mw[k >> 2] >> (8 * (k & 3)));
+                vcodes[e0 + k] = (uint8_t)(vw[k >> 2] >> (8 * (k & 3)));
+            }
+        }
+    }
+    if ((FULL || blk_ok) && sub == 0) {
+        mscales[blk] = s_m;
+        vscales[blk] = s_v;
+    }
+}
+
+template <bool CLIP>
+__global__ __launch_bounds__(256) void k_step8(const DevTensor* __restrict__ tab,
+                                                const int64_t* __restrict__ chunk_begin, int n_tensors,
+                                                int64_t total_chunks, StepScalars sc) {
+    __shared__ Step8Lds lds;
+    {
+        const int t = threadIdx.x;  // 256 threads: one entry each
+        lds.dec_m[t] = bits2f(c_cb8[0][t]);
+        lds.dec_v[t] = bits2f(c_cb8[1][t]);
+        // FP32 midpoints of adjacent levels in ascending order, the same
+        // product the definition forms
+        lds.mid_m[t] = t < 254 ? (bits2f(c_cb8[0][sdyn8_code(t)]) + bits2f(c_cb8[0][sdyn8_code(t + 1)])) * 0.5f
+                               : __builtin_inff();
+        lds.mid_v[t] = t < 255 ? (bits2f(c_cb8[1][t]) + bits2f(c_cb8[1][t + 1])) * 0.5f : __builtin_inff();
+    }
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const float gs = CLIP ? *clip_of_table(tab) : 1.0f;
+    int t = first_tensor(chunk_begin, n_tensors, (int64_t)blockIdx.x * kWavesPerGroup + wave);
+    for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks;
+         c += (int64_t)gridDim.x * kWavesPerGroup) {
+        while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
+        const DevTensor T = tab[t];
+        const int64_t lc = c - T.chunk_begin;
+        if ((lc + 1) * kChunkElems <= T.numel) step8_chunk<true, CLIP>(T, lc, sc, lds, lane, gs);
+        else step8_chunk<false, CLIP>(T, lc, sc, lds, lane, gs);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_dequant8(DevTensor T, float* __restrict__ m_out, float* __restrict__ v_out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T.numel) return;
+    m_out[i] = bits2f(c_cb8[0][T.m_codes[i]]) * T.m_scales[i / kBlock];
+    v_out[i] = bits2f(c_cb8[1][T.v_codes[i]]) * T.v_scales[i / kBlock];
+}
+
+// ---------------------------------------------------------------------------
 // K2 / K3: factored second moment (row and column means of g^2)
 // ---------------------------------------------------------------------------
 
@@ -1337,9 +1522,28 @@ hipError_t launch_fill(void* p, size_t bytes, uint8_t value, hipStream_t stream)
     return hipGetLastError();
 }
 
+hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
+                              int n_tensors, int64_t total_chunks, hipStream_t stream) {
+    if (total_chunks <= 0) return hipSuccess;
+    if (sc.flags & SF_CLIP) {
+        static std::atomic<int> occ{0};
+        k_step8<true><<<step_grid(k_step8<true>, total_chunks, occ), 256, 0, stream>>>(d_tab, d_chunk_begin,
+                                                                                      n_tensors, total_chunks, sc);
+    } else {
+        static std::atomic<int> occ{0};
+        k_step8<false><<<step_grid(k_step8<false>, total_chunks, occ), 256, 0, stream>>>(d_tab, d_chunk_begin,
+                                                                                        n_tensors, total_chunks, sc);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_dequant(int mcb, int vcb, const DevTensor& t, int64_t rows, float* m_out, float* v_out,
                           double* ws_partials, float* ws_inv, hipStream_t stream) {
     if (t.numel == 0) return hipSuccess;
+    if (t.kind == KIND_BYTE8) {
+        k_dequant8<<<(unsigned)((t.numel + 255) / 256), 256, 0, stream>>>(t, m_out, v_out);
+        return hipGetLastError();
+    }
     if (t.kind == KIND_FACTORED) {
         const int64_t ng = (rows + kGroup - 1) / kGroup;
         k_rsum_groups<<<(unsigned)ng, 256, 0, stream>>>(t.v_row, rows, ws_partials);

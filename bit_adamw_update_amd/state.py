@@ -14,7 +14,7 @@ import torch
 from . import api
 
 RECIPE_BY_NAME = {"zip_sr": api.RECIPE_ZIP_SR, "ze_eden": api.RECIPE_ZE_EDEN, "factored": api.RECIPE_FACTORED,
-                  "fp32": api.RECIPE_FP32, "custom": api.RECIPE_CUSTOM}
+                  "fp32": api.RECIPE_FP32, "custom": api.RECIPE_CUSTOM, "block8": api.RECIPE_BLOCK8}
 
 
 class _Buffers:
@@ -45,6 +45,12 @@ class Q4State:
                 b.kind = "fp32"
                 b.m32 = torch.empty(n, dtype=torch.float32, device=self.device)
                 b.v32 = torch.empty(n, dtype=torch.float32, device=self.device)
+            elif self.cfg.recipe == api.RECIPE_BLOCK8:
+                b.kind = "byte8"   # one byte per code
+                b.m_codes = torch.empty(n, dtype=torch.uint8, device=self.device)
+                b.m_scales = torch.empty(nb, dtype=torch.float32, device=self.device)
+                b.v_codes = torch.empty(n, dtype=torch.uint8, device=self.device)
+                b.v_scales = torch.empty(nb, dtype=torch.float32, device=self.device)
             else:
                 b.m_codes = torch.empty(nc, dtype=torch.uint8, device=self.device)
                 b.m_scales = torch.empty(nb, dtype=torch.float32, device=self.device)

@@ -71,7 +71,10 @@ typedef enum {
     Q4_RECIPE_ZE_EDEN = 1,  /* NF4 m (RTN); Dyn4-NZ v (zero-excluding), State-RTN; EDEN rescale */
     Q4_RECIPE_FACTORED = 2, /* NF4 m; matrices: row/column means of g^2; 1-D: Dyn4-NZ v, State-RTN */
     Q4_RECIPE_FP32 = 3,     /* quantization off: FP32 m and v (32-bit AdamW) */
-    Q4_RECIPE_CUSTOM = 4    /* codebooks and rules taken from the q4_config fields */
+    Q4_RECIPE_CUSTOM = 4,   /* codebooks and rules taken from the q4_config fields */
+    Q4_RECIPE_BLOCK8 = 5    /* 8-bit blockwise AdamW ([A] names it beside the 4-bit optimizer; the two are
+                               mutually exclusive): SDyn8 m, Dyn8 v, one byte per code, State-RTN, no
+                               factorization */
 } q4_recipe;
 
 typedef enum {
@@ -79,7 +82,9 @@ typedef enum {
     Q4_CB_SDYN4 = 1,   /* signed dynamic-exponent map: sign bit + 3-bit magnitude */
     Q4_CB_DYN4 = 2,    /* unsigned dynamic-exponent map, zero-inclusive */
     Q4_CB_DYN4_NZ = 3, /* unsigned dynamic-exponent map, zero-excluding (floor 1e-4) */
-    Q4_CB_LIN4_NZ = 4  /* linear zero-excluding map k/16, k = 1..16 */
+    Q4_CB_LIN4_NZ = 4, /* linear zero-excluding map k/16, k = 1..16 */
+    Q4_CB_SDYN8 = 5,   /* 8-bit: sign bit + 7-bit dynamic magnitude (Q4_RECIPE_BLOCK8 only) */
+    Q4_CB_DYN8 = 6     /* 8-bit unsigned dynamic-exponent map, zero-inclusive (Q4_RECIPE_BLOCK8 only) */
 } q4_codebook;
 
 /* Rounding rules ([P] Table 1). State rules round in v; Update rules round
@@ -138,8 +143,9 @@ typedef struct {
  *                                                    column means of g^2 (in place)
  *   m_fp32, v_fp32 float[n]  FP32 recipe only (in place)
  * Codes: element 2j in the low nibble of byte j, element 2j+1 in the high
- * nibble (0 when n is odd).  Blocks are parameter-local: block b covers
- * elements [128 b, min(128 b + 128, n)). */
+ * nibble (0 when n is odd).  Q4_RECIPE_BLOCK8: m_codes and v_codes are
+ * uint8[n], byte i holding element i.  Blocks are parameter-local: block b
+ * covers elements [128 b, min(128 b + 128, n)). */
 typedef struct {
     uint32_t tensor_id; /* Philox counter word; stable across steps, distinct per tensor */
     uint32_t flags;     /* Q4_TF_* */
@@ -203,8 +209,8 @@ q4_status q4adamw_check_header(const q4_config* cfg, const q4_state_header* hdr)
 q4_status q4adamw_host_scalars(const q4_hparams* hp, float out[5]);
 
 /* The library's decode table of a codebook, indexed by code (host copy of
- * the table the kernels use). */
-q4_status q4adamw_codebook(int32_t codebook, float out[16]);
+ * the table the kernels use): 16 entries, or 256 for the 8-bit maps. */
+q4_status q4adamw_codebook(int32_t codebook, float* out);
 
 /* ---- device entry points ---------------------------------------------- */
 

@@ -52,6 +52,32 @@ def test_library_codebooks_equal_oracle_construction(cb):
     assert np.array_equal(got.view(np.uint32), O.codebook(cb).view(np.uint32))
 
 
+@pytest.mark.parametrize("cb,cb8", [(5, O.CB8_SDYN8), (6, O.CB8_DYN8)])
+def test_library_8bit_codebooks_equal_oracle_construction(cb, cb8):
+    got = np.array(q4.q4adamw_codebook(cb), np.float32)
+    assert got.size == 256
+    assert np.array_equal(got.view(np.uint32), O.codebook8(cb8).view(np.uint32))
+
+
+def test_8bit_recipe_is_one_configuration():
+    """[A] "Requirements and errors": 4-bit and 8-bit options do not mix."""
+    b = q4.q4adamw_default_config(q4.RECIPE_BLOCK8)
+    assert (b.m_codebook, b.v_codebook, b.m_rule, b.v_rule, b.eden) == (
+        q4.CB_SDYN8, q4.CB_DYN8, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 0)
+    t = [fake_tensor((64, 32))]
+    q4.q4adamw_validate(b, hp(), t)
+    b.v_codebook = q4.CB_DYN4
+    assert status_of(q4.q4adamw_validate, b, hp(), t) == 4
+    c = q4.q4adamw_default_config(q4.RECIPE_CUSTOM)
+    c.v_codebook = q4.CB_DYN8
+    assert status_of(q4.q4adamw_validate, c, hp(), t) == 4
+    # an 8-bit state never resumes as 4-bit, nor the reverse
+    h8 = q4.q4adamw_make_header(q4.q4adamw_default_config(q4.RECIPE_BLOCK8))
+    assert status_of(q4.q4adamw_check_header, q4.q4adamw_default_config(q4.RECIPE_ZIP_SR), h8) == 5
+    sb = q4.q4adamw_state_bytes(q4.q4adamw_default_config(q4.RECIPE_BLOCK8), [fake_tensor((1024,))])
+    assert sb["adam4_quantized_state_bytes"] == 2048 and sb["adam4_scale_metadata_bytes"] == 64
+
+
 def test_default_configs_follow_table2():
     z = q4.q4adamw_default_config(q4.RECIPE_ZIP_SR)
     assert (z.m_codebook, z.v_codebook, z.m_rule, z.v_rule, z.eden) == (

@@ -1,0 +1,115 @@
+"""GPU parity of the 8-bit blockwise AdamW recipe (SDyn8 m, Dyn8 v, one byte
+per code) against the CPU oracle on the same seeded bytes: codes and scales
+bit-exact, weights within 1e-6 relative to max(|w|, rms(w))."""
+import numpy as np
+import pytest
+import torch
+
+import bit_adamw_update_amd as q4
+from bit_adamw_update_amd import inputs
+from oracle import oracle as O
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def _flush(msg):
+    print(msg, flush=True)
+
+
+def _check_weights(p, ref, what):
+    scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
+    scale[scale == 0] = 1.0
+    err = float((np.abs(p - ref) / scale).max()) if p.size else 0.0
+    assert err <= parity.W_TOL, f"{what}: weight error {err:.3e}"
+
+
+def run_windows(w, steps, windows=None, grads_on="cpu", clip=0.0):
+    """Step the GPU state over the whole workload and the oracle over
+    block windows [(i, b0, b1)] (all of every tensor when None); compare."""
+    dev = torch.device("cuda")
+    consts = w._tensor_consts(grads_on)
+    params = [p.reshape(-1) for p in w.init_params(grads_on)]
+    gp = [p.to(dev).contiguous() for p in params]
+    st = q4.Q4State("block8", w.tensors, dev)
+    if windows is None:
+        windows = [(i, 0, (t.numel + 127) // 128) for i, t in enumerate(w.tensors)]
+    ost, op = [], []
+    for i, b0, b1 in windows:
+        t = w.tensors[i]
+        lo, hi = b0 * 128, min(b1 * 128, t.numel)
+        ost.append(O.TensorState8((hi - lo,), t.tensor_id, t.flags))
+        op.append(params[i][lo:hi].cpu().numpy().copy())
+    for s in range(1, steps + 1):
+        g = w.grads(s, grads_on, consts)
+        gg = [x.to(dev).reshape(-1).contiguous() for x in g]
+        scale = 1.0
+        if clip > 0:
+            st.grad_stats(gp, gg)
+            scale = O.clip_factor(sum(O.grad_sumsq(x.view(torch.uint16).cpu().numpy().reshape(-1)) for x in g),
+                                  clip)
+        st.step(gp, gg, s, max_grad_norm=clip, **w.hp)
+        hp = O.HParams(step=s, grad_scale=scale, **w.hp)
+        for k, (i, b0, b1) in enumerate(windows):
+            t = w.tensors[i]
+            lo, hi = b0 * 128, min(b1 * 128, t.numel)
+            # the window is its own tensor for the oracle: the tensor id and
+            # the block-aligned offset are all the 8-bit step depends on
+            gw = g[i].reshape(-1)[lo:hi].view(torch.uint16).cpu().numpy().copy()
+            ost[k].step(hp, op[k], gw)
+    torch.cuda.synchronize()
+    for k, (i, b0, b1) in enumerate(windows):
+        b = st.bufs[i]
+        t = w.tensors[i]
+        lo, hi = b0 * 128, min(b1 * 128, t.numel)
+        o = ost[k]
+        assert np.array_equal(b.m_codes[lo:hi].cpu().numpy(), o.m_codes), f"tensor {i} m codes"
+        assert np.array_equal(b.v_codes[lo:hi].cpu().numpy(), o.v_codes), f"tensor {i} v codes"
+        assert np.array_equal(b.m_scales[b0:b1].cpu().numpy().view(np.uint32), o.m_scales.view(np.uint32))
+        assert np.array_equal(b.v_scales[b0:b1].cpu().numpy().view(np.uint32), o.v_scales.view(np.uint32))
+        _check_weights(gp[i][lo:hi].cpu().numpy(), op[k], f"tensor {i}")
+    return st
+
+
+def test_tiny_workload_10_steps():
+    _flush("block8 tiny")
+    run_windows(inputs.tiny(), 10)
+
+
+def test_ragged_shapes():
+    shapes = [(1,), (127,), (129,), (1000,), (4097,), (3, 5), (7, 129), (300, 3), (2, 1031)]
+    _flush("block8 ragged")
+    run_windows(inputs.custom(shapes, grad_kind="masked", seed=41), 5)
+
+
+def test_clipped_steps():
+    _flush("block8 clipped")
+    run_windows(inputs.custom([(3000,), (64, 200)], grad_kind="masked", seed=42), 4, clip=2e-3)
+
+
+def test_dequant_matches_oracle():
+    w = inputs.custom([(3000,), (48, 200)], grad_kind="masked", seed=43)
+    st = run_windows(w, 3)
+    # the oracle of the whole tensors again, for its dequantization
+    consts = w._tensor_consts("cpu")
+    params = [p.reshape(-1).numpy().copy() for p in w.init_params("cpu")]
+    ost = [O.TensorState8(t.shape, t.tensor_id) for t in w.tensors]
+    for s in range(1, 4):
+        g = w.grads(s, "cpu", consts)
+        for i, o in enumerate(ost):
+            o.step(O.HParams(step=s, **w.hp), params[i], g[i].view(torch.uint16).numpy().reshape(-1).copy())
+    for i, o in enumerate(ost):
+        m, v = st.dequant(i)
+        torch.cuda.synchronize()
+        om, ov = o.dequant()
+        assert np.array_equal(m.cpu().numpy().view(np.uint32), om.view(np.uint32))
+        assert np.array_equal(v.cpu().numpy().view(np.uint32), ov.view(np.uint32))
+
+
+def test_gpt_162m_sampled_20_steps():
+    """The GPT-style 162M set (123.6M parameters as written), 20 steps,
+    first/last blocks of every tensor and random interior windows."""
+    w = inputs.gpt_162m()
+    wins = parity.sample_windows(w, n_random=32, seed=5)
+    _flush("block8 gpt-162m")
+    run_windows(w, 20, windows=wins, grads_on="cuda")
