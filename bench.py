@@ -47,6 +47,8 @@ def alg_bytes(workload, recipe: str) -> int:
         codes = (n + 1) // 2
         if recipe == "fp32":
             total += 10 * n + 16 * n
+        elif recipe == "block8":
+            total += 10 * n + 4 * n + 16 * nb   # one byte per code, read and written, two moments
         elif recipe == "factored" and len(t.shape) >= 2:
             total += 10 * n + 2 * codes + 8 * nb + 4 * (t.shape[0] + n // t.shape[0])
         else:
@@ -182,7 +184,7 @@ def cpu_baseline(workload, recipe: str, max_elems: int):
     import torch
 
     from oracle import oracle as O
-    orec = {"zip_sr": O.ZIP_SR, "ze_eden": O.ZE_EDEN, "factored": O.FACTORED, "fp32": O.FP32}[recipe]
+    orec = {"zip_sr": O.ZIP_SR, "ze_eden": O.ZE_EDEN, "factored": O.FACTORED, "fp32": O.FP32}.get(recipe)
     picked, n = [], 0
     for i, t in enumerate(workload.tensors):
         if n + t.numel > max_elems and picked:
@@ -196,7 +198,8 @@ def cpu_baseline(workload, recipe: str, max_elems: int):
         t = workload.tensors[i]
         p = (torch.randn(t.numel, generator=g) * 0.02).numpy()
         gr = (torch.randn(t.numel, generator=g) * 1e-3).to(torch.bfloat16).view(torch.uint16).numpy().copy()
-        host.append((t, p, gr, O.TensorState(O.Config.of(orec), t.shape, t.tensor_id, t.flags)))
+        host.append((t, p, gr, O.TensorState8(t.shape, t.tensor_id, t.flags) if recipe == "block8"
+                     else O.TensorState(O.Config.of(orec), t.shape, t.tensor_id, t.flags)))
     hp = O.HParams(step=1, **workload.hp)
     t0 = time.perf_counter()
     for t, p, gr, st in host:
@@ -279,7 +282,7 @@ def main():
     if not args.no_variants:
         variants = {}
         plan = [("gpt-2.7b", "ze_eden"), ("llama-1.1b", "zip_sr"), ("qwen3-0.6b-factored", "factored"),
-                ("gpt-162m", "zip_sr")]
+                ("gpt-162m", "zip_sr"), ("gpt-2.7b", "block8")]
         for wname, rec in plan:
             if (wname, rec) == (args.workload, args.recipe):
                 continue

@@ -802,26 +802,80 @@ __global__ __launch_bounds__(256) void k_fp32_step(const DevTensor* __restrict__
 // Same lane layout as K1 (8 consecutive elements per lane, a 128-block per
 // 16-lane row).  A code is one byte, so a lane's 8 codes of a moment are one
 // 8-byte access.  256-entry maps do not fit ds_bpermute's 64 lanes: decoding
-// reads a code-indexed table in LDS, and the nearest level is the number of
-// FP32 midpoints strictly below x, found by an 8-step binary search over the
-// sorted midpoints in LDS (padded with +inf).
+// reads a code-indexed table in LDS.  The nearest level is the number of
+// FP32 midpoints strictly below x.  Counting them with a binary search over
+// a sorted table in LDS puts every probe of one step on the same bank (the
+// probes of a step sit s apart, s a power of two), so it is counted with a
+// bucket table instead: a non-negative float's bit pattern shifted right
+// (exponent and top mantissa bits) names a bucket that holds at most two
+// midpoints; the table gives the midpoints below the bucket, one 8-byte read
+// gives the two candidates, and two compares finish the count.
+//
+// SDyn8 is symmetric about zero with 127 positive midpoints P: for x >= 0
+// the ascending level index is 127 + #{P < x}, and for x < 0 it is
+// 127 - #{P <= |x|}, which is #{P < nextup(|x|)}.  Either count is the
+// magnitude part of the code; the sign bit goes on a non-zero magnitude.
 
 __constant__ uint32_t c_cb8[2][256] = {Q4_CB8_BITS_SDYN8, Q4_CB8_BITS_DYN8};
 
 struct Step8Lds {
-    float dec_m[256], dec_v[256];  // code-indexed levels
-    float mid_m[256], mid_v[256];  // ascending FP32 midpoints, +inf padded
+    float dec_m[256], dec_v[256];   // code-indexed levels
+    float mid_p[128];               // SDyn8's positive midpoints ascending, +inf padded
+    float mid_v[256];               // Dyn8's midpoints ascending, +inf padded
+    float2 pair_m[128], pair_v[256];  // {mid[i], mid[i + 1]}
+    uint8_t floor_m[Q4_RTN8_M_NB], floor_v[Q4_RTN8_V_NB];  // midpoints below each bucket
 };
 
-// SDyn8 in ascending order: -1 .. -1e-6 are codes 255 .. 129, then 0, then
-// 1 .. 127 (the code 128, "-0", is never written).
-__device__ __forceinline__ uint32_t sdyn8_code(int k) { return k < 127 ? 255u - k : (k == 127 ? 0u : (uint32_t)(k - 127)); }
-
-__device__ __forceinline__ int rtn8(const float* mid, float x) {
+// Count of sorted, +inf padded table entries strictly below x (N a power of two).
+template <int N>
+__device__ __forceinline__ int count_below_sorted(const float* mid, float x) {
     int idx = 0;
 #pragma unroll
-    for (int s = 128; s > 0; s >>= 1) idx += mid[idx + s - 1] < x ? s : 0;
+    for (int s = N / 2; s > 0; s >>= 1) idx += mid[idx + s - 1] < x ? s : 0;
     return idx;
+}
+
+// #{midpoints < bits2f(key)} for a non-negative key; keys outside the
+// bucketed range clamp to the first or last bucket (in bounds for any key).
+template <int SHIFT, int LO, int NB>
+__device__ __forceinline__ uint32_t count_below8(const uint8_t* floor_tab, const float2* pair, uint32_t key) {
+    const int b = min(max((int)(key >> SHIFT) - LO, 0), NB - 1);
+    const uint32_t f = floor_tab[b];
+    const float2 pr = pair[f];
+    const float a = bits2f(key);
+    return f + (pr.x < a ? 1u : 0u) + (pr.y < a ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t rtn8_m(const Step8Lds& lds, float x) {
+    const uint32_t xb = __float_as_uint(x);
+    const uint32_t neg = xb >> 31;
+    const uint32_t c = count_below8<Q4_RTN8_M_SHIFT, Q4_RTN8_M_LO, Q4_RTN8_M_NB>(lds.floor_m, lds.pair_m,
+                                                                                 (xb & 0x7FFFFFFFu) + neg);
+    return c | ((neg != 0u && c != 0u) ? 0x80u : 0u);
+}
+
+__device__ __forceinline__ uint32_t rtn8_v(const Step8Lds& lds, float x) {
+    return count_below8<Q4_RTN8_V_SHIFT, Q4_RTN8_V_LO, Q4_RTN8_V_NB>(lds.floor_v, lds.pair_v, __float_as_uint(x));
+}
+
+// Fills the tables; every thread of a 256-thread group takes part.
+__device__ void step8_tables(Step8Lds& lds) {
+    const int t = threadIdx.x;
+    const float inf = __builtin_inff();
+    lds.dec_m[t] = bits2f(c_cb8[0][t]);
+    lds.dec_v[t] = bits2f(c_cb8[1][t]);
+    // the same FP32 sum and halving the definition forms; SDyn8's codes
+    // 0..127 ascend from 0, Dyn8's codes 0..255 ascend from 0
+    if (t < 128) lds.mid_p[t] = t < 127 ? (bits2f(c_cb8[0][t]) + bits2f(c_cb8[0][t + 1])) * 0.5f : inf;
+    lds.mid_v[t] = t < 255 ? (bits2f(c_cb8[1][t]) + bits2f(c_cb8[1][t + 1])) * 0.5f : inf;
+    __syncthreads();
+    if (t < 128) lds.pair_m[t] = float2{lds.mid_p[t], t < 127 ? lds.mid_p[t + 1] : inf};
+    lds.pair_v[t] = float2{lds.mid_v[t], t < 255 ? lds.mid_v[t + 1] : inf};
+    for (int b = t; b < Q4_RTN8_M_NB; b += 256)
+        lds.floor_m[b] = (uint8_t)count_below_sorted<128>(lds.mid_p, bits2f((uint32_t)(b + Q4_RTN8_M_LO) << Q4_RTN8_M_SHIFT));
+    for (int b = t; b < Q4_RTN8_V_NB; b += 256)
+        lds.floor_v[b] = (uint8_t)count_below_sorted<256>(lds.mid_v, bits2f((uint32_t)(b + Q4_RTN8_V_LO) << Q4_RTN8_V_SHIFT));
+    __syncthreads();
 }
 
 template <bool FULL, bool CLIP>
@@ -916,8 +970,8 @@ __device__ __forceinline__ void step8_chunk(const DevTensor& T, const int64_t lc
     for (int k = 0; k < 8; ++k) {
         const float xm = fminf(fmaxf(m1[k] * inv_m, -1.0f), 1.0f);
         const float xv = fminf(v1[k] * inv_v, 1.0f);
-        mw[k >> 2] |= sdyn8_code(rtn8(lds.mid_m, xm)) << (8 * (k & 3));
-        vw[k >> 2] |= (uint32_t)rtn8(lds.mid_v, xv) << (8 * (k & 3));
+        mw[k >> 2] |= rtn8_m(lds, xm) << (8 * (k & 3));
+        vw[k >> 2] |= rtn8_v(lds, xv) << (8 * (k & 3));
     }
     if (FULL || nv == 8) {
         *reinterpret_cast<gptr<u32x2>>(mcodes + e0) = u32x2{mw[0], mw[1]};
@@ -942,17 +996,7 @@ __global__ __launch_bounds__(256) void k_step8(const DevTensor* __restrict__ tab
                                                 const int64_t* __restrict__ chunk_begin, int n_tensors,
                                                 int64_t total_chunks, StepScalars sc) {
     __shared__ Step8Lds lds;
-    {
-        const int t = threadIdx.x;  // 256 threads: one entry each
-        lds.dec_m[t] = bits2f(c_cb8[0][t]);
-        lds.dec_v[t] = bits2f(c_cb8[1][t]);
-        // FP32 midpoints of adjacent levels in ascending order, the same
-        // product the definition forms
-        lds.mid_m[t] = t < 254 ? (bits2f(c_cb8[0][sdyn8_code(t)]) + bits2f(c_cb8[0][sdyn8_code(t + 1)])) * 0.5f
-                               : __builtin_inff();
-        lds.mid_v[t] = t < 255 ? (bits2f(c_cb8[1][t]) + bits2f(c_cb8[1][t + 1])) * 0.5f : __builtin_inff();
-    }
-    __syncthreads();
+    step8_tables(lds);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float gs = CLIP ? *clip_of_table(tab) : 1.0f;

@@ -59,6 +59,37 @@ def test_library_8bit_codebooks_equal_oracle_construction(cb, cb8):
     assert np.array_equal(got.view(np.uint32), O.codebook8(cb8).view(np.uint32))
 
 
+_CB_INC = os.path.join(os.path.dirname(build.__file__), "csrc", "q4_codebooks.inc")
+
+
+@pytest.mark.parametrize("cb8,name", [(O.CB8_SDYN8, "M"), (O.CB8_DYN8, "V")])
+def test_8bit_nearest_level_buckets(cb8, name):
+    """The 8-bit step counts midpoints below x with a bucket table (key >> SHIFT
+    from LO, NB buckets, two candidate midpoints per bucket).  The compiled-in
+    bucket parameters must leave at most two of the oracle's positive
+    midpoints in any bucket, and the bucketed count must equal the plain count
+    at every midpoint, its FP32 neighbours, and a dense sample of [0, 1]."""
+    d = {k: int(v) for k, v in re.findall(r"#define Q4_RTN8_%s_(\w+) (\d+)" % name, open(_CB_INC).read())}
+    shift, lo, nb = d["SHIFT"], d["LO"], d["NB"]
+    mid = np.asarray(O.sorted_levels8(cb8)[2], np.float32)
+    mid = mid[np.isfinite(mid)]
+    pos = mid[mid > 0]
+    keys = pos.view(np.uint32)
+    assert keys[0] >> shift == lo
+    assert np.bincount((keys >> shift) - lo).max() <= 2
+    assert (np.uint32(0x3F800001) >> shift) - lo == nb - 1
+    pad = np.append(pos, np.full(256 - len(pos), np.inf, np.float32)).astype(np.float32)
+    lower = ((np.arange(nb, dtype=np.uint64) + lo) << shift).astype(np.uint32).view(np.float32)
+    floor = np.searchsorted(pad, lower, side="left")
+    x = np.concatenate([pos, np.nextafter(pos, np.float32(0)), np.nextafter(pos, np.float32(2)),
+                        np.linspace(0, 1, 1 << 20, dtype=np.float32), np.float32([0, 1, 1e-30])])
+    key = x.view(np.uint32)
+    b = np.clip((key >> shift).astype(np.int64) - lo, 0, nb - 1)
+    f = floor[b]
+    got = f + (pad[f] < x) + (pad[np.minimum(f + 1, 255)] < x)
+    assert np.array_equal(got, np.searchsorted(pos, x, side="left"))
+
+
 def test_8bit_recipe_is_one_configuration():
     """[A] "Requirements and errors": 4-bit and 8-bit options do not mix."""
     b = q4.q4adamw_default_config(q4.RECIPE_BLOCK8)
