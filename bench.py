@@ -61,10 +61,15 @@ def kernel_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def step_kernel(recipe: str) -> str:
+    """The kernel that dominates a recipe's step."""
+    return {"block8": "k_step8", "fp32": "k_fp32_step"}.get(recipe, "k_fused_step")
+
+
 def read_traffic(workload_name: str, recipe: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if
     it was taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", f"k_fused_step_{workload_name}_{recipe}_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"{step_kernel(recipe)}_{workload_name}_{recipe}_counters.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -267,11 +272,12 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "params": n, "tensors": len(wl.tensors), "recipe": args.recipe,
-                   "block": 128, "state": "4-bit codes + FP32 block scales per moment",
+                   "block": 128, "state": ("8-bit" if args.recipe == "block8" else "4-bit")
+                   + " codes + FP32 block scales per moment",
                    "grads": "bf16", "masters": "fp32"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "k_fused_step", "alg_bytes_per_launch": ab,
+                     "kernel": step_kernel(args.recipe), "alg_bytes_per_launch": ab,
                      "alg_bytes_per_param": ab / n, "avg_launch_ms": avg_launch},
     }
     try:

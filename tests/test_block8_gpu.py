@@ -113,3 +113,24 @@ def test_gpt_162m_sampled_20_steps():
     wins = parity.sample_windows(w, n_random=32, seed=5)
     _flush("block8 gpt-162m")
     run_windows(w, 20, windows=wins, grads_on="cuda")
+
+
+def test_gpt_2_7b_sampled():
+    """The GPT-style 2.7B set in the launch configuration the benchmark times,
+    10 steps, first/last blocks of every tensor and random interior windows."""
+    w = inputs.gpt_2_7b()
+    wins = parity.sample_windows(w, n_random=48, seed=6)
+    _flush("block8 gpt-2.7b")
+    run_windows(w, 10, windows=wins, grads_on="cuda")
+
+
+def test_tensor_beyond_2_32_elements():
+    """One tensor of 2^32 + 1000 elements: 64-bit element and code offsets,
+    a ragged last block."""
+    n = (1 << 32) + 1000
+    w = inputs.custom([(n,)], grad_kind="masked", seed=28)
+    nb = (n + 127) // 128
+    lo32, lo31 = (1 << 32) // 128, (1 << 31) // 128
+    wins = [(0, 0, 2), (0, lo31 - 2, lo31 + 2), (0, lo32 - 3, lo32 + 3), (0, nb - 3, nb)]
+    _flush("block8 2^32 + 1000 elements")
+    run_windows(w, 2, windows=wins, grads_on="cuda")
