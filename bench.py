@@ -148,7 +148,9 @@ def time_step_before(workload, recipe: str, steps: int, warmup: int, max_grad_no
         step += 1
         state.step(params, grads, step, grad_stats=True, max_grad_norm=max_grad_norm, **hp)
     torch.cuda.synchronize()
-    acc_ms, step_ms = [], []
+    # enqueued back to back, as a training loop would: the events then time
+    # the GPU work, not the host's launch overhead
+    ev = []
     for _ in range(steps):
         a0, a1, s1 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         a0.record(stream)
@@ -157,9 +159,10 @@ def time_step_before(workload, recipe: str, steps: int, warmup: int, max_grad_no
         step += 1
         state.step(params, grads, step, grad_stats=True, max_grad_norm=max_grad_norm, **hp)
         s1.record(stream)
-        torch.cuda.synchronize()
-        acc_ms.append(a0.elapsed_time(a1))
-        step_ms.append(a1.elapsed_time(s1))
+        ev.append((a0, a1, s1))
+    torch.cuda.synchronize()
+    acc_ms = [a0.elapsed_time(a1) for a0, a1, _ in ev]
+    step_ms = [a1.elapsed_time(s1) for _, a1, s1 in ev]
     return sum(acc_ms) / len(acc_ms), sum(step_ms) / len(step_ms)
 
 

@@ -231,13 +231,19 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 // Workspace layout of a step.
 
 struct Plan {
-    size_t off_tab, off_chunks, off_mats, off_inv, off_prow, off_pcol, off_pmean, off_sqpart, total;
+    size_t off_tab, off_chunks, off_mats, off_tab1, off_chunks1, off_inv, off_prow, off_pcol, off_pmean, off_sqpart,
+        total;
     int64_t total_chunks = 0;
     int n_mats = 0;
     int64_t total_tiles = 0, total_rgroups = 0, total_cgroups = 0;
     std::vector<DevTensor> tab;
     std::vector<int64_t> chunks;
     std::vector<DevMatrix> mats;
+    // with matrices: the other tensors alone and their chunk prefix, for
+    // the chunk-order pass that runs beside the tile kernel
+    std::vector<DevTensor> tab1;
+    std::vector<int64_t> chunks1;
+    int64_t total_chunks1 = 0;
 };
 
 void plan_layout(const Resolved& r, const q4_tensor* t, int32_t n, Plan& P, uint8_t* ws) {
@@ -297,10 +303,24 @@ void plan_layout(const Resolved& r, const q4_tensor* t, int32_t n, Plan& P, uint
     }
     P.chunks[n] = P.total_chunks;
     P.n_mats = (int)P.mats.size();
+    P.tab1.clear();
+    P.chunks1.clear();
+    P.total_chunks1 = 0;
+    if (P.n_mats > 0) {
+        for (int32_t i = 0; i < n; ++i) {
+            if (P.tab[i].kind == KIND_FACTORED && P.tab[i].numel > 0) continue;
+            P.chunks1.push_back(P.total_chunks1);
+            P.tab1.push_back(P.tab[i]);  // keeps its chunk_begin in the full prefix (the flat offset)
+            P.total_chunks1 += P.chunks[i + 1] - P.chunks[i];
+        }
+        P.chunks1.push_back(P.total_chunks1);
+    }
     size_t o = kWsOffTable;
     P.off_tab = o;       o = round256(o + sizeof(DevTensor) * n);
     P.off_chunks = o;    o = round256(o + sizeof(int64_t) * (n + 1));
     P.off_mats = o;      o = round256(o + sizeof(DevMatrix) * P.mats.size());
+    P.off_tab1 = o;      o = round256(o + sizeof(DevTensor) * P.tab1.size());
+    P.off_chunks1 = o;   o = round256(o + sizeof(int64_t) * P.chunks1.size());
     P.off_inv = o;       o = round256(o + sizeof(float) * P.mats.size());
     P.off_prow = o;      o = round256(o + sizeof(double) * prow);
     P.off_pcol = o;      o = round256(o + sizeof(double) * pcol);
@@ -358,6 +378,10 @@ q4_status upload_tables(const Plan& P, int32_t n, uint8_t* wsb, hipStream_t st) 
     std::memcpy(host.data() + (P.off_chunks - P.off_tab), P.chunks.data(), sizeof(int64_t) * (n + 1));
     if (!P.mats.empty())
         std::memcpy(host.data() + (P.off_mats - P.off_tab), P.mats.data(), sizeof(DevMatrix) * P.mats.size());
+    if (!P.tab1.empty())
+        std::memcpy(host.data() + (P.off_tab1 - P.off_tab), P.tab1.data(), sizeof(DevTensor) * P.tab1.size());
+    if (!P.chunks1.empty())
+        std::memcpy(host.data() + (P.off_chunks1 - P.off_tab), P.chunks1.data(), sizeof(int64_t) * P.chunks1.size());
     const hipError_t e = hipMemcpyAsync(wsb + P.off_tab, host.data(), upload, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return hip_fail(e, "tensor table upload");
     return Q4_OK;
@@ -620,8 +644,9 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
             // one read of the gradients: their norm and, for factored
             // matrices, the row/column partials the step needs anyway
             e = launch_grad_pass(GRAD_STATS_ONLY, true, P.n_mats > 0, d_tab, d_chunks, n, P.total_chunks, d_mats,
-                                 P.n_mats, P.total_tiles, nullptr, reinterpret_cast<double*>(wsb + P.off_sqpart), sq,
-                                 st);
+                                 P.n_mats, P.total_tiles, reinterpret_cast<const DevTensor*>(wsb + P.off_tab1),
+                                 reinterpret_cast<const int64_t*>(wsb + P.off_chunks1), (int)P.tab1.size(),
+                                 P.total_chunks1, nullptr, reinterpret_cast<double*>(wsb + P.off_sqpart), sq, st);
             if (e != hipSuccess) return hip_fail(e, "gradient statistics launch");
             stats_ready = true;
         }
@@ -723,7 +748,10 @@ q4_status q4adamw_accumulate(const q4_config* cfg, const q4_tensor* t, int32_t n
                                           reinterpret_cast<const DevTensor*>(wsb + P.off_tab),
                                           reinterpret_cast<const int64_t*>(wsb + P.off_chunks), n, P.total_chunks,
                                           reinterpret_cast<const DevMatrix*>(wsb + P.off_mats), P.n_mats,
-                                          P.total_tiles, micro, reinterpret_cast<double*>(wsb + P.off_sqpart),
+                                          P.total_tiles, reinterpret_cast<const DevTensor*>(wsb + P.off_tab1),
+                                          reinterpret_cast<const int64_t*>(wsb + P.off_chunks1),
+                                          (int)P.tab1.size(), P.total_chunks1, micro,
+                                          reinterpret_cast<double*>(wsb + P.off_sqpart),
                                           reinterpret_cast<double*>(wsb + kWsOffSq), st);
     if (e != hipSuccess) return hip_fail(e, "accumulate launch");
     return ok();
@@ -742,7 +770,10 @@ q4_status q4adamw_grad_stats(const q4_config* cfg, const q4_tensor* t, int32_t n
                                           reinterpret_cast<const DevTensor*>(wsb + P.off_tab),
                                           reinterpret_cast<const int64_t*>(wsb + P.off_chunks), n, P.total_chunks,
                                           reinterpret_cast<const DevMatrix*>(wsb + P.off_mats), P.n_mats,
-                                          P.total_tiles, nullptr, reinterpret_cast<double*>(wsb + P.off_sqpart),
+                                          P.total_tiles, reinterpret_cast<const DevTensor*>(wsb + P.off_tab1),
+                                          reinterpret_cast<const int64_t*>(wsb + P.off_chunks1),
+                                          (int)P.tab1.size(), P.total_chunks1, nullptr,
+                                          reinterpret_cast<double*>(wsb + P.off_sqpart),
                                           reinterpret_cast<double*>(wsb + kWsOffSq), st);
     if (e != hipSuccess) return hip_fail(e, "gradient statistics launch");
     return ok();

@@ -107,9 +107,13 @@ hipError_t launch_factored_stats(const DevMatrix* d_mats, int n_mats, int64_t to
 // factored row/column partials of matrices (when `tiles_for_matrices`) and
 // the binary64 sums of squares in sq_part (kAccGroups + total_tiles slots),
 // then their total in *sq.
+// With last and matrices, the tile kernel takes the matrices and the chunk
+// pass runs over d_tab1 / d_chunks1 (the other tensors alone, each entry
+// keeping its chunk_begin in the full prefix for the flat offset).
 hipError_t launch_grad_pass(int mode, bool last, bool tiles_for_matrices, const DevTensor* d_tab,
                             const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks, const DevMatrix* d_mats,
-                            int n_mats, int64_t total_tiles, const uint16_t* micro, double* sq_part, double* sq,
+                            int n_mats, int64_t total_tiles, const DevTensor* d_tab1, const int64_t* d_chunks1,
+                            int n_tensors1, int64_t total_chunks1, const uint16_t* micro, double* sq_part, double* sq,
                             hipStream_t stream);
 // *clip = min(1, max_norm / (sqrt(*sq) + 1e-6)) rounded to FP32.
 hipError_t launch_clip_factor(const double* sq, float max_norm, float* clip, hipStream_t stream);

@@ -1206,30 +1206,29 @@ __global__ __launch_bounds__(256) void k_rowcol_partial(const DevMatrix* __restr
     }
 }
 
-// The accumulation / statistics pass in chunk order over every tensor (but
-// the factored matrices when skip_factored: the tile kernel above takes
-// them), grid-stride over tensor-aligned chunks of 512 elements, lane l on
-// elements 8l .. 8l+7.  micro holds the microbatch gradients flat: tensor i
-// at element 512 * chunk_begin(i).  With LAST each lane keeps a binary64 sum
+// The accumulation / statistics pass in chunk order over the tensors of
+// `tab` (every tensor, or all but the factored matrices when the tile kernel
+// above takes them), grid-stride over tensor-aligned chunks of 512 elements
+// numbered by the prefix `chunk_begin`, lane l on elements 8l .. 8l+7.  micro
+// holds the microbatch gradients flat: tensor i at element 512 times its
+// chunk_begin in the full prefix (the table entry's own field).  With LAST each lane keeps a binary64 sum
 // of its squares over its chunks; the work-group leaves the sum of its four
 // waves at sq_part[blockIdx.x].
 template <int MODE, bool LAST>
 __global__ __launch_bounds__(256) void k_grad_chunks(const DevTensor* __restrict__ tab,
                                                       const int64_t* __restrict__ chunk_begin, int n_tensors,
-                                                      int64_t total_chunks, int skip_factored,
-                                                      const uint16_t* __restrict__ micro,
+                                                      int64_t total_chunks, const uint16_t* __restrict__ micro,
                                                       double* __restrict__ sq_part) {
     __shared__ double lds[kWavesPerGroup];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     double sq = 0.0;
+    const int64_t stride = (int64_t)gridDim.x * kWavesPerGroup;
     int t = first_tensor(chunk_begin, n_tensors, (int64_t)blockIdx.x * kWavesPerGroup + wave);
-    for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks;
-         c += (int64_t)gridDim.x * kWavesPerGroup) {
+    for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks; c += stride) {
         while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
         const DevTensor T = tab[t];
-        if (skip_factored && T.kind == KIND_FACTORED) continue;
-        const int64_t lc = c - T.chunk_begin;
+        const int64_t lc = c - chunk_begin[t];
         const int64_t e0 = lc * kChunkElems + lane * 8;
         const int64_t rem = T.numel - e0;
         const int nv = rem >= 8 ? 8 : (rem > 0 ? (int)rem : 0);
@@ -1500,33 +1499,41 @@ hipError_t launch_factored_stats(const DevMatrix* d_mats, int n_mats, int64_t to
 
 template <int MODE>
 static void launch_grad_mode(bool last, int64_t groups, const DevTensor* d_tab, const int64_t* d_chunk_begin,
-                             int n_tensors, int64_t total_chunks, int skip_factored, const uint16_t* micro,
-                             double* sq_part, hipStream_t stream) {
+                             int n_tensors, int64_t total_chunks, const uint16_t* micro, double* sq_part,
+                             hipStream_t stream) {
     if (last)
         k_grad_chunks<MODE, true><<<(unsigned)groups, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks,
-                                                                        skip_factored, micro, sq_part);
+                                                                        micro, sq_part);
     else
         k_grad_chunks<MODE, false><<<(unsigned)groups, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors,
-                                                                         total_chunks, skip_factored, micro, sq_part);
+                                                                         total_chunks, micro, sq_part);
 }
 
 hipError_t launch_grad_pass(int mode, bool last, bool tiles_for_matrices, const DevTensor* d_tab,
                             const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks, const DevMatrix* d_mats,
-                            int n_mats, int64_t total_tiles, const uint16_t* micro, double* sq_part, double* sq,
+                            int n_mats, int64_t total_tiles, const DevTensor* d_tab1, const int64_t* d_chunks1,
+                            int n_tensors1, int64_t total_chunks1, const uint16_t* micro, double* sq_part, double* sq,
                             hipStream_t stream) {
     const bool tiles = last && tiles_for_matrices && n_mats > 0;
+    if (tiles) {
+        // the chunk pass covers the other tensors only
+        d_tab = d_tab1;
+        d_chunk_begin = d_chunks1;
+        n_tensors = n_tensors1;
+        total_chunks = total_chunks1;
+    }
     int64_t groups = 0;
     if (total_chunks > 0) {
         groups = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
         if (groups > kAccGroups) groups = kAccGroups;
         if (mode == GRAD_STATS_ONLY)
-            launch_grad_mode<GRAD_STATS_ONLY>(last, groups, d_tab, d_chunk_begin, n_tensors, total_chunks, tiles, micro,
+            launch_grad_mode<GRAD_STATS_ONLY>(last, groups, d_tab, d_chunk_begin, n_tensors, total_chunks, micro,
                                               sq_part, stream);
         else if (mode == GRAD_FIRST)
-            launch_grad_mode<GRAD_FIRST>(last, groups, d_tab, d_chunk_begin, n_tensors, total_chunks, tiles, micro,
+            launch_grad_mode<GRAD_FIRST>(last, groups, d_tab, d_chunk_begin, n_tensors, total_chunks, micro,
                                          sq_part, stream);
         else
-            launch_grad_mode<GRAD_ADD>(last, groups, d_tab, d_chunk_begin, n_tensors, total_chunks, tiles, micro,
+            launch_grad_mode<GRAD_ADD>(last, groups, d_tab, d_chunk_begin, n_tensors, total_chunks, micro,
                                        sq_part, stream);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

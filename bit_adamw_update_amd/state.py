@@ -67,6 +67,7 @@ class Q4State:
         self.ws_bytes = api.q4adamw_workspace_bytes(self.cfg, desc)
         self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=self.device)
         self._last_key = None
+        self._flat = None
         api.q4adamw_init_state(self.cfg, desc, stream)
 
     def describe(self, params, grads) -> list:
@@ -123,7 +124,10 @@ class Q4State:
 
     def flat_offsets(self) -> tuple[list, int]:
         """Element offsets of each tensor in a flat microbatch gradient buffer, and its length."""
-        return api.q4adamw_flat_offsets(self.describe(None, None))
+        if self._flat is None:   # fixed by the shapes
+            self._flat = api.q4adamw_flat_offsets(self.describe(None, None))
+        offs, total = self._flat
+        return list(offs), total
 
     def accumulate(self, params, grads, micro, first: bool, last: bool, stream=None) -> None:
         """grads <- micro (first) or bf16(grads + micro), from the flat BF16
