@@ -368,12 +368,30 @@ __device__ __forceinline__ const BucketEntry& bucket_of(const BucketEntry* tab, 
 // K1: the fused step for packed and factored tensors
 // ---------------------------------------------------------------------------
 
-template <int MCB, int VCB> struct StepLds {
-    BucketEntry enc_m[Enc<MCB>::SIZE];
+// Flat bucket layout, for the ZIP-SR kernels (their VALU issue rate is what
+// bounds them): the entry of x in [-1, 1] sits at its bit pattern >> 20
+// (sign, exponent, 3 mantissa bits), slots 0 .. 1016 for x >= 0 and
+// 2048 .. 3064 for x < 0, so finding it is a shift; the v floor entries of
+// x in [0, 1] fill the slots between, at 1017 + (bits >> 20).  Each flat
+// bucket lies inside one bucket of the compact tables above (which merge
+// the magnitudes below the smallest midpoint), so it takes that entry.
+constexpr int kFlatPos = (127 << 3) + 1;          // bits >> 20 of x in [+0, 1]
+constexpr int kFlatNeg = 2048;                     // bits >> 20 of x in [-1, -0]
+constexpr int kFlatSlots = kFlatNeg + kFlatPos;
+static_assert(2 * kFlatPos <= kFlatNeg, "the floor entries must fit between the two halves");
+
+template <int VCB, int VRULE> constexpr bool flat_tables() {
+    return VRULE == Q4_RULE_UPDATE_SR && VCB == Q4_CB_DYN4;
+}
+
+template <int MCB, int VCB, bool FLAT> struct StepLds {
+    BucketEntry enc_m[FLAT ? 1 : Enc<MCB>::SIZE];
     BucketEntry enc_v[Enc<VCB>::SIZE];
-    FloorEntry floor_v[VCB == Q4_CB_DYN4 ? Enc<VCB>::NPOS : 1];
+    FloorEntry floor_v[(VCB == Q4_CB_DYN4 && !FLAT) ? Enc<VCB>::NPOS : 1];
+    BucketEntry flat[FLAT ? kFlatSlots : 1];  // m entries; v floor entries as {thr, lo}
     float lev_m[16], lev_v[16];  // sorted levels (rare SR paths)
 };
+
 
 // Per-lane constants of the codebooks: lane `sub` of each 16-lane row holds
 // the code-`sub` level of each map (decode) and the sorted level `sub` of v.
@@ -383,16 +401,28 @@ struct LaneBooks {
 
 template <int MCB, int VCB, int VRULE, bool FULL, bool PACKED, bool CLIP>
 __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc, const int64_t chunk,
-                                           const StepScalars& sc, const StepLds<MCB, VCB>& lds,
+                                           const StepScalars& sc,
+                                           const StepLds<MCB, VCB, flat_tables<VCB, VRULE>()>& lds,
                                            const LaneBooks& lb, const int lane, const float gs) {
     constexpr int NM = Book<MCB>::N, NV = Book<VCB>::N;
+    constexpr bool FLAT = flat_tables<VCB, VRULE>();
+    // the m bucket entry of x in [-1, 1] (the clamps below keep every x,
+    // NaN included, in that range, so a flat index stays inside its half)
+    auto m_entry = [&](float x) -> const BucketEntry& {
+        if constexpr (FLAT) return lds.flat[__float_as_uint(x) >> 20];
+        else return bucket_of<MCB>(lds.enc_m, x);
+    };
     constexpr bool V_SR = VRULE == Q4_RULE_STATE_SR || VRULE == Q4_RULE_UPDATE_SR;
     constexpr bool V_UPD = VRULE == Q4_RULE_UPDATE_SR || VRULE == Q4_RULE_UPDATE_RTN;
     const int sub = lane & 15, row_base = lane & 48;
     const uint32_t rb4 = (uint32_t)row_base << 2;
     const int64_t n = T.numel;
     const int64_t blk = lc * kBlocksPerChunk + (lane >> 4);
-    const int64_t e0 = blk * kBlock + sub * 8;
+    // the chunk's bases are wave-uniform (scalar registers); a lane adds a
+    // 32-bit offset, so no per-lane 64-bit address arithmetic
+    const int64_t c0 = lc * kChunkElems;
+    const int le = lane * 8;  // the lane's first element within the chunk
+    const int64_t e0 = c0 + le;
     int nv = 8;
     bool blk_ok = true;
     if (!FULL) {
@@ -401,38 +431,39 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
         blk_ok = blk * kBlock < n;
     }
     constexpr bool packed_v = PACKED;  // packed v; else the factored estimate
-    const gptr<float> param = G(T.param);
-    const gptr<const uint16_t> grad = G(T.grad);
-    const gptr<uint8_t> mcodes = G(T.m_codes);
-    const gptr<uint8_t> vcodes = G(T.v_codes);
-    const gptr<float> mscales = G(T.m_scales);
-    const gptr<float> vscales = G(T.v_scales);
+    const gptr<float> param = G(T.param) + c0;
+    const gptr<const uint16_t> grad = G(T.grad) + c0;
+    const gptr<uint8_t> mcodes = G(T.m_codes) + (c0 >> 1);
+    const gptr<uint8_t> vcodes = G(T.v_codes) + (c0 >> 1);
+    const gptr<float> mscales = G(T.m_scales) + lc * kBlocksPerChunk;
+    const gptr<float> vscales = G(T.v_scales) + lc * kBlocksPerChunk;
+    const int lb4 = lane >> 4;  // the lane's block within the chunk
 
     // ---- loads
     float p[8], g[8];
     uint32_t mc = 0, vc = 0;
     if (FULL || nv == 8) {
-        const f32x4 a = *reinterpret_cast<const gptr<const f32x4>>(param + e0);
-        const f32x4 b = *reinterpret_cast<const gptr<const f32x4>>(param + e0 + 4);
+        const f32x4 a = *reinterpret_cast<const gptr<const f32x4>>(param + le);
+        const f32x4 b = *reinterpret_cast<const gptr<const f32x4>>(param + le + 4);
         p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
-        const u32x4 gq = *reinterpret_cast<const gptr<const u32x4>>(grad + e0);
+        const u32x4 gq = *reinterpret_cast<const gptr<const u32x4>>(grad + le);
         g[0] = bf16_to_f32(gq.x & 0xFFFFu); g[1] = bf16_to_f32(gq.x >> 16);
         g[2] = bf16_to_f32(gq.y & 0xFFFFu); g[3] = bf16_to_f32(gq.y >> 16);
         g[4] = bf16_to_f32(gq.z & 0xFFFFu); g[5] = bf16_to_f32(gq.z >> 16);
         g[6] = bf16_to_f32(gq.w & 0xFFFFu); g[7] = bf16_to_f32(gq.w >> 16);
-        mc = *reinterpret_cast<const gptr<const uint32_t>>(mcodes + (e0 >> 1));
-        if (packed_v) vc = *reinterpret_cast<const gptr<const uint32_t>>(vcodes + (e0 >> 1));
+        mc = *reinterpret_cast<const gptr<const uint32_t>>(mcodes + (le >> 1));
+        if (packed_v) vc = *reinterpret_cast<const gptr<const uint32_t>>(vcodes + (le >> 1));
     } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            p[k] = k < nv ? param[e0 + k] : 0.0f;
-            g[k] = k < nv ? bf16_to_f32(grad[e0 + k]) : 0.0f;
+            p[k] = k < nv ? param[le + k] : 0.0f;
+            g[k] = k < nv ? bf16_to_f32(grad[le + k]) : 0.0f;
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             if (2 * j < nv) {
-                mc |= (uint32_t)mcodes[(e0 >> 1) + j] << (8 * j);
-                if (packed_v) vc |= (uint32_t)vcodes[(e0 >> 1) + j] << (8 * j);
+                mc |= (uint32_t)mcodes[(le >> 1) + j] << (8 * j);
+                if (packed_v) vc |= (uint32_t)vcodes[(le >> 1) + j] << (8 * j);
             }
         }
     }
@@ -441,8 +472,8 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
 #pragma unroll
         for (int k = 0; k < 8; ++k) g[k] *= gs;
     }
-    const float sm_old = (FULL || blk_ok) ? mscales[blk] : 0.0f;
-    const float sv_old = ((FULL || blk_ok) && packed_v) ? vscales[blk] : 0.0f;
+    const float sm_old = (FULL || blk_ok) ? mscales[lb4] : 0.0f;
+    const float sv_old = ((FULL || blk_ok) && packed_v) ? vscales[lb4] : 0.0f;
     // lane `sub` of the row holds level(sub) * old scale: decoding is one
     // ds_bpermute per element (the same product the definition forms)
     const float dm_own = lb.dec_m * sm_old;
@@ -531,12 +562,12 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
         }
     }
     if (FULL || nv == 8) {
-        *reinterpret_cast<gptr<f32x4>>(param + e0) = f32x4{p[0], p[1], p[2], p[3]};
-        *reinterpret_cast<gptr<f32x4>>(param + e0 + 4) = f32x4{p[4], p[5], p[6], p[7]};
+        *reinterpret_cast<gptr<f32x4>>(param + le) = f32x4{p[0], p[1], p[2], p[3]};
+        *reinterpret_cast<gptr<f32x4>>(param + le + 4) = f32x4{p[4], p[5], p[6], p[7]};
     } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            if (k < nv) param[e0 + k] = p[k];
+            if (k < nv) param[le + k] = p[k];
     }
 
     // ---- first moment: absmax scale of the block, RTN or state-space SR
@@ -551,7 +582,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const float x = fminf(fmaxf(m1[k] * inv_m, -1.0f), 1.0f);
-            const BucketEntry& e = bucket_of<MCB>(lds.enc_m, x);
+            const BucketEntry& e = m_entry(x);
             const int idx = e.base + (x > e.thr ? 1 : 0);
             const int code = MCB == Q4_CB_SDYN4 ? (idx < 7 ? 15 - idx : (idx == 7 ? 0 : idx - 7)) : idx;
             mword |= (uint32_t)code << (4 * k);
@@ -562,7 +593,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
         for (int k = 0; k < 8; ++k) {
             if ((k & 3) == 0) uniforms4((uint32_t)(e0 >> 2) + (k >> 2), sc.step, T.tensor_id, 0u, sc.key0, sc.key1, um);
             const float x = fminf(fmaxf(m1[k] * inv_m, -1.0f), 1.0f);
-            const BucketEntry& e = bucket_of<MCB>(lds.enc_m, x);
+            const BucketEntry& e = m_entry(x);
             const bool gt = x > e.thr;
             const int idx = e.base + (gt ? 1 : 0);
             const float Lidx = lds.lev_m[idx];
@@ -578,15 +609,15 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
         }
     }
     if (FULL || nv == 8) {
-        *reinterpret_cast<gptr<uint32_t>>(mcodes + (e0 >> 1)) = mword;
+        *reinterpret_cast<gptr<uint32_t>>(mcodes + (le >> 1)) = mword;
     } else {
         // nibbles past the end of the tensor stay 0
         mword &= (1u << (4 * nv)) - 1u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (2 * j < nv) mcodes[(e0 >> 1) + j] = (uint8_t)(mword >> (8 * j));
+            if (2 * j < nv) mcodes[(le >> 1) + j] = (uint8_t)(mword >> (8 * j));
     }
-    if ((FULL || blk_ok) && sub == 0) mscales[blk] = s_m;
+    if ((FULL || blk_ok) && sub == 0) mscales[lb4] = s_m;
 
     if constexpr (!packed_v) return;
 
@@ -621,10 +652,21 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
             const float x = fminf(v1[k] * inv_v, 1.0f);
             // lower level: the floor bucket gives it directly; an exact level
             // hit needs no draw (the top level 1 can only be hit exactly)
-            const FloorEntry& f = lds.floor_v[bucket_index<VCB>(x)];
-            const bool ge = x >= f.thr;
-            const int lo = f.lo + (ge ? 1 : 0);
-            const bool hit = x == f.thr;
+            float fthr;
+            int flo;
+            if constexpr (FLAT) {
+                // 11 bits: the slot stays below the negative half for any x
+                const BucketEntry& f = lds.flat[kFlatPos + __builtin_amdgcn_ubfe(__float_as_uint(x), 20, 11)];
+                fthr = f.thr;
+                flo = f.base;
+            } else {
+                const FloorEntry& f = lds.floor_v[bucket_index<VCB>(x)];
+                fthr = f.thr;
+                flo = f.lo;
+            }
+            const bool ge = x >= fthr;
+            const int lo = flo + (ge ? 1 : 0);
+            const bool hit = x == fthr;
             const int src = row_base + lo;
             const float rlo = bperm(root_own, src);
             const float rhe = bperm(rnext_eps, src);
@@ -678,12 +720,12 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     }
     }
     if (FULL || nv == 8) {
-        *reinterpret_cast<gptr<uint32_t>>(vcodes + (e0 >> 1)) = vword;
+        *reinterpret_cast<gptr<uint32_t>>(vcodes + (le >> 1)) = vword;
     } else {
         vword &= (1u << (4 * nv)) - 1u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (2 * j < nv) vcodes[(e0 >> 1) + j] = (uint8_t)(vword >> (8 * j));
+            if (2 * j < nv) vcodes[(le >> 1) + j] = (uint8_t)(vword >> (8 * j));
     }
     float stored = s_v;
     if (eden) {
@@ -693,7 +735,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
         const float S = sxq > 0.0f ? sxx / sxq : 1.0f;
         stored = s_v * S;
     }
-    if ((FULL || blk_ok) && sub == 0) vscales[blk] = stored;
+    if ((FULL || blk_ok) && sub == 0) vscales[lb4] = stored;
 }
 
 // Last tensor whose first chunk is <= c (binary search over the prefix).
@@ -719,15 +761,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves<
 void k_fused_step(const DevTensor* __restrict__ tab,
                                                      const int64_t* __restrict__ chunk_begin, int n_tensors,
                                                      int64_t total_chunks, StepScalars sc) {
-    __shared__ StepLds<MCB, VCB> lds;
+    constexpr bool FLAT = flat_tables<VCB, VRULE>();
+    __shared__ StepLds<MCB, VCB, FLAT> lds;
     {
         // stage the bucket tables and sorted levels in LDS
         const BucketEntry* gm = enc_table_global<MCB>();
         const BucketEntry* gv = enc_table_global<VCB>();
-        for (int i = threadIdx.x; i < Enc<MCB>::SIZE; i += blockDim.x) lds.enc_m[i] = gm[i];
         for (int i = threadIdx.x; i < Enc<VCB>::SIZE; i += blockDim.x) lds.enc_v[i] = gv[i];
-        if constexpr (VCB == Q4_CB_DYN4)
-            for (int i = threadIdx.x; i < Enc<VCB>::NPOS; i += blockDim.x) lds.floor_v[i] = c_floor_dyn4.e[i];
+        if constexpr (FLAT) {
+            // each flat slot takes the compact entry of a value inside it
+            for (int i = threadIdx.x; i < kFlatSlots; i += blockDim.x) {
+                BucketEntry d{3.0f, 0};
+                if (i < kFlatPos) {
+                    d = gm[bucket_index<MCB>(bits2f((uint32_t)i << 20))];
+                } else if (i >= kFlatNeg) {
+                    d = gm[bucket_index<MCB>(bits2f(0x80000000u | ((uint32_t)(i - kFlatNeg) << 20)))];
+                } else if (i - kFlatPos < kFlatPos) {
+                    const FloorEntry& f = c_floor_dyn4.e[bucket_index<VCB>(bits2f((uint32_t)(i - kFlatPos) << 20))];
+                    d.thr = f.thr;
+                    d.base = f.lo;
+                }
+                lds.flat[i] = d;
+            }
+        } else {
+            for (int i = threadIdx.x; i < Enc<MCB>::SIZE; i += blockDim.x) lds.enc_m[i] = gm[i];
+            if constexpr (VCB == Q4_CB_DYN4)
+                for (int i = threadIdx.x; i < Enc<VCB>::NPOS; i += blockDim.x) lds.floor_v[i] = c_floor_dyn4.e[i];
+        }
         if (threadIdx.x < 16) {
             const int t = threadIdx.x;
             lds.lev_m[t] = t < Book<MCB>::N ? sorted_level_rt<MCB>(t) : 1.0f;
