@@ -211,6 +211,22 @@ __device__ __forceinline__ float sqrt_rn_normal(float x) {
     return r;
 }
 
+// 1/s of a block scale s >= 0 (0 for s = 0).  For s in [2^-126, 2^126) the
+// hardware reciprocal refined by one FMA Newton step equals the IEEE
+// quotient (an exhaustive comparison over every float of that range found
+// no difference); a wave with a lane outside the range divides.
+__device__ __forceinline__ float inv_scale(float s) {
+    const bool fast = s >= 0x1p-126f && s < 0x1p126f;
+    float r;
+    if (__builtin_amdgcn_ballot_w64(!fast && s > 0.0f) == 0) {
+        const float y = __builtin_amdgcn_rcpf(s);
+        r = __builtin_fmaf(__builtin_fmaf(-s, y, 1.0f), y, y);
+    } else {
+        r = 1.0f / s;
+    }
+    return s > 0.0f ? r : 0.0f;
+}
+
 // ---------------------------------------------------------------------------
 // Global-memory views
 // ---------------------------------------------------------------------------
@@ -575,7 +591,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
 #pragma unroll
     for (int k = 0; k < 8; ++k) am = fmaxf(am, fabsf(m1[k]));
     const float s_m = row_max16(am);
-    const float inv_m = s_m > 0.0f ? 1.0f / s_m : 0.0f;
+    const float inv_m = inv_scale(s_m);
     const bool m_sr = (sc.flags & SF_M_SR_ALL) || ((T.flags & Q4_TF_LM_HEAD) && (sc.flags & SF_LM_HEAD_SR));
     uint32_t mword = 0;
     if (!m_sr) {
@@ -626,7 +642,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
 #pragma unroll
     for (int k = 0; k < 8; ++k) av = fmaxf(av, v1[k]);
     const float s_v = row_max16(av);
-    const float inv_v = s_v > 0.0f ? 1.0f / s_v : 0.0f;
+    const float inv_v = inv_scale(s_v);
     // lane `sub` holds sqrt(level_sub * s_v): the square root of the state
     // each level would store, for the preconditioner-space rules
     const float root_own = V_UPD ? sqrtf(lb.lev_v * s_v) : 0.0f;
@@ -1023,8 +1039,8 @@ __device__ __forceinline__ void step8_chunk(const DevTensor& T, const int64_t lc
         av = fmaxf(av, v1[k]);
     }
     const float s_m = row_max16(am), s_v = row_max16(av);
-    const float inv_m = s_m > 0.0f ? 1.0f / s_m : 0.0f;
-    const float inv_v = s_v > 0.0f ? 1.0f / s_v : 0.0f;
+    const float inv_m = inv_scale(s_m);
+    const float inv_v = inv_scale(s_v);
     uint32_t mw[2] = {0u, 0u}, vw[2] = {0u, 0u};
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
