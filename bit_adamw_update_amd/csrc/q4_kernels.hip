@@ -754,6 +754,15 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     if ((FULL || blk_ok) && sub == 0) vscales[lb4] = stored;
 }
 
+// The work-group's logical index: the dispatcher hands work-groups to the
+// 8 XCDs in turn, so group b runs on XCD b mod 8; numbering the groups of
+// one XCD consecutively gives each XCD a contiguous share of every sweep.
+__device__ __forceinline__ int64_t xcd_group() {
+    const uint32_t b = blockIdx.x, n = gridDim.x;
+    const uint32_t q = n >> 3, r = n & 7u, x = b & 7u;
+    return (int64_t)(x * q + (x < r ? x : r) + (b >> 3));
+}
+
 // Last tensor whose first chunk is <= c (binary search over the prefix).
 __device__ __forceinline__ int first_tensor(const int64_t* __restrict__ chunk_begin, int n_tensors, int64_t c) {
     int lo = 0, hi = n_tensors - 1;
@@ -822,8 +831,11 @@ void k_fused_step(const DevTensor* __restrict__ tab,
     // clipping is a separate instantiation: the unclipped kernel carries no
     // trace of it (its live values are what limits occupancy)
     const float gs = CLIP ? *clip_of_table(tab) : 1.0f;
-    int t = first_tensor(chunk_begin, n_tensors, (int64_t)blockIdx.x * kWavesPerGroup + wave);
-    for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks;
+    // XCD-contiguous groups measured 1.5% faster for the ZIP-SR kernels and
+    // 0.6% slower for the others (GPT-2.7B set, same box)
+    const int64_t g = FLAT ? xcd_group() : (int64_t)blockIdx.x;
+    int t = first_tensor(chunk_begin, n_tensors, g * kWavesPerGroup + wave);
+    for (int64_t c = g * kWavesPerGroup + wave; c < total_chunks;
          c += (int64_t)gridDim.x * kWavesPerGroup) {
         while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
         const DevTensor T = tab[t];
