@@ -185,30 +185,40 @@ __device__ __forceinline__ float tree8(const float* v) {
 __device__ __forceinline__ float bperm(float v, int lane) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(lane << 2, __float_as_int(v)));
 }
-// ds_bpermute byte address of lane row + code, code = nibble k of `codes`,
-// rb4 = 4 * row (the row's first lane): the nibble is shifted straight into
-// place (two instructions).
-__device__ __forceinline__ int nibble_addr(uint32_t codes, int k, uint32_t rb4) {
-    const uint32_t c4 = k == 0 ? (codes << 2) : (codes >> (4 * k - 2));
-    return (int)((c4 & 0x3Cu) | rb4);
+// ds_bpermute byte addresses of the 8 nibbles of `codes` for lane row + code,
+// rb4x4 = 4 * row (the row's first lane) in every byte: byte j of `ev` is
+// 4 * nibble(2j) + 4 * row, of `od` 4 * nibble(2j + 1) + 4 * row (the two
+// fields share no bit).  ds_bpermute reads only bits 2..7 of an address
+// (checked on gfx950 over random upper bits), so element k takes its word
+// shifted right by 8 * (k / 2): two instructions per word, then one shift
+// per element.
+struct NibbleAddrs {
+    uint32_t ev, od;
+};
+__device__ __forceinline__ NibbleAddrs nibble_addrs(uint32_t codes, uint32_t rb4x4) {
+    return {((codes << 2) & 0x3C3C3C3Cu) | rb4x4, ((codes >> 2) & 0x3C3C3C3Cu) | rb4x4};
+}
+__device__ __forceinline__ int nibble_addr(const NibbleAddrs& a, int k) {
+    return (int)(((k & 1) ? a.od : a.ev) >> (8 * (k >> 1)));
 }
 __device__ __forceinline__ float bperm_addr(float v, int addr) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(addr, __float_as_int(v)));
 }
 
 // IEEE (correctly rounded) square root of x from the hardware one, which is
-// faithful: of s - 1ulp, s and s + 1ulp the signs of the exact residuals
-// x - t s (one FMA each) pick the right one (Tuckerman's rounding test).
-// Valid while the residuals cannot underflow, x >= 2^-96, and for x = 0.
+// faithful: the root lies on the side of s that the sign of the exact
+// residual x - s s shows (one FMA), and only the neighbour t of s on that
+// side can be nearer; the sign of the exact residual x - s t decides it
+// (Tuckerman's rounding test).  A zero (or NaN, x = inf) residual leans up,
+// where the test then keeps s.  Valid while the residuals cannot underflow:
+// x >= 2^-96 (through +inf) and x = 0, checked exhaustively on gfx950
+// against the IEEE square root.
 __device__ __forceinline__ float sqrt_rn_normal(float x) {
     const float s = __builtin_amdgcn_sqrtf(x);
-    const float sd = __uint_as_float(__float_as_uint(s) - 1u);
-    const float su = __uint_as_float(__float_as_uint(s) + 1u);
-    const float rd = __builtin_fmaf(-sd, s, x);
-    const float ru = __builtin_fmaf(-su, s, x);
-    float r = rd <= 0.0f ? sd : s;
-    r = ru > 0.0f ? su : r;
-    return r;
+    const bool up = !(__builtin_fmaf(-s, s, x) < 0.0f);
+    const float t = __uint_as_float(__float_as_uint(s) + (up ? 1u : 0xFFFFFFFFu));
+    const bool beyond = __builtin_fmaf(-s, t, x) > 0.0f;  // up: x > s t; down: x <= s t
+    return beyond == up ? t : s;
 }
 
 // 1/s of a block scale s >= 0 (0 for s = 0).  For s in [2^-126, 2^126) the
@@ -431,7 +441,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     constexpr bool V_SR = VRULE == Q4_RULE_STATE_SR || VRULE == Q4_RULE_UPDATE_SR;
     constexpr bool V_UPD = VRULE == Q4_RULE_UPDATE_SR || VRULE == Q4_RULE_UPDATE_RTN;
     const int sub = lane & 15, row_base = lane & 48;
-    const uint32_t rb4 = (uint32_t)row_base << 2;
+    const uint32_t rb4x4 = ((uint32_t)row_base << 2) * 0x01010101u;
     const int64_t n = T.numel;
     const int64_t blk = lc * kBlocksPerChunk + (lane >> 4);
     // the chunk's bases are wave-uniform (scalar registers); a lane adds a
@@ -531,15 +541,17 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     }
 
     // ---- AdamW on the unquantized moments
+    const NibbleAddrs ma = nibble_addrs(mc, rb4x4);
+    const NibbleAddrs va = nibble_addrs(vc, rb4x4);
     float m1[8], v1[8], sv[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const float gk = g[k];
-        const float m0 = bperm_addr(dm_own, nibble_addr(mc, k, rb4));
+        const float m0 = bperm_addr(dm_own, nibble_addr(ma, k));
         // each recurrence is one fused multiply-add onto the gradient term
         m1[k] = __builtin_fmaf(sc.beta1, m0, sc.omb1 * gk);
         if constexpr (packed_v) {
-            const float v0 = bperm_addr(dv_own, nibble_addr(vc, k, rb4));
+            const float v0 = bperm_addr(dv_own, nibble_addr(va, k));
             v1[k] = __builtin_fmaf(sc.beta2, v0, sc.omb2 * (gk * gk));
         } else {
             v1[k] = vf[k];
