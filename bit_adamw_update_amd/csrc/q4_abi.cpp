@@ -670,7 +670,7 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
                                   clip, stats_ready, st);
         if (e != hipSuccess) return hip_fail(e, "factored statistics launch");
     }
-    e = launch_fused_step(r.var, sc, d_tab, d_chunks, n, P.total_chunks, st);
+    e = launch_fused_step(r.var, sc, d_tab, d_chunks, n, P.total_chunks, P.n_mats > 0, st);
     if (e != hipSuccess) return hip_fail(e, "fused step launch");
     return ok();
 }

@@ -92,9 +92,11 @@ __host__ __device__ inline const float* clip_of_table(const DevTensor* tab) {
 // Kernel variants that exist (m codebook, v codebook, v rule).
 struct Variant { int mcb, vcb, vrule; };
 
+// has_matrices: the tensor list holds factored matrices (their row/column
+// gathers run best at 7 work-groups per CU, which the launch then enforces).
 hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevTensor* d_tab,
                              const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks,
-                             hipStream_t stream);
+                             bool has_matrices, hipStream_t stream);
 hipError_t launch_fp32_step(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
                             int n_tensors, int64_t total_chunks, hipStream_t stream);
 hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,

@@ -1509,7 +1509,8 @@ __global__ __launch_bounds__(256) void k_dequant(DevTensor T, float* __restrict_
 
 // Grid-stride grid sized from the kernel's occupancy and the number of
 // compute units, never more groups than there are chunk groups.
-template <class K> static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache) {
+template <class K>
+static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds = 0) {
     static std::atomic<int> cus{0};
     if (cus.load() == 0) {
         int dev = 0;
@@ -1519,7 +1520,7 @@ template <class K> static int step_grid(K kernel, int64_t total_chunks, std::ato
     }
     int per_cu = per_cu_cache.load();
     if (per_cu == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, dyn_lds) != hipSuccess || per_cu < 1)
             per_cu = 1;
         per_cu_cache.store(per_cu);
     }
@@ -1547,21 +1548,30 @@ bool variant_supported(const Variant& v) {
     return false;
 }
 
+// Reserved (unused) LDS that caps a 4-wave work-group of the step at 7 per
+// CU (160 KiB of LDS): with factored matrices the kernel that fits 8 ran the
+// Qwen3-0.6B set 3% slower than at 7 (same box).
+constexpr size_t kCap7Lds = 19456;
+
 hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevTensor* d_tab,
-                             const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks, hipStream_t stream) {
+                             const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks, bool has_matrices,
+                             hipStream_t stream) {
     if (total_chunks <= 0) return hipSuccess;
+    const int cap = has_matrices ? 1 : 0;
 #define Q4_LAUNCH(A, B, C)                                                                                   \
     if (v.mcb == A && v.vcb == B && v.vrule == C) {                                                          \
         if (sc.flags & SF_CLIP) {                                                                            \
-            static std::atomic<int> occ{0};                                                                  \
-            const int grid = step_grid(k_fused_step<A, B, C, true>, total_chunks, occ);                      \
-            k_fused_step<A, B, C, true><<<grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, \
-                                                                  sc);                                       \
-        } else {                                                                                             \
-            static std::atomic<int> occ{0};                                                                  \
-            const int grid = step_grid(k_fused_step<A, B, C, false>, total_chunks, occ);                     \
-            k_fused_step<A, B, C, false><<<grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors,          \
+            static std::atomic<int> occ[2];                                                                  \
+            const size_t dl = (cap && !flat_tables<B, C>()) ? kCap7Lds : 0;                                  \
+            const int grid = step_grid(k_fused_step<A, B, C, true>, total_chunks, occ[cap], dl);             \
+            k_fused_step<A, B, C, true><<<grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors,          \
                                                                    total_chunks, sc);                        \
+        } else {                                                                                             \
+            static std::atomic<int> occ[2];                                                                  \
+            const size_t dl = (cap && !flat_tables<B, C>()) ? kCap7Lds : 0;                                  \
+            const int grid = step_grid(k_fused_step<A, B, C, false>, total_chunks, occ[cap], dl);            \
+            k_fused_step<A, B, C, false><<<grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors,         \
+                                                                    total_chunks, sc);                       \
         }                                                                                                    \
         return hipGetLastError();                                                                            \
     }
