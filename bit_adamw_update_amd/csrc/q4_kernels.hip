@@ -221,20 +221,23 @@ __device__ __forceinline__ float sqrt_rn_normal(float x) {
     return beyond == up ? t : s;
 }
 
-// 1/s of a block scale s >= 0 (0 for s = 0).  For s in [2^-126, 2^126) the
-// hardware reciprocal refined by one FMA Newton step equals the IEEE
-// quotient (an exhaustive comparison over every float of that range found
-// no difference); a wave with a lane outside the range divides.
+// The inverse that normalizes a block, x = value * (1/s), for a block scale
+// s >= 0: 0 for a zero scale and for one below the smallest normal float
+// (whose reciprocal may overflow; 0 * inf would not be 0), so such blocks
+// store the code of zero.  For s in [2^-126, 2^126) the hardware reciprocal
+// refined by one FMA Newton step equals the IEEE quotient (an exhaustive
+// comparison over every float of that range found no difference); a wave
+// with a larger scale divides.
 __device__ __forceinline__ float inv_scale(float s) {
-    const bool fast = s >= 0x1p-126f && s < 0x1p126f;
+    const bool normal = s >= 0x1p-126f;
     float r;
-    if (__builtin_amdgcn_ballot_w64(!fast && s > 0.0f) == 0) {
+    if (__builtin_amdgcn_ballot_w64(s >= 0x1p126f) == 0) {
         const float y = __builtin_amdgcn_rcpf(s);
         r = __builtin_fmaf(__builtin_fmaf(-s, y, 1.0f), y, y);
     } else {
         r = 1.0f / s;
     }
-    return s > 0.0f ? r : 0.0f;
+    return normal ? r : 0.0f;
 }
 
 // ---------------------------------------------------------------------------

@@ -45,7 +45,7 @@ class TensorSpec:
 class Workload:
     name: str
     tensors: list
-    grad_kind: str            # "masked" | "logscale" | "microbatch4"
+    grad_kind: str            # "masked" | "logscale" | "microbatch4" | "edge"
     steps: int
     recipes: tuple
     seed: int = 0
@@ -89,6 +89,24 @@ class Workload:
             c.addcmul_(w, w)
         return z.div_(c.div_(3.0).sqrt_())
 
+    # magnitude classes of the "edge" kind, one per 128-block in turn
+    EDGE_SCALES = (1e-3, 1e-16, 1e-39, 0.0, 1e-3, 1e-25, 1e-20)
+
+    def _edge(self, shape, g, device) -> torch.Tensor:
+        """Blocks of normal, tiny (squares below 2^-96), BF16-subnormal,
+        signed-zero, mixed (exact zeros and values 10^6 times larger), and
+        vanishing (squares underflow to zero or to subnormals) gradients."""
+        x = self._student_t3(shape, g, device).reshape(-1)
+        cls = (torch.arange(x.numel(), device=device) // 128) % len(self.EDGE_SCALES)
+        y = x * torch.tensor(self.EDGE_SCALES, device=device, dtype=torch.float32)[cls]
+        y = torch.where(cls == 3, torch.where(x < 0, torch.tensor(-0.0, device=device),
+                                              torch.tensor(0.0, device=device)), y)
+        idx = torch.arange(x.numel(), device=device)
+        mixed = cls == 4
+        y = torch.where(mixed & (idx % 9 == 0), torch.zeros_like(y), y)
+        y = torch.where(mixed & (idx % 61 == 0), x * 1e3, y)
+        return y.to(torch.bfloat16).reshape(shape)
+
     def grads(self, step: int, device="cpu", consts=None) -> list:
         """BF16 gradients of `step` (1-based), one tensor per parameter."""
         if consts is None:
@@ -100,6 +118,8 @@ class Workload:
                 x = self._student_t3(t.shape, g, device)
                 scale = torch.where(c, torch.tensor(1e-9, device=device), torch.tensor(1e-3, device=device))
                 out.append(x.mul_(scale).to(torch.bfloat16))
+            elif self.grad_kind == "edge":
+                out.append(self._edge(t.shape, g, device))
             elif self.grad_kind == "logscale":
                 out.append(self._student_t3(t.shape, g, device).mul_(c).to(torch.bfloat16))
             else:  # four microbatches, accumulated in BF16 in order

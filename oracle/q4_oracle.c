@@ -330,6 +330,13 @@ static float or_pairwise(const float* x, int n) {
     return or_pairwise(x, h) + or_pairwise(x + h, n - h);
 }
 
+/* Inverse of a block scale for normalization, x = value * (1/s).  A zero
+ * block normalizes to x = 0 (reading of zero blocks); so does a block whose
+ * scale is below the smallest normal float (reading of subnormal scales:
+ * its reciprocal may overflow, and 0 * inf would not be 0).  The scale
+ * itself is stored as computed. */
+static float or_scale_inverse(float s) { return s >= 0x1p-126f ? 1.0f / s : 0.0f; }
+
 /* First moment of one block: absmax scale, normalization, then RTN or
  * state-space SR (the LM-head rule of [P] Table 2) over the signed map.
  * m1[0..n) are the unquantized values; writes n nibbles starting at
@@ -339,7 +346,7 @@ static float or_requant_m_levels(const or_levels* lvp, int rule, const float* m1
     const or_levels lv = *lvp;
     float s = 0.0f;
     for (int k = 0; k < n; ++k) { float a = fabsf(m1[k]); if (a > s) s = a; }
-    float inv = s > 0.0f ? 1.0f / s : 0.0f;
+    float inv = or_scale_inverse(s);
     for (int k = 0; k < n; ++k) {
         float x = m1[k] * inv;
         if (x > 1.0f) x = 1.0f;
@@ -360,7 +367,7 @@ static float or_requant_v_levels(const or_levels* lvp, int rule, int eden, const
     const or_levels lv = *lvp;
     float s = 0.0f;
     for (int k = 0; k < n; ++k) if (v1[k] > s) s = v1[k];
-    float inv = s > 0.0f ? 1.0f / s : 0.0f;
+    float inv = or_scale_inverse(s);
     float xx[OR_BLOCK], xq[OR_BLOCK];
     for (int k = 0; k < OR_BLOCK; ++k) { xx[k] = 0.0f; xq[k] = 0.0f; }
     for (int k = 0; k < n; ++k) {
@@ -722,7 +729,7 @@ int or_step8_window(const or_hparams* hp, const or_window* w) {
             if (a > sm) sm = a;
             if (v1[k] > sv) sv = v1[k];
         }
-        float im = sm > 0.0f ? 1.0f / sm : 0.0f, iv = sv > 0.0f ? 1.0f / sv : 0.0f;
+        float im = or_scale_inverse(sm), iv = or_scale_inverse(sv);
         for (int k = 0; k < n; ++k) {
             float xm = fminf(fmaxf(m1[k] * im, -1.0f), 1.0f);
             float xv = fminf(v1[k] * iv, 1.0f);

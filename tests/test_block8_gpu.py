@@ -106,6 +106,13 @@ def test_dequant_matches_oracle():
         assert np.array_equal(v.cpu().numpy().view(np.uint32), ov.view(np.uint32))
 
 
+def test_edge_magnitudes():
+    """Tiny, BF16-subnormal (block scales below 2^-126), signed-zero, mixed
+    and vanishing gradient blocks."""
+    _flush("block8 edge magnitudes")
+    run_windows(inputs.custom([(7 * 128 * 3 + 77,), (21, 140)], grad_kind="edge", seed=52), 6)
+
+
 def test_gpt_162m_sampled_20_steps():
     """The GPT-style 162M set (123.6M parameters as written), 20 steps,
     first/last blocks of every tensor and random interior windows."""

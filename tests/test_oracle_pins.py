@@ -698,3 +698,31 @@ def test_8bit_first_step_rounds_to_the_nearest_level_and_matches_fp32():
             best = lcode[np.argmin(d, axis=1)]     # argmin takes the first (lower) level on a tie
             assert np.array_equal(codes[b * 128: b * 128 + blk.size], best)
             assert np.all(np.abs(table[codes[b * 128: b * 128 + blk.size]] - x) <= np.diff(L).max() / 2 + 1e-7)
+
+
+def test_subnormal_block_scales_normalize_to_zero():
+    """Reading of subnormal scales: a block whose scale is below the smallest
+    normal float stores the code of zero in every slot (its reciprocal may
+    overflow, and 0 * inf is not 0) and keeps the scale as computed; the next
+    block, of normal values, is quantized as usual.  4-bit and 8-bit states.
+    (Here 1/s is still finite, so a plain x = m1 * (1/s) would spread the
+    block over many codes.)"""
+    import torch
+    g = torch.Generator().manual_seed(61)
+    x = torch.randn(256, generator=g)
+    grad = torch.cat([x[:128] * 2e-38, x[128:] * 1e-3]).to(torch.bfloat16).view(torch.uint16).numpy().copy()
+    hp = O.HParams(step=1)
+    tiny = np.float32(2.0 ** -126)
+    for recipe in (O.ZIP_SR, O.ZE_EDEN):
+        cfg = O.Config.of(recipe)
+        st = O.TensorState(cfg, (256,), 3)
+        st.step(hp, np.zeros(256, np.float32), grad)
+        c = O.unpack(st.m_codes, 256)
+        assert 0 < st.m_scales[0] < tiny and np.isfinite(np.float32(1) / st.m_scales[0])
+        assert np.all(c[:128] == O.zero_code(cfg.m_cb))
+        assert len(set(c[128:].tolist())) > 4
+    st8 = O.TensorState8((256,), 3)
+    st8.step(hp, np.zeros(256, np.float32), grad)
+    assert 0 < st8.m_scales[0] < tiny
+    assert np.all(st8.m_codes[:128] == 0)
+    assert len(set(st8.m_codes[128:].tolist())) > 4

@@ -194,6 +194,20 @@ def test_qwen3_factored_full_rc():
     rep.check()
 
 
+@pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden", "factored", "fp32"])
+def test_edge_magnitudes(recipe):
+    """Blocks whose v falls below 2^-96 (the square root's wave-level IEEE
+    fallback), BF16-subnormal blocks (block scales below 2^-126: the
+    reciprocal's division fallback), signed zeros (the negative half of the
+    flat bucket table), mixed zeros and large values, and squares that
+    underflow; every element, 6 steps."""
+    w = inputs.custom([(7 * 128 * 3 + 77,), (21, 140)], grad_kind="edge", seed=51)
+    _flush(f"edge magnitudes {recipe}")
+    rep = parity.run(w, recipe, 6)
+    rep.check()
+    assert rep.codes_differ == 0
+
+
 def test_tensor_beyond_2_32_elements():
     """One tensor of 2^32 + 1000 elements (17 GB of FP32 masters): 64-bit
     element indices, Philox counters past 2^32 / 4, a ragged last block."""
