@@ -228,6 +228,10 @@ def main():
     ap.add_argument("--recipe", default="zip_sr")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--step-before", action="store_true",
+                    help="time only the last microbatch's accumulation pass (with the statistics) and the step "
+                         "that reuses them, on this workload and recipe (a profiling aid; prints its own JSON line)")
+    ap.add_argument("--max-grad-norm", type=float, default=0.0, help="clipping for --step-before")
     ap.add_argument("--cpu-sample", type=int, default=160_000_000, help="elements in the oracle sample")
     args = ap.parse_args()
 
@@ -248,6 +252,12 @@ def main():
     wl = inputs.WORKLOADS[args.workload]()
     n = wl.numel
     log(f"{wl.name}: {n:,} params in {len(wl.tensors)} tensors, recipe {args.recipe}")
+    if args.step_before:
+        acc_ms, st_ms = time_step_before(wl, args.recipe, args.steps, args.warmup, max_grad_norm=args.max_grad_norm)
+        print(json.dumps({"workload": wl.name, "recipe": args.recipe, "params": n, "steps": args.steps,
+                          "accumulate_ms": acc_ms, "accumulate_gbs": 6 * n / (acc_ms * 1e-3) / 1e9,
+                          "step_ms": st_ms, "max_grad_norm": args.max_grad_norm}), flush=True)
+        return
     r = time_workload(wl, args.recipe, args.steps, args.warmup,
                       lm_head_phase=wl.lm_head_switch)
     ms_step = r["wall_s"] * 1e3 / args.steps
