@@ -1512,6 +1512,8 @@ __global__ __launch_bounds__(256) void k_dequant(DevTensor T, float* __restrict_
 
 // Grid-stride grid sized from the kernel's occupancy and the number of
 // compute units, never more groups than there are chunk groups.
+constexpr int64_t kMinChunksPerWave = 20;
+
 template <class K>
 static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds = 0) {
     static std::atomic<int> cus{0};
@@ -1529,8 +1531,13 @@ static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_ca
     }
     const int64_t groups = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
     // four times the resident groups: the queued groups balance the uneven
-    // finishing times of the first wave of groups (measured best on gfx950)
-    const int64_t cap = 4 * (int64_t)per_cu * cus.load();
+    // finishing times of the first wave of groups (measured best on gfx950
+    // for the large sets); but every wavefront should get some 20 chunks, or
+    // each group's table setup dominates (GPT-162M set: 0.45 ms at 4x, 0.40
+    // ms at 2x the resident groups)
+    const int64_t resident = (int64_t)per_cu * cus.load();
+    int64_t cap = total_chunks / (kWavesPerGroup * kMinChunksPerWave);
+    cap = cap < resident ? resident : (cap > 4 * resident ? 4 * resident : cap);
     return (int)(groups < cap ? (groups > 0 ? groups : 1) : cap);
 }
 
