@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -216,7 +217,19 @@ def cpu_baseline(workload, recipe: str, max_elems: int):
     names = ", ".join(f"{workload.tensors[i].name} {list(workload.tensors[i].shape)}" for i in picked)
     return {"value": n / dt / 1e9, "unit": "G params/s", "cores": 1, "kind": "oracle",
             "sample": f"one {recipe} step over {n:,} parameters ({names}) of {workload.name}, "
-                      f"single-threaded C oracle, {dt:.1f} s"}
+                      f"single-threaded C oracle, {dt:.1f} s",
+            "host_cpu": host_cpu_model(), "host_nproc": os.cpu_count(), "oracle_threads": 1}
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -291,7 +304,9 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": step_kernel(args.recipe), "alg_bytes_per_launch": ab,
-                     "alg_bytes_per_param": ab / n, "avg_launch_ms": avg_launch},
+                     "alg_bytes_per_param": ab / n, "avg_launch_ms": avg_launch,
+                     "launch_ms": {"mean": avg_launch, "median": statistics.median(launch_ms),
+                                   "min": min(launch_ms), "max": max(launch_ms)}},
     }
     try:
         result["copy_ceiling_gbs"] = copy_ceiling_gbs()
