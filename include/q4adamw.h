@@ -228,7 +228,10 @@ q4_status q4adamw_init_state(const q4_config* cfg, const q4_tensor* t, int32_t n
  * and C take their own EMA of this step's row/column means of g^2), update
  * the weight p <- p decay - step_size m1 / (sqrt(v1) rsbc2 + eps) from the
  * unquantized m1, v1, then requantize: absmax scales, the m rule (RTN, or
- * SR for the LM head in the final phase), the v rule, EDEN.
+ * SR for the LM head in the final phase), the v rule, EDEN.  A block whose
+ * scale is 0 or below the smallest normal float (2^-126) stores the code of
+ * zero in every slot and keeps its scale as computed (the reciprocal of a
+ * subnormal scale may overflow).
  * Clipping (hp->max_grad_norm > 0): s = min(1, max_grad_norm / (norm +
  * 1e-6)) in binary64, rounded to FP32, from the global norm of the
  * gradients (the statistics in ws with Q4_HP_GRAD_STATS, else gathered
