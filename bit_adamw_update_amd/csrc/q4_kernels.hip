@@ -1515,7 +1515,8 @@ __global__ __launch_bounds__(256) void k_dequant(DevTensor T, float* __restrict_
 constexpr int64_t kMinChunksPerWave = 20;
 
 template <class K>
-static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds = 0) {
+static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds = 0,
+                     int64_t max_mult = 4) {
     static std::atomic<int> cus{0};
     if (cus.load() == 0) {
         int dev = 0;
@@ -1530,14 +1531,14 @@ static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_ca
         per_cu_cache.store(per_cu);
     }
     const int64_t groups = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
-    // four times the resident groups: the queued groups balance the uneven
-    // finishing times of the first wave of groups (measured best on gfx950
-    // for the large sets); but every wavefront should get some 20 chunks, or
-    // each group's table setup dominates (GPT-162M set: 0.45 ms at 4x, 0.40
-    // ms at 2x the resident groups)
+    // max_mult (4) times the resident groups: the queued groups balance the
+    // uneven finishing times of the first wave of groups (measured best on
+    // gfx950 for the large sets); but every wavefront should get some 20
+    // chunks, or each group's table setup dominates (GPT-162M set: 0.45 ms at
+    // 4x, 0.40 ms at 2x the resident groups)
     const int64_t resident = (int64_t)per_cu * cus.load();
     int64_t cap = total_chunks / (kWavesPerGroup * kMinChunksPerWave);
-    cap = cap < resident ? resident : (cap > 4 * resident ? 4 * resident : cap);
+    cap = cap < resident ? resident : (cap > max_mult * resident ? max_mult * resident : cap);
     return (int)(groups < cap ? (groups > 0 ? groups : 1) : cap);
 }
 
@@ -1560,7 +1561,8 @@ bool variant_supported(const Variant& v) {
 
 // Reserved (unused) LDS that caps a 4-wave work-group of the step at 7 per
 // CU (160 KiB of LDS): with factored matrices the kernel that fits 8 ran the
-// Qwen3-0.6B set 3% slower than at 7 (same box).
+// Qwen3-0.6B set 3% slower than at 7 (same box).  Those launches also take
+// at most 2x the resident groups (4x: 1.83 ms, 2x: 1.76 ms, 8x: 2.05 ms).
 constexpr size_t kCap7Lds = 19456;
 
 hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevTensor* d_tab,
@@ -1573,13 +1575,13 @@ hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevT
         if (sc.flags & SF_CLIP) {                                                                            \
             static std::atomic<int> occ[2];                                                                  \
             const size_t dl = (cap && !flat_tables<B, C>()) ? kCap7Lds : 0;                                  \
-            const int grid = step_grid(k_fused_step<A, B, C, true>, total_chunks, occ[cap], dl);             \
+            const int grid = step_grid(k_fused_step<A, B, C, true>, total_chunks, occ[cap], dl, cap ? 2 : 4);             \
             k_fused_step<A, B, C, true><<<grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors,          \
                                                                    total_chunks, sc);                        \
         } else {                                                                                             \
             static std::atomic<int> occ[2];                                                                  \
             const size_t dl = (cap && !flat_tables<B, C>()) ? kCap7Lds : 0;                                  \
-            const int grid = step_grid(k_fused_step<A, B, C, false>, total_chunks, occ[cap], dl);            \
+            const int grid = step_grid(k_fused_step<A, B, C, false>, total_chunks, occ[cap], dl, cap ? 2 : 4);            \
             k_fused_step<A, B, C, false><<<grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors,         \
                                                                     total_chunks, sc);                       \
         }                                                                                                    \
