@@ -287,7 +287,7 @@ void plan_layout(const Resolved& r, const q4_tensor* t, int32_t n, Plan& P, uint
             m.n_rgroups = (m.rows + kGroup - 1) / kGroup;
             m.rgroup_begin = P.total_rgroups;
             P.total_rgroups += m.n_rgroups;
-            m.n_cgroups = (m.cols + kGroup - 1) / kGroup;
+            m.n_cgroups = (m.cols + kColGroup - 1) / kColGroup;
             m.cgroup_begin = P.total_cgroups;
             P.total_cgroups += m.n_cgroups;
             // offsets (in doubles) filled into pointers below

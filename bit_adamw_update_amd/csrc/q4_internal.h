@@ -15,7 +15,8 @@ constexpr int kChunkElems = kBlock * kBlocksPerChunk;
 constexpr int kWavesPerGroup = 4;      // 256-thread work-groups
 constexpr int kBandRows = 256;         // rows per band of the row/column partial kernel
 constexpr int kTileCols = 512;         // columns per tile (64 lanes x 8 BF16)
-constexpr int kGroup = 256;            // rows (columns) per finalize work-group
+constexpr int kGroup = 256;            // rows per finalize work-group
+constexpr int kColGroup = 64;          // columns per finalize work-group (4 band slices of 64 lanes)
 constexpr int kAccGroups = 2048;       // work-groups of the chunk-order accumulation pass (at most)
 
 // Gradient pass modes: read the gradient for its statistics only, copy the

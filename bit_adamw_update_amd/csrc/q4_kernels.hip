@@ -1422,22 +1422,31 @@ __global__ __launch_bounds__(256) void k_rowcol_finalize(const DevMatrix* __rest
         const double s = group_sum_d(mine, lds);
         if (threadIdx.x == 0) M.part_mean[lg] = s;
     } else {
+        // kColGroup columns, wave w summing bands w, w + 4, ... of each (a
+        // wave reads 64 consecutive columns of a band); eight interleaved
+        // accumulators per lane keep eight loads in flight; the lane's
+        // accumulators and then the four waves combine in a fixed tree
         const int64_t cg = g - total_rgroups;
         const int mi = find_matrix(mats, n_mats, cg, 2);
         const DevMatrix M = mats[mi];
-        const int64_t cidx = (cg - M.cgroup_begin) * kGroup + threadIdx.x;
+        const int lane = threadIdx.x & 63, slice = threadIdx.x >> 6;
+        const int64_t cidx = (cg - M.cgroup_begin) * kColGroup + lane;
+        double cs = 0.0;
         if (cidx < M.cols) {
-            // eight interleaved accumulators (band b into a[b mod 8]) keep
-            // eight loads in flight; combined in a fixed tree
             double a[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-            int64_t b = 0;
-            for (; b + 8 <= M.n_bands; b += 8) {
+            int64_t b = slice;
+            for (; b + 28 < M.n_bands; b += 32) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j) a[j] += M.part_col[(b + j) * M.cols + cidx];
+                for (int j = 0; j < 8; ++j) a[j] += M.part_col[(b + 4 * j) * M.cols + cidx];
             }
-            for (int j = 0; b < M.n_bands; ++b, ++j) a[j] += M.part_col[b * M.cols + cidx];
-            const double cs = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
-            M.C[cidx] = beta2 * M.C[cidx] + omb2 * ((float)(cs * s2) / (float)M.rows);
+            for (int j = 0; b < M.n_bands; b += 4, ++j) a[j] += M.part_col[b * M.cols + cidx];
+            cs = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+        }
+        lds[threadIdx.x] = cs;
+        __syncthreads();
+        if (slice == 0 && cidx < M.cols) {
+            const double t = (lds[lane] + lds[64 + lane]) + (lds[128 + lane] + lds[192 + lane]);
+            M.C[cidx] = beta2 * M.C[cidx] + omb2 * ((float)(t * s2) / (float)M.rows);
         }
     }
 }
