@@ -208,6 +208,17 @@ def test_edge_magnitudes(recipe):
     assert rep.codes_differ == 0
 
 
+def test_edge_magnitudes_lm_head_phase():
+    """The edge-magnitude blocks on a tensor flagged as the LM head, with the
+    final-phase switch: its m takes state-space SR (Philox stream 0) on the
+    last of 10 steps."""
+    w = inputs.custom([(7 * 128 * 3 + 77,), (21, 140)], grad_kind="edge", seed=53, flags=[inputs.TF_LM_HEAD, 0])
+    _flush("edge magnitudes zip_sr + LM-head phase")
+    rep = parity.run(w, "zip_sr", 10, lm_head_phase=True)
+    rep.check()
+    assert rep.codes_differ == 0
+
+
 def test_tensor_beyond_2_32_elements():
     """One tensor of 2^32 + 1000 elements (17 GB of FP32 masters): 64-bit
     element indices, Philox counters past 2^32 / 4, a ragged last block."""
