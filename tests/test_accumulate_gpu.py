@@ -150,3 +150,147 @@ def test_statistics_inside_the_step_equal_the_accumulated_ones(recipe):
         for f in ("m_codes", "m_scales", "v_codes", "v_scales", "v_row", "v_col"):
             if getattr(a, f) is not None:
                 assert torch.equal(getattr(a, f), getattr(b, f)), f
+
+
+def test_gpt_2_7b_accumulation_and_clipped_step_sampled():
+    """The GPT-style 2.7B set in the launch configuration the benchmark times
+    for the step before: one accumulation pass with the statistics, then a
+    clipped ZIP-SR step that reuses them.  Accumulated gradients on sampled
+    windows bit for bit; the norm against a float64 sum of every accumulated
+    gradient (an independent reduction, 1e-12); the clip factor bit for bit;
+    the step's codes, scales and weights on the windows."""
+    w = inputs.gpt_2_7b()
+    dev = torch.device("cuda")
+    st = q4.Q4State("zip_sr", w.tensors, dev)
+    params = [p.reshape(-1) for p in w.init_params(dev)]
+    consts = w._tensor_consts(dev)
+    grads = [g.reshape(-1).contiguous() for g in w.grads(1, dev, consts)]
+    offsets, total = st.flat_offsets()
+    micro = torch.zeros(total, dtype=torch.bfloat16, device=dev)
+    for i, g in enumerate(w.grads(2, dev, consts)):
+        micro[offsets[i]: offsets[i] + g.numel()].copy_(g.reshape(-1))
+    del consts
+    wins = parity.sample_windows(w, n_random=32, seed=8)
+    ocfg = parity.oracle_config("zip_sr")
+    host = []
+    for i, b0, b1 in wins:
+        t = w.tensors[i]
+        lo, hi = 128 * b0, min(128 * b1, t.numel)
+        n = hi - lo
+        zm, zv = O.zero_code(ocfg.m_cb), O.zero_code(ocfg.v_cb)
+        win = dict(i=i, b0=b0, b1=b1, lo=lo, hi=hi, param=params[i][lo:hi].cpu().numpy().copy(),
+                   g0=grads[i][lo:hi].view(torch.uint16).cpu().numpy().copy(),
+                   mic=micro[offsets[i] + lo: offsets[i] + hi].view(torch.uint16).cpu().numpy().copy(),
+                   m_codes=np.full((n + 1) // 2, zm | (zm << 4), np.uint8), m_scales=np.zeros(b1 - b0, np.float32),
+                   v_codes=np.full((n + 1) // 2, zv | (zv << 4), np.uint8), v_scales=np.zeros(b1 - b0, np.float32))
+        if n % 2:
+            win["m_codes"][-1], win["v_codes"][-1] = zm, zv
+        host.append(win)
+    _flush("gpt-2.7b accumulate + clipped zip_sr step")
+    st.accumulate(params, grads, micro, first=False, last=True)
+    norm = st.grad_norm()
+    ref_sq = sum(float((g.double() ** 2).sum()) for g in grads)
+    assert abs(norm - np.sqrt(ref_sq)) <= 1e-12 * np.sqrt(ref_sq)
+    for h in host:
+        acc = h["g0"].copy()
+        O.accumulate_bf16(acc, h["mic"], first=False)
+        got = grads[h["i"]][h["lo"]:h["hi"]].view(torch.uint16).cpu().numpy()
+        assert np.array_equal(got, acc), f"tensor {h['i']} accumulated gradients"
+        h["acc"] = acc
+    max_norm = 0.5 * norm
+    st.step(params, grads, 1, grad_stats=True, max_grad_norm=max_norm, **w.hp)
+    c = O.clip_factor(ref_sq, max_norm)
+    gpu_c = float(st.ws[8:12].view(torch.float32).cpu()[0])
+    assert np.float32(gpu_c).view(np.uint32) == np.float32(c).view(np.uint32), (gpu_c, c)
+    hp = O.HParams(step=1, grad_scale=c, **w.hp)
+    torch.cuda.synchronize()
+    for h in host:
+        t = w.tensors[h["i"]]
+        O.step_window(ocfg, hp, tensor_id=t.tensor_id, flags=t.flags, numel=t.numel, base=h["lo"], param=h["param"],
+                      grad=h["acc"], m_codes=h["m_codes"], m_scales=h["m_scales"], v_codes=h["v_codes"],
+                      v_scales=h["v_scales"])
+        b = st.bufs[h["i"]]
+        cl, ch = h["lo"] // 2, (h["hi"] + 1) // 2
+        for mine, ref in ((b.m_codes, h["m_codes"]), (b.v_codes, h["v_codes"])):
+            assert np.array_equal(parity.unpack(mine[cl:ch].cpu().numpy())[:h["hi"] - h["lo"]],
+                                  parity.unpack(ref)[:h["hi"] - h["lo"]]), f"tensor {h['i']} codes"
+        for mine, ref in ((b.m_scales, h["m_scales"]), (b.v_scales, h["v_scales"])):
+            assert np.array_equal(mine[h["b0"]:h["b1"]].cpu().numpy().view(np.uint32), ref.view(np.uint32))
+        p = params[h["i"]][h["lo"]:h["hi"]].cpu().numpy()
+        ref = h["param"]
+        scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
+        assert (np.abs(p - ref) / scale).max() <= parity.W_TOL, f"tensor {h['i']} weights"
+
+
+def test_qwen3_factored_step_from_accumulated_statistics():
+    """The Qwen3-0.6B-shaped factored set in the benchmark's launch
+    configuration: one accumulation pass leaves the row/column partials, and
+    the step that reuses them (no second gradient read) gives every matrix's
+    R and C within 1e-6 of the oracle's full recomputation from the
+    accumulated gradients; m codes, scales and weights on sampled windows."""
+    w = inputs.qwen3_0_6b_factored()
+    dev = torch.device("cuda")
+    st = q4.Q4State("factored", w.tensors, dev)
+    params = [p.reshape(-1) for p in w.init_params(dev)]
+    consts = w._tensor_consts(dev)
+    grads = [g.reshape(-1).contiguous() for g in w.grads(1, dev, consts)]
+    offsets, total = st.flat_offsets()
+    micro = torch.zeros(total, dtype=torch.bfloat16, device=dev)
+    for i, g in enumerate(w.grads(2, dev, consts)):
+        micro[offsets[i]: offsets[i] + g.numel()].copy_(g.reshape(-1))
+    del consts
+    wins = parity.sample_windows(w, n_random=24, seed=9)
+    ocfg = parity.oracle_config("factored")
+    p0 = {i: params[i].cpu().numpy().copy() for i in {i for i, _, _ in wins}}
+    _flush("qwen3-0.6b factored step from accumulated statistics")
+    st.accumulate(params, grads, micro, first=False, last=True)
+    st.step(params, grads, 1, grad_stats=True, **w.hp)
+    torch.cuda.synchronize()
+    hp = O.HParams(step=1, **w.hp)
+    fact = {}
+    max_rc = 0.0
+    for i, t in enumerate(w.tensors):
+        if len(t.shape) < 2:
+            continue
+        g = grads[i].view(torch.uint16).cpu().numpy()
+        rows, cols = t.shape[0], t.numel // t.shape[0]
+        R, Cc = np.zeros(rows, np.float32), np.zeros(cols, np.float32)
+        inv = O.factored_update(hp, rows, cols, g, R, Cc)
+        fact[i] = (R, Cc, inv)
+        b = st.bufs[i]
+        for mine, ref in ((b.v_row, R), (b.v_col, Cc)):
+            x = mine.cpu().numpy().astype(np.float64)
+            r = ref.astype(np.float64)
+            max_rc = max(max_rc, float((np.abs(x - r) / np.maximum(np.abs(r), 1e-30)).max()))
+    assert max_rc <= parity.RC_TOL, max_rc
+    for i, b0, b1 in wins:
+        t = w.tensors[i]
+        lo, hi = 128 * b0, min(128 * b1, t.numel)
+        n = hi - lo
+        zm = O.zero_code(ocfg.m_cb)
+        mc = np.full((n + 1) // 2, zm | (zm << 4), np.uint8)
+        if n % 2:
+            mc[-1] = zm
+        ms = np.zeros(b1 - b0, np.float32)
+        kw = dict(tensor_id=t.tensor_id, flags=t.flags, numel=t.numel, base=lo, param=p0[i][lo:hi].copy(),
+                  grad=grads[i][lo:hi].view(torch.uint16).cpu().numpy().copy(), m_codes=mc, m_scales=ms)
+        if i in fact:
+            R, Cc, inv = fact[i]
+            kw.update(cols=t.numel // t.shape[0], R=R, Cc=Cc, inv_meanR=inv)
+        else:
+            zv = O.zero_code(ocfg.v_cb)
+            vc = np.full((n + 1) // 2, zv | (zv << 4), np.uint8)
+            if n % 2:
+                vc[-1] = zv
+            kw.update(v_codes=vc, v_scales=np.zeros(b1 - b0, np.float32))
+        O.step_window(ocfg, hp, **kw)
+        b = st.bufs[i]
+        cl, ch = lo // 2, (hi + 1) // 2
+        assert np.array_equal(parity.unpack(b.m_codes[cl:ch].cpu().numpy())[:n], parity.unpack(mc)[:n]), f"tensor {i}"
+        assert np.array_equal(b.m_scales[b0:b1].cpu().numpy().view(np.uint32), ms.view(np.uint32))
+        if i not in fact:
+            assert np.array_equal(parity.unpack(b.v_codes[cl:ch].cpu().numpy())[:n], parity.unpack(kw["v_codes"])[:n])
+        p = params[i][lo:hi].cpu().numpy()
+        ref = kw["param"]
+        scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
+        assert (np.abs(p - ref) / scale).max() <= parity.W_TOL, f"tensor {i} weights"
