@@ -28,7 +28,6 @@
 // out: the two moment recurrences, the denominator and the weight update.
 
 #include <atomic>
-#include <utility>
 
 #include "q4_internal.h"
 #include "../../include/q4adamw.h"
@@ -60,7 +59,6 @@ template <int CB> struct Book {
     static constexpr float level(int k) { return bits2f(CbBits<CB>::b[code_of(k)]); }
     // FP32 midpoint of adjacent levels; an exact midpoint rounds down.
     static constexpr float mid(int k) { return (level(k) + level(k + 1)) * 0.5f; }
-    template <int J> static constexpr float midc() { constexpr float m = mid(J); return m; }
 };
 
 static constexpr bool sorted_ok(int cb) {
@@ -99,16 +97,6 @@ void codebook_table(int cb, float* out) {
         return;
     }
     for (int i = 0; i < 16; ++i) out[i] = bits2f(host[cb][i]);
-}
-
-// Round-to-nearest sorted index: the number of midpoints strictly below x,
-// as a sum of compares against compile-time constants.
-template <int CB, int... J>
-__device__ __forceinline__ int rtn_count(float x, std::integer_sequence<int, J...>) {
-    return (0 + ... + (x > Book<CB>::template midc<J>() ? 1 : 0));
-}
-template <int CB> __device__ __forceinline__ int rtn_index(float x) {
-    return rtn_count<CB>(x, std::make_integer_sequence<int, Book<CB>::N - 1>{});
 }
 
 // ---------------------------------------------------------------------------
