@@ -63,7 +63,7 @@ def test_lm_head_switch_final_phase():
     assert rep.codes_differ == 0
 
 
-@pytest.mark.parametrize("variant", [
+VARIANTS = [
     (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 0),
     (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_STATE_SR, 0),
     (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_RTN, 0),
@@ -72,15 +72,46 @@ def test_lm_head_switch_final_phase():
     (q4.CB_SDYN4, q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 1),
     (q4.CB_SDYN4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_SR, 0),
     (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_SR, q4.RULE_UPDATE_SR, 0),
-])
+]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
 def test_rule_and_codebook_variants(variant):
     """The component grid of the paper's Tables 1, 3 and 8 on the same kernel."""
-    cfg = q4.q4adamw_default_config(q4.RECIPE_CUSTOM)
-    cfg.m_codebook, cfg.v_codebook, cfg.m_rule, cfg.v_rule, cfg.eden = variant
+    cfg = _variant_cfg(variant)
     w = inputs.custom([(3000,), (40, 300)], grad_kind="masked", seed=24)
     rep = parity.run(w, "custom", 6, cfg=cfg)
     rep.check()
     assert rep.codes_differ == 0
+
+
+def _variant_cfg(variant):
+    cfg = q4.q4adamw_default_config(q4.RECIPE_CUSTOM)
+    cfg.m_codebook, cfg.v_codebook, cfg.m_rule, cfg.v_rule, cfg.eden = variant
+    return cfg
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_rule_and_codebook_variants_edge_magnitudes(variant):
+    """The grid on the edge-magnitude blocks (subnormal scales, v below
+    2^-96, signed zeros, underflowing squares), every element, 6 steps."""
+    w = inputs.custom([(7 * 128 * 3 + 77,), (21, 140)], grad_kind="edge", seed=54)
+    _flush(f"edge magnitudes variant {variant}")
+    rep = parity.run(w, "custom", 6, cfg=_variant_cfg(variant))
+    rep.check()
+    assert rep.codes_differ == 0
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_rule_and_codebook_variants_gpt_162m_sampled(variant):
+    """The grid on the GPT-style 162M set in the benchmark's launch
+    configuration, 5 steps, on windows."""
+    w = inputs.gpt_162m()
+    wins = parity.sample_windows(w, n_random=16, seed=11)
+    _flush(f"gpt-162m variant {variant}")
+    rep = parity.run(w, "custom", 5, cfg=_variant_cfg(variant), windows=wins, grads_on="cuda",
+                     check_every_step=False)
+    rep.check()
 
 
 def test_determinism_and_resume():
