@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "G params updated/sec for fused 4-bit AdamW step; HBM GB/s vs 8 TB/s peak"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = os.path.join(ROOT, "bit_adamw_update_amd", "csrc", "q4_kernels.hip")
+KERNEL_SRC = [os.path.join(ROOT, "bit_adamw_update_amd", "csrc", f) for f in ("q4_kernels.hip", "q4_exact.h")]
 
 
 def log(msg):
@@ -58,8 +58,12 @@ def alg_bytes(workload, recipe: str) -> int:
 
 
 def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the device source of the step kernels."""
+    h = hashlib.sha256()
+    for p in KERNEL_SRC:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def step_kernel(recipe: str) -> str:

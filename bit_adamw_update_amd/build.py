@@ -1,4 +1,6 @@
-"""Build the HIP library (libq4adamw.so) for gfx950, in-tree.
+"""Build the HIP library (libq4adamw.so) for gfx950, in-tree, and beside it
+the self-test library of its exact primitives (libq4selftest.so, loaded only
+by the tests).
 
 hipcc flags: -ffp-contract=off (no FMA contraction, so every FP32 operation
 rounds where it is written); HIP's default IEEE division and square root;
@@ -16,8 +18,11 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(BUILD_DIR, "libq4adamw.so")
 SOURCES = [os.path.join(CSRC, "q4_kernels.hip"), os.path.join(CSRC, "q4_abi.cpp")]
-DEPS = SOURCES + [os.path.join(CSRC, "q4_internal.h"), os.path.join(CSRC, "q4_codebooks.inc"),
-                  os.path.join(ROOT, "include", "q4adamw.h")]
+DEPS = SOURCES + [os.path.join(CSRC, "q4_internal.h"), os.path.join(CSRC, "q4_exact.h"),
+                  os.path.join(CSRC, "q4_codebooks.inc"), os.path.join(ROOT, "include", "q4adamw.h")]
+SELFTEST_PATH = os.path.join(BUILD_DIR, "libq4selftest.so")
+SELFTEST_SOURCES = [os.path.join(CSRC, "q4_selftest.hip")]
+SELFTEST_DEPS = SELFTEST_SOURCES + [os.path.join(CSRC, "q4_exact.h")]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
@@ -34,19 +39,25 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the GPU library cannot be built")
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
+def _build_one(path: str, sources: list, deps: list, force: bool, verbose: bool) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    if not force and os.path.exists(LIB_PATH):
-        t = os.path.getmtime(LIB_PATH)
-        if all(os.path.getmtime(d) <= t for d in DEPS):
-            return LIB_PATH
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *SOURCES]
+    if not force and os.path.exists(path):
+        t = os.path.getmtime(path)
+        if all(os.path.getmtime(d) <= t for d in deps):
+            return path
+    tmp = path + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, path)
+    return path
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Builds both libraries; returns the optimizer library's path."""
+    _build_one(SELFTEST_PATH, SELFTEST_SOURCES, SELFTEST_DEPS, force, verbose)
+    return _build_one(LIB_PATH, SOURCES, DEPS, force, verbose)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,94 @@
+"""Exhaustive checks of the step kernels' exact primitives (q4_exact.h):
+
+  * sqrt_rn_normal, the hardware square root plus a one-sided Tuckerman
+    correction, is the correctly rounded square root at x = 0 and for every
+    x in [2^-96, +inf];
+  * inv_scale, the hardware reciprocal plus one Newton step, returns the
+    correctly rounded 1/s for every s >= 2^-126 (through +inf) and +0 below
+    that, for zero and for NaN;
+  * the nibble-addressed ds_bpermute decode fetches lane row + code for
+    every nibble, and ds_bpermute ignores address bits 0-1 and 8-31.
+
+The library checks each result against the definition of correct rounding
+(the input must lie strictly between the squares, or reciprocals, of the
+result's two midpoints, compared exactly in binary64).  The bare hardware
+operations must fail the same check, which shows that it can fail.
+"""
+import ctypes
+import os
+
+import pytest
+
+from bit_adamw_update_amd import build
+
+SQRT, INV_SCALE = 0, 1
+FAST, BARE = 0, 1
+F32_INF = 0x7F800000
+
+
+def _lib():
+    if not os.path.exists(build.SELFTEST_PATH):
+        pytest.fail(f"{build.SELFTEST_PATH} is not built")
+    lib = ctypes.CDLL(build.SELFTEST_PATH)
+    lib.q4st_sweep.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
+                               ctypes.POINTER(ctypes.c_ulonglong), ctypes.POINTER(ctypes.c_uint32)]
+    lib.q4st_sweep.restype = ctypes.c_int
+    lib.q4st_nibble_decode.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
+                                       ctypes.POINTER(ctypes.c_ulonglong)]
+    lib.q4st_nibble_decode.restype = ctypes.c_int
+    return lib
+
+
+def _sweep(lib, what, form, lo, hi):
+    n, first = ctypes.c_ulonglong(0), ctypes.c_uint32(0)
+    rc = lib.q4st_sweep(what, form, lo, hi, ctypes.byref(n), ctypes.byref(first))
+    assert rc == 0, f"q4st_sweep returned {rc}"
+    print(f"sweep what={what} form={form} [{lo:#010x}, {hi:#010x}): {n.value} mismatches, "
+          f"first {first.value:#010x}", flush=True)
+    return n.value, first.value
+
+
+def test_selftest_library_exports_and_validates():
+    lib = _lib()
+    out = os.popen(f"nm -D --defined-only {build.SELFTEST_PATH}").read()
+    for sym in ("q4st_sweep", "q4st_nibble_decode"):
+        assert f" T {sym}" in out
+    n, first = ctypes.c_ulonglong(0), ctypes.c_uint32(0)
+    # rejected before any device call
+    assert lib.q4st_sweep(2, 0, 0, 1, ctypes.byref(n), ctypes.byref(first)) == -1
+    assert lib.q4st_sweep(0, 2, 0, 1, ctypes.byref(n), ctypes.byref(first)) == -1
+    assert lib.q4st_sweep(0, 0, 5, 4, ctypes.byref(n), ctypes.byref(first)) == -1
+    assert lib.q4st_sweep(0, 0, 0, (1 << 32) + 1, ctypes.byref(n), ctypes.byref(first)) == -1
+    assert lib.q4st_nibble_decode(1, 6, 0, ctypes.byref(n)) == -1
+    assert lib.q4st_nibble_decode(1, 0, 0, ctypes.byref(n)) == -1
+
+
+@pytest.mark.gpu
+def test_sqrt_rn_normal_exhaustive():
+    lib = _lib()
+    assert _sweep(lib, SQRT, FAST, 0, 1) == (0, 0xFFFFFFFF)                  # x = +0
+    assert _sweep(lib, SQRT, FAST, 0x0F800000, F32_INF + 1) == (0, 0xFFFFFFFF)  # [2^-96, +inf]
+    # the hardware square root alone is not correctly rounded
+    assert _sweep(lib, SQRT, BARE, 0x3F800000, 0x40800000)[0] > 0             # [1, 4)
+    # below 2^-96 the residuals underflow and the correction fails, which is
+    # why a wave with such an input takes the IEEE square root instead
+    assert _sweep(lib, SQRT, FAST, 1, 0x0F800000)[0] > 0
+
+
+@pytest.mark.gpu
+def test_inv_scale_exhaustive():
+    lib = _lib()
+    # every s >= +0: zero, subnormal, normal, +inf and NaN bit patterns
+    assert _sweep(lib, INV_SCALE, FAST, 0, 0x80000000) == (0, 0xFFFFFFFF)
+    # the hardware reciprocal alone is not correctly rounded
+    assert _sweep(lib, INV_SCALE, BARE, 0x3F800000, 0x40000000)[0] > 0        # [1, 2)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("form", [FAST, BARE])
+def test_nibble_decode(form):
+    lib = _lib()
+    for seed in (1, 2, 3):
+        n = ctypes.c_ulonglong(0)
+        assert lib.q4st_nibble_decode(seed, 1 << 16, form, ctypes.byref(n)) == 0
+        assert n.value == 0, f"seed {seed}: {n.value} elements fetched the wrong lane"
