@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "G params updated/sec for fused 4-bit AdamW step; HBM GB/s vs 8 TB/s peak"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = [os.path.join(ROOT, "bit_adamw_update_amd", "csrc", f) for f in ("q4_kernels.hip", "q4_exact.h")]
+KERNEL_SRC = [os.path.join(ROOT, "bit_adamw_update_amd", "csrc", f) for f in ("q4_kernels.hip", "q4_exact.h", "q4_quant.h")]
 
 
 def log(msg):

@@ -19,10 +19,12 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(BUILD_DIR, "libq4adamw.so")
 SOURCES = [os.path.join(CSRC, "q4_kernels.hip"), os.path.join(CSRC, "q4_abi.cpp")]
 DEPS = SOURCES + [os.path.join(CSRC, "q4_internal.h"), os.path.join(CSRC, "q4_exact.h"),
-                  os.path.join(CSRC, "q4_codebooks.inc"), os.path.join(ROOT, "include", "q4adamw.h")]
+                  os.path.join(CSRC, "q4_quant.h"), os.path.join(CSRC, "q4_codebooks.inc"),
+                  os.path.join(ROOT, "include", "q4adamw.h")]
 SELFTEST_PATH = os.path.join(BUILD_DIR, "libq4selftest.so")
 SELFTEST_SOURCES = [os.path.join(CSRC, "q4_selftest.hip")]
-SELFTEST_DEPS = SELFTEST_SOURCES + [os.path.join(CSRC, "q4_exact.h")]
+SELFTEST_DEPS = SELFTEST_SOURCES + [os.path.join(CSRC, "q4_exact.h"), os.path.join(CSRC, "q4_quant.h"),
+                                    os.path.join(CSRC, "q4_codebooks.inc")]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",

@@ -1,0 +1,336 @@
+// q4_quant.h -- codebooks and the round-to-nearest machinery of the step
+// kernels: the compile-time bucket tables that turn "the number of FP32
+// midpoints strictly below x" into one table read and one compare, their
+// flat layout for the ZIP-SR kernels, and the 8-bit tables.  Included by
+// q4_kernels.hip and by the self-test library (q4_selftest.hip), which
+// compares every lookup here with a plain count over every FP32 input in
+// [-1, 1] (signed maps) or [0, 1] (unsigned maps).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/q4adamw.h"
+#include "q4_codebooks.inc"
+
+namespace q4 {
+
+// ---------------------------------------------------------------------------
+// Codebooks
+// ---------------------------------------------------------------------------
+
+__host__ __device__ constexpr float bits2f(uint32_t b) { return __builtin_bit_cast(float, b); }
+
+template <int CB> struct CbBits;
+template <> struct CbBits<Q4_CB_NF4> { static constexpr uint32_t b[16] = Q4_CB_BITS_NF4; };
+template <> struct CbBits<Q4_CB_SDYN4> { static constexpr uint32_t b[16] = Q4_CB_BITS_SDYN4; };
+template <> struct CbBits<Q4_CB_DYN4> { static constexpr uint32_t b[16] = Q4_CB_BITS_DYN4; };
+template <> struct CbBits<Q4_CB_DYN4_NZ> { static constexpr uint32_t b[16] = Q4_CB_BITS_DYN4_NZ; };
+template <> struct CbBits<Q4_CB_LIN4_NZ> { static constexpr uint32_t b[16] = Q4_CB_BITS_LIN4_NZ; };
+
+// Sorted view of a codebook: N distinct levels ascending; code_of maps a
+// sorted index to its code (identity except for the sign-magnitude SDyn4,
+// whose "-0" code 8 is never produced).
+template <int CB> struct Book {
+    static constexpr int N = CB == Q4_CB_SDYN4 ? 15 : 16;
+    static constexpr int code_of(int k) {
+        return CB == Q4_CB_SDYN4 ? (k < 7 ? 15 - k : (k == 7 ? 0 : k - 7)) : k;
+    }
+    static constexpr float level(int k) { return bits2f(CbBits<CB>::b[code_of(k)]); }
+    // FP32 midpoint of adjacent levels; an exact midpoint rounds down.
+    static constexpr float mid(int k) { return (level(k) + level(k + 1)) * 0.5f; }
+};
+
+static constexpr bool sorted_ok(int cb) {
+    // levels strictly increasing and every midpoint strictly inside its cell
+    switch (cb) {
+#define Q4_CHECK(CB)                                                                             \
+    case CB:                                                                                     \
+        for (int k = 0; k + 1 < Book<CB>::N; ++k)                                                \
+            if (!(Book<CB>::level(k) < Book<CB>::mid(k) && Book<CB>::mid(k) < Book<CB>::level(k + 1))) \
+                return false;                                                                    \
+        return true;
+        Q4_CHECK(Q4_CB_NF4) Q4_CHECK(Q4_CB_SDYN4) Q4_CHECK(Q4_CB_DYN4) Q4_CHECK(Q4_CB_DYN4_NZ)
+        Q4_CHECK(Q4_CB_LIN4_NZ)
+#undef Q4_CHECK
+    }
+    return false;
+}
+static_assert(sorted_ok(Q4_CB_NF4) && sorted_ok(Q4_CB_SDYN4) && sorted_ok(Q4_CB_DYN4) &&
+                  sorted_ok(Q4_CB_DYN4_NZ) && sorted_ok(Q4_CB_LIN4_NZ),
+              "codebook levels must be strictly increasing with interior midpoints");
+
+// Device copies, indexed at run time when the LDS tables are filled.
+__constant__ uint32_t c_decode[5][16] = {Q4_CB_BITS_NF4, Q4_CB_BITS_SDYN4, Q4_CB_BITS_DYN4, Q4_CB_BITS_DYN4_NZ,
+                                         Q4_CB_BITS_LIN4_NZ};
+
+template <int CB> __device__ __forceinline__ float sorted_level_rt(int k) {
+    return bits2f(c_decode[CB][Book<CB>::code_of(k)]);
+}
+
+// ---------------------------------------------------------------------------
+// Round-to-nearest by bucket table
+// ---------------------------------------------------------------------------
+//
+// The RTN index of x is the number of FP32 midpoints strictly below x.
+// Buckets split |x| by its binary exponent and MB leading mantissa bits;
+// every bucket holds at most one midpoint (checked at compile time), so one
+// 8-byte table entry {thr, base} gives the exact count: base + (x > thr).  A bucket of a negative x covers (-hi, -lo], one
+// of a positive x [lo, hi); magnitudes below 2^(EMIN-127) share bucket 0.
+
+struct alignas(8) BucketEntry {
+    float thr;     // the one midpoint inside the bucket, or 3 (never exceeded)
+    int32_t base;  // midpoints below every x of the bucket
+};
+
+__host__ __device__ constexpr uint32_t f2bits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+template <int CB> struct Enc {
+    static constexpr int MB = 3;
+    static constexpr bool SIGNED = CB == Q4_CB_NF4 || CB == Q4_CB_SDYN4;
+    static constexpr int N = Book<CB>::N;
+    static constexpr int min_mid_exp() {
+        int e = 255;
+        for (int k = 0; k + 1 < N; ++k) {
+            const int ek = (int)((f2bits(Book<CB>::mid(k)) >> 23) & 0xFF);
+            if (ek < e) e = ek;
+        }
+        return e;
+    }
+    // bucket 0 ends at 2^(EMIN-127) * 1.125, below every midpoint magnitude
+    static constexpr int EMIN = min_mid_exp() - 1;
+    static constexpr int NPOS = ((127 - EMIN) << MB) + 1;
+    static constexpr int pow2ceil(int v) { int p = 1; while (p < v) p <<= 1; return p; }
+    static constexpr int PAD = pow2ceil(NPOS);
+    static constexpr int SIZE = SIGNED ? 2 * PAD : NPOS;
+};
+
+template <int CB> struct EncTable {
+    BucketEntry e[Enc<CB>::SIZE];
+    bool ok;
+    constexpr EncTable() : e(), ok(true) {
+        using E = Enc<CB>;
+        for (int s = 0; s < (E::SIGNED ? 2 : 1); ++s) {
+            for (int b = 0; b < (E::SIGNED ? E::PAD : E::NPOS); ++b) {
+                const int bb = b < E::NPOS ? b : E::NPOS - 1;  // padding repeats the last bucket
+                const float lo = bb == 0 ? 0.0f : bits2f((uint32_t)((E::EMIN << E::MB) + bb) << (23 - E::MB));
+                const float hi = bits2f((uint32_t)((E::EMIN << E::MB) + bb + 1) << (23 - E::MB));
+                int base = 0, inside = 0;
+                float thr = 3.0f;
+                for (int k = 0; k + 1 < E::N; ++k) {
+                    const float m = Book<CB>::mid(k);
+                    if (s == 0) {          // x in [lo, hi)
+                        if (m < lo) ++base;
+                        else if (m < hi) { ++inside; thr = m; }
+                    } else {               // x in (-hi, -lo]
+                        if (m <= -hi) ++base;
+                        else if (m <= -lo) { ++inside; thr = m; }
+                    }
+                }
+                if (inside > 1) ok = false;
+                BucketEntry& d = e[s * E::PAD + b];
+                d.thr = thr;
+                d.base = base;
+            }
+        }
+    }
+};
+
+static_assert(EncTable<Q4_CB_NF4>().ok && EncTable<Q4_CB_SDYN4>().ok && EncTable<Q4_CB_DYN4>().ok &&
+                  EncTable<Q4_CB_DYN4_NZ>().ok && EncTable<Q4_CB_LIN4_NZ>().ok,
+              "a bucket holds two midpoints: use more mantissa bits");
+
+// Floor buckets of an unsigned map whose first level is 0: the index of the
+// largest level <= x.  Each bucket holds at most one level, so one entry
+// {thr, lo} gives it: lo + (x >= thr).  Every level below the bucket lies
+// below every x of the bucket, so x sits exactly on a level iff x == thr.
+struct alignas(8) FloorEntry {
+    float thr;      // the one level inside the bucket, or 3 (never reached)
+    int32_t lo;     // index of the largest level below the bucket (-1 below 0)
+};
+
+template <int CB> struct FloorTable {
+    FloorEntry e[Enc<CB>::NPOS];
+    bool ok;
+    constexpr FloorTable() : e(), ok(true) {
+        using E = Enc<CB>;
+        if (Book<CB>::level(0) != 0.0f) ok = false;
+        for (int b = 0; b < E::NPOS; ++b) {
+            const float lo = b == 0 ? 0.0f : bits2f((uint32_t)((E::EMIN << E::MB) + b) << (23 - E::MB));
+            const float hi = bits2f((uint32_t)((E::EMIN << E::MB) + b + 1) << (23 - E::MB));
+            int below = 0, inside = 0;
+            float thr = 3.0f;
+            for (int k = 0; k < E::N; ++k) {
+                const float L = Book<CB>::level(k);
+                if (L < lo) ++below;
+                else if (L < hi) { ++inside; thr = L; }
+            }
+            if (inside > 1) ok = false;
+            FloorEntry& d = e[b];
+            d.thr = thr;
+            d.lo = below - 1;
+        }
+    }
+};
+static_assert(FloorTable<Q4_CB_DYN4>().ok, "floor buckets of Dyn4 must hold one level each");
+__constant__ FloorTable<Q4_CB_DYN4> c_floor_dyn4 = FloorTable<Q4_CB_DYN4>();
+
+__constant__ EncTable<Q4_CB_NF4> c_enc_nf4 = EncTable<Q4_CB_NF4>();
+__constant__ EncTable<Q4_CB_SDYN4> c_enc_sdyn4 = EncTable<Q4_CB_SDYN4>();
+__constant__ EncTable<Q4_CB_DYN4> c_enc_dyn4 = EncTable<Q4_CB_DYN4>();
+__constant__ EncTable<Q4_CB_DYN4_NZ> c_enc_dyn4nz = EncTable<Q4_CB_DYN4_NZ>();
+__constant__ EncTable<Q4_CB_LIN4_NZ> c_enc_lin4nz = EncTable<Q4_CB_LIN4_NZ>();
+
+template <int CB> __device__ __forceinline__ const BucketEntry* enc_table_global() {
+    if constexpr (CB == Q4_CB_NF4) return c_enc_nf4.e;
+    else if constexpr (CB == Q4_CB_SDYN4) return c_enc_sdyn4.e;
+    else if constexpr (CB == Q4_CB_DYN4) return c_enc_dyn4.e;
+    else if constexpr (CB == Q4_CB_DYN4_NZ) return c_enc_dyn4nz.e;
+    else return c_enc_lin4nz.e;
+}
+
+// Bucket index of x.  NaN or |x| > 1 land in the last bucket, so the
+// index never leaves the table.
+template <int CB> __device__ __forceinline__ uint32_t bucket_index(float x) {
+    using E = Enc<CB>;
+    const uint32_t u = __float_as_uint(x);
+    uint32_t raw = __builtin_amdgcn_ubfe(u, 23 - E::MB, 8 + E::MB);
+    raw = raw < (uint32_t)(E::EMIN << E::MB) ? (uint32_t)(E::EMIN << E::MB) : raw;
+    raw = raw > (uint32_t)(127 << E::MB) ? (uint32_t)(127 << E::MB) : raw;
+    uint32_t idx = raw - (uint32_t)(E::EMIN << E::MB);
+    if constexpr (E::SIGNED) idx += (u >> 31) * (uint32_t)E::PAD;
+    return idx;
+}
+template <int CB>
+__device__ __forceinline__ const BucketEntry& bucket_of(const BucketEntry* tab, float x) {
+    return tab[bucket_index<CB>(x)];
+}
+
+// The RTN index of x (midpoints strictly below x) from its bucket entry.
+__device__ __forceinline__ int rtn_index(const BucketEntry& e, float x) { return e.base + (x > e.thr ? 1 : 0); }
+// The floor index of x (largest level <= x) from a floor entry's {thr, lo}.
+__device__ __forceinline__ int floor_index(float thr, int lo, float x) { return lo + (x >= thr ? 1 : 0); }
+
+// ---------------------------------------------------------------------------
+// Flat layout
+// ---------------------------------------------------------------------------
+
+// Flat bucket layout, for the ZIP-SR kernels (their VALU issue rate is what
+// bounds them): the entry of x in [-1, 1] sits at its bit pattern >> 20
+// (sign, exponent, 3 mantissa bits), slots 0 .. 1016 for x >= 0 and
+// 2048 .. 3064 for x < 0, so finding it is a shift; the v floor entries of
+// x in [0, 1] fill the slots between, at 1017 + (bits >> 20).  Each flat
+// bucket lies inside one bucket of the compact tables above (which merge
+// the magnitudes below the smallest midpoint), so it takes that entry.
+constexpr int kFlatPos = (127 << 3) + 1;          // bits >> 20 of x in [+0, 1]
+constexpr int kFlatNeg = 2048;                     // bits >> 20 of x in [-1, -0]
+constexpr int kFlatSlots = kFlatNeg + kFlatPos;
+static_assert(2 * kFlatPos <= kFlatNeg, "the floor entries must fit between the two halves");
+
+template <int VCB, int VRULE> constexpr bool flat_tables() {
+    return VRULE == Q4_RULE_UPDATE_SR && VCB == Q4_CB_DYN4;
+}
+
+// Flat slots of x: the m entry of x in [-1, 1], and the v floor entry of
+// x in [0, 1] (11 bits: the slot stays below the negative half for any x).
+__device__ __forceinline__ uint32_t flat_m_slot(float x) { return __float_as_uint(x) >> 20; }
+__device__ __forceinline__ uint32_t flat_floor_slot(float x) {
+    return kFlatPos + __builtin_amdgcn_ubfe(__float_as_uint(x), 20, 11);
+}
+// Flat slot i: the compact entry of a value inside it (m entries of MCB,
+// Dyn4 floor entries as {thr, lo}, unused slots never exceeded).
+template <int MCB> __device__ __forceinline__ BucketEntry flat_slot(int i) {
+    BucketEntry d{3.0f, 0};
+    if (i < kFlatPos) {
+        d = enc_table_global<MCB>()[bucket_index<MCB>(bits2f((uint32_t)i << 20))];
+    } else if (i >= kFlatNeg) {
+        d = enc_table_global<MCB>()[bucket_index<MCB>(bits2f(0x80000000u | ((uint32_t)(i - kFlatNeg) << 20)))];
+    } else if (i - kFlatPos < kFlatPos) {
+        const FloorEntry& f = c_floor_dyn4.e[bucket_index<Q4_CB_DYN4>(bits2f((uint32_t)(i - kFlatPos) << 20))];
+        d.thr = f.thr;
+        d.base = f.lo;
+    }
+    return d;
+}
+
+// ---------------------------------------------------------------------------
+// 8-bit maps (SDyn8 m, Dyn8 v)
+// ---------------------------------------------------------------------------
+//
+// The nearest level is the number of FP32 midpoints strictly below x.
+// Counting them with a binary search over a sorted table in LDS puts every
+// probe of one step on the same bank (the probes of a step sit s apart, s a
+// power of two), so it is counted with a bucket table instead: a
+// non-negative float's bit pattern shifted right (exponent and top mantissa
+// bits) names a bucket that holds at most two midpoints; the table gives the
+// midpoints below the bucket, one 8-byte read gives the two candidates, and
+// two compares finish the count.
+//
+// SDyn8 is symmetric about zero with 127 positive midpoints P: for x >= 0
+// the ascending level index is 127 + #{P < x}, and for x < 0 it is
+// 127 - #{P <= |x|}, which is #{P < nextup(|x|)}.  Either count is the
+// magnitude part of the code; the sign bit goes on a non-zero magnitude.
+
+__constant__ uint32_t c_cb8[2][256] = {Q4_CB8_BITS_SDYN8, Q4_CB8_BITS_DYN8};
+
+struct Step8Lds {
+    float dec_m[256], dec_v[256];   // code-indexed levels
+    float mid_p[128];               // SDyn8's positive midpoints ascending, +inf padded
+    float mid_v[256];               // Dyn8's midpoints ascending, +inf padded
+    float2 pair_m[128], pair_v[256];  // {mid[i], mid[i + 1]}
+    uint8_t floor_m[Q4_RTN8_M_NB], floor_v[Q4_RTN8_V_NB];  // midpoints below each bucket
+};
+
+// Count of sorted, +inf padded table entries strictly below x (N a power of two).
+template <int N>
+__device__ __forceinline__ int count_below_sorted(const float* mid, float x) {
+    int idx = 0;
+#pragma unroll
+    for (int s = N / 2; s > 0; s >>= 1) idx += mid[idx + s - 1] < x ? s : 0;
+    return idx;
+}
+
+// #{midpoints < bits2f(key)} for a non-negative key; keys outside the
+// bucketed range clamp to the first or last bucket (in bounds for any key).
+template <int SHIFT, int LO, int NB>
+__device__ __forceinline__ uint32_t count_below8(const uint8_t* floor_tab, const float2* pair, uint32_t key) {
+    const int b = min(max((int)(key >> SHIFT) - LO, 0), NB - 1);
+    const uint32_t f = floor_tab[b];
+    const float2 pr = pair[f];
+    const float a = bits2f(key);
+    return f + (pr.x < a ? 1u : 0u) + (pr.y < a ? 1u : 0u);
+}
+
+__device__ __forceinline__ uint32_t rtn8_m(const Step8Lds& lds, float x) {
+    const uint32_t xb = __float_as_uint(x);
+    const uint32_t neg = xb >> 31;
+    const uint32_t c = count_below8<Q4_RTN8_M_SHIFT, Q4_RTN8_M_LO, Q4_RTN8_M_NB>(lds.floor_m, lds.pair_m,
+                                                                                 (xb & 0x7FFFFFFFu) + neg);
+    return c | ((neg != 0u && c != 0u) ? 0x80u : 0u);
+}
+
+__device__ __forceinline__ uint32_t rtn8_v(const Step8Lds& lds, float x) {
+    return count_below8<Q4_RTN8_V_SHIFT, Q4_RTN8_V_LO, Q4_RTN8_V_NB>(lds.floor_v, lds.pair_v, __float_as_uint(x));
+}
+
+// Fills the tables; every thread of a 256-thread group takes part.
+__device__ void step8_tables(Step8Lds& lds) {
+    const int t = threadIdx.x;
+    const float inf = __builtin_inff();
+    lds.dec_m[t] = bits2f(c_cb8[0][t]);
+    lds.dec_v[t] = bits2f(c_cb8[1][t]);
+    // the same FP32 sum and halving the definition forms; SDyn8's codes
+    // 0..127 ascend from 0, Dyn8's codes 0..255 ascend from 0
+    if (t < 128) lds.mid_p[t] = t < 127 ? (bits2f(c_cb8[0][t]) + bits2f(c_cb8[0][t + 1])) * 0.5f : inf;
+    lds.mid_v[t] = t < 255 ? (bits2f(c_cb8[1][t]) + bits2f(c_cb8[1][t + 1])) * 0.5f : inf;
+    __syncthreads();
+    if (t < 128) lds.pair_m[t] = float2{lds.mid_p[t], t < 127 ? lds.mid_p[t + 1] : inf};
+    lds.pair_v[t] = float2{lds.mid_v[t], t < 255 ? lds.mid_v[t + 1] : inf};
+    for (int b = t; b < Q4_RTN8_M_NB; b += 256)
+        lds.floor_m[b] = (uint8_t)count_below_sorted<128>(lds.mid_p, bits2f((uint32_t)(b + Q4_RTN8_M_LO) << Q4_RTN8_M_SHIFT));
+    for (int b = t; b < Q4_RTN8_V_NB; b += 256)
+        lds.floor_v[b] = (uint8_t)count_below_sorted<256>(lds.mid_v, bits2f((uint32_t)(b + Q4_RTN8_V_LO) << Q4_RTN8_V_SHIFT));
+    __syncthreads();
+}
+
+}  // namespace q4

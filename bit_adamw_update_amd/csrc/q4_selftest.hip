@@ -1,5 +1,6 @@
-// q4_selftest.hip -- exhaustive checks of the primitives in q4_exact.h, built
-// as a library of its own (libq4selftest.so) that only the tests load.
+// q4_selftest.hip -- exhaustive checks of the primitives in q4_exact.h and of
+// the round-to-nearest tables in q4_quant.h, built as a library of its own
+// (libq4selftest.so) that only the tests load.
 //
 // Correct rounding is checked from its definition, not against another
 // implementation: a finite y > 0 is the nearest float to a real z > 0 iff z
@@ -12,6 +13,7 @@
 #include <stdint.h>
 
 #include "q4_exact.h"
+#include "q4_quant.h"
 
 namespace {
 
@@ -97,6 +99,176 @@ __global__ void __launch_bounds__(256) k_nibble(uint64_t seed, unsigned long lon
     if (n != 0) atomicAdd(bad, (unsigned long long)n);
 }
 
+
+// ---------------------------------------------------------------------------
+// Round-to-nearest tables against plain counts
+// ---------------------------------------------------------------------------
+//
+// Each check takes the lookup the step kernels make (tables staged in LDS as
+// they stage them) and compares it with the definition: the RTN index of x
+// is the number of FP32 midpoints strictly below x, the floor index the
+// number of levels <= x less one.  The 4-bit counts run over the codebook's
+// 15 midpoints for every x.  The 8-bit counts keep a pointer into the sorted
+// midpoints that follows x through a run of consecutive bit patterns (x
+// rises through positive patterns and falls through negative ones); each
+// run starts from, and ends checked against, a count over all midpoints.
+
+enum QuantCheck {
+    QC_RTN_NF4 = 0, QC_RTN_SDYN4, QC_RTN_DYN4, QC_RTN_DYN4_NZ, QC_RTN_LIN4_NZ,  // compact tables
+    QC_FLOOR_DYN4,                  // compact floor table of Dyn4
+    QC_FLAT_NF4, QC_FLAT_SDYN4,     // flat m slots
+    QC_FLAT_FLOOR,                  // flat Dyn4 floor slots
+    QC_RTN8_M, QC_RTN8_V,           // 8-bit bucket counts
+    QC_CONTROL_NF4_TIES_UP,         // control: NF4 lookup that rounds midpoints up
+    QC_COUNT
+};
+constexpr int kRun = 4096;  // bit patterns per thread
+
+__host__ __device__ constexpr bool qc_signed(int c) {
+    return c == QC_RTN_NF4 || c == QC_RTN_SDYN4 || c == QC_FLAT_NF4 || c == QC_FLAT_SDYN4 || c == QC_RTN8_M ||
+           c == QC_CONTROL_NF4_TIES_UP;
+}
+
+template <int CB> __device__ __forceinline__ int plain_rtn4(float x) {
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k + 1 < q4::Book<CB>::N; ++k) n += q4::Book<CB>::mid(k) < x ? 1 : 0;
+    return n;
+}
+__device__ __forceinline__ int plain_floor_dyn4(float x) {
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < q4::Book<Q4_CB_DYN4>::N; ++k) n += q4::Book<Q4_CB_DYN4>::level(k) <= x ? 1 : 0;
+    return n - 1;
+}
+
+struct QuantLds {
+    q4::BucketEntry enc[q4::Enc<Q4_CB_NF4>::SIZE > q4::Enc<Q4_CB_SDYN4>::SIZE ? q4::Enc<Q4_CB_NF4>::SIZE
+                                                                                : q4::Enc<Q4_CB_SDYN4>::SIZE];
+    q4::FloorEntry floor[q4::Enc<Q4_CB_DYN4>::NPOS];
+    q4::BucketEntry flat[q4::kFlatSlots];
+    q4::Step8Lds t8;
+    float mids8[256];  // the 8-bit map's midpoints ascending, from its decoded levels
+};
+static_assert(q4::Enc<Q4_CB_DYN4>::SIZE <= q4::Enc<Q4_CB_NF4>::SIZE && q4::Enc<Q4_CB_DYN4_NZ>::SIZE <= q4::Enc<Q4_CB_NF4>::SIZE &&
+                  q4::Enc<Q4_CB_LIN4_NZ>::SIZE <= q4::Enc<Q4_CB_NF4>::SIZE,
+              "the staging array must hold every compact table");
+
+// Check one x of a 4-bit map; returns true when the lookup equals the count.
+template <int CHECK> __device__ __forceinline__ bool check4(const QuantLds& L, float x) {
+    if constexpr (CHECK <= QC_RTN_LIN4_NZ) {
+        return q4::rtn_index(q4::bucket_of<CHECK>(L.enc, x), x) == plain_rtn4<CHECK>(x);
+    } else if constexpr (CHECK == QC_FLOOR_DYN4 || CHECK == QC_FLAT_FLOOR) {
+        float thr;
+        int lo;
+        if constexpr (CHECK == QC_FLOOR_DYN4) {
+            const q4::FloorEntry& f = L.floor[q4::bucket_index<Q4_CB_DYN4>(x)];
+            thr = f.thr;
+            lo = f.lo;
+        } else {
+            const q4::BucketEntry& f = L.flat[q4::flat_floor_slot(x)];
+            thr = f.thr;
+            lo = f.base;
+        }
+        const int want = plain_floor_dyn4(x);
+        // the kernels also take "x is a level" from the entry: x == thr
+        return q4::floor_index(thr, lo, x) == want && (x == thr) == (x == q4::Book<Q4_CB_DYN4>::level(want));
+    } else if constexpr (CHECK == QC_CONTROL_NF4_TIES_UP) {
+        // differs from the count exactly at the 15 midpoints
+        const q4::BucketEntry& e = q4::bucket_of<Q4_CB_NF4>(L.enc, x);
+        return e.base + (x >= e.thr ? 1 : 0) == plain_rtn4<Q4_CB_NF4>(x);
+    } else {
+        constexpr int CB = CHECK == QC_FLAT_NF4 ? Q4_CB_NF4 : Q4_CB_SDYN4;
+        return q4::rtn_index(L.flat[q4::flat_m_slot(x)], x) == plain_rtn4<CB>(x);
+    }
+}
+
+template <int CHECK>
+__global__ void __launch_bounds__(256) k_quant(uint64_t lo, uint64_t hi, unsigned long long* bad, uint32_t* first_bad) {
+    __shared__ QuantLds L;
+    const int t = threadIdx.x;
+    if constexpr (CHECK <= QC_RTN_LIN4_NZ) {
+        for (int i = t; i < q4::Enc<CHECK>::SIZE; i += blockDim.x) L.enc[i] = q4::enc_table_global<CHECK>()[i];
+    } else if constexpr (CHECK == QC_CONTROL_NF4_TIES_UP) {
+        for (int i = t; i < q4::Enc<Q4_CB_NF4>::SIZE; i += blockDim.x) L.enc[i] = q4::enc_table_global<Q4_CB_NF4>()[i];
+    } else if constexpr (CHECK == QC_FLOOR_DYN4) {
+        for (int i = t; i < q4::Enc<Q4_CB_DYN4>::NPOS; i += blockDim.x) L.floor[i] = q4::c_floor_dyn4.e[i];
+    } else if constexpr (CHECK == QC_FLAT_NF4 || CHECK == QC_FLAT_FLOOR) {
+        for (int i = t; i < q4::kFlatSlots; i += blockDim.x) L.flat[i] = q4::flat_slot<Q4_CB_NF4>(i);
+    } else if constexpr (CHECK == QC_FLAT_SDYN4) {
+        for (int i = t; i < q4::kFlatSlots; i += blockDim.x) L.flat[i] = q4::flat_slot<Q4_CB_SDYN4>(i);
+    }
+    constexpr bool EIGHT = CHECK == QC_RTN8_M || CHECK == QC_RTN8_V;
+    constexpr int NMID = CHECK == QC_RTN8_M ? 254 : 255;
+    if constexpr (EIGHT) {
+        q4::step8_tables(L.t8);  // synchronizes the group
+        // ascending levels as decoded: SDyn8 from its most negative code
+        // (0x80 | 127) through 0x80 | 1, then codes 0 .. 127; Dyn8 codes 0 .. 255
+        auto level = [](int j) {
+            if constexpr (CHECK == QC_RTN8_M)
+                return q4::bits2f(q4::c_cb8[0][j < 127 ? (0x80 | (127 - j)) : (j - 127)]);
+            else
+                return q4::bits2f(q4::c_cb8[1][j]);
+        };
+        if (t < NMID) L.mids8[t] = (level(t) + level(t + 1)) * 0.5f;
+    }
+    __syncthreads();
+
+    const uint64_t r0 = lo + ((uint64_t)blockIdx.x * blockDim.x + t) * kRun;
+    if (r0 >= hi) return;
+    const uint64_t r1 = r0 + kRun < hi ? r0 + kRun : hi;
+    uint32_t n = 0, first = 0xFFFFFFFFu;
+    if constexpr (!EIGHT) {
+        for (uint64_t i = r0; i < r1; ++i) {
+            const uint32_t b = (uint32_t)i;
+            if (!check4<CHECK>(L, __uint_as_float(b))) {
+                ++n;
+                first = min(first, b);
+            }
+        }
+    } else {
+        auto full_count = [&](float x) {
+            int c = 0;
+            for (int j = 0; j < NMID; ++j) c += L.mids8[j] < x ? 1 : 0;
+            return c;
+        };
+        auto code_of = [](int idx) -> uint32_t {
+            if constexpr (CHECK == QC_RTN8_M) return idx >= 127 ? (uint32_t)(idx - 127) : 0x80u | (uint32_t)(127 - idx);
+            else return (uint32_t)idx;
+        };
+        const bool neg = ((uint32_t)r0 >> 31) != 0;
+        int j = full_count(__uint_as_float((uint32_t)r0));
+        for (uint64_t i = r0; i < r1; ++i) {
+            const uint32_t b = (uint32_t)i;
+            const float x = __uint_as_float(b);
+            if (neg) {
+                while (j > 0 && !(L.mids8[j - 1] < x)) --j;
+            } else {
+                while (j < NMID && L.mids8[j] < x) ++j;
+            }
+            const uint32_t got = CHECK == QC_RTN8_M ? q4::rtn8_m(L.t8, x) : q4::rtn8_v(L.t8, x);
+            if (got != code_of(j)) {
+                ++n;
+                first = min(first, b);
+            }
+        }
+        // the pointer must agree with a fresh count at the end of the run
+        if (j != full_count(__uint_as_float((uint32_t)(r1 - 1)))) {
+            ++n;
+            first = min(first, (uint32_t)(r1 - 1));
+        }
+    }
+    if (n != 0) {
+        atomicAdd(bad, (unsigned long long)n);
+        atomicMin(first_bad, first);
+    }
+}
+
+template <int C> void launch_quant(uint64_t lo, uint64_t hi, unsigned long long* bad, uint32_t* first) {
+    const uint64_t runs = (hi - lo + kRun - 1) / kRun;
+    k_quant<C><<<(unsigned)((runs + 255) / 256), 256>>>(lo, hi, bad, first);
+}
+
 struct DevCounters {
     unsigned long long* bad = nullptr;
     uint32_t* first = nullptr;
@@ -170,6 +342,48 @@ int q4st_nibble_decode(uint64_t seed, uint32_t waves, int form, unsigned long lo
     e = hipGetLastError();
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e == hipSuccess) e = hipMemcpy(mismatches, c.bad, sizeof(*mismatches), hipMemcpyDeviceToHost);
+    return (int)e;
+}
+
+// Checks one round-to-nearest lookup of the step kernels (check: 0-4 the
+// compact RTN tables of codebooks 0-4, 5 the compact Dyn4 floor table, 6-7
+// the flat m slots of NF4 and SDyn4, 8 the flat Dyn4 floor slots, 9-10 the
+// 8-bit SDyn8 and Dyn8 counts; 11 is a control, an NF4 lookup that rounds
+// a midpoint up) over every float bit pattern in [lo, hi)
+// against the plain count.  [lo, hi) must lie inside the lookup's domain:
+// the patterns of [+0, 1] (0 .. 0x3F800001), or for a signed map also those
+// of [-1, -0] (0x80000000 .. 0xBF800001).  Writes the number of inputs whose
+// lookup differs and the smallest such pattern (0xFFFFFFFF if none).
+// Returns 0, -1 for invalid arguments, or a HIP error code.  Synchronous.
+int q4st_quant_sweep(int check, uint64_t lo, uint64_t hi, unsigned long long* mismatches, uint32_t* first_bad) {
+    if (check < 0 || check >= QC_COUNT || lo > hi || !mismatches || !first_bad) return -1;
+    const bool pos = hi <= 0x3F800001ull;
+    const bool negr = lo >= 0x80000000ull && hi <= 0xBF800001ull;
+    if (!(pos || (negr && qc_signed(check)))) return -1;
+    DevCounters c;
+    hipError_t e = c.init();
+    if (e != hipSuccess) return (int)e;
+    if (hi > lo) {
+        switch (check) {
+        case QC_RTN_NF4: launch_quant<QC_RTN_NF4>(lo, hi, c.bad, c.first); break;
+        case QC_RTN_SDYN4: launch_quant<QC_RTN_SDYN4>(lo, hi, c.bad, c.first); break;
+        case QC_RTN_DYN4: launch_quant<QC_RTN_DYN4>(lo, hi, c.bad, c.first); break;
+        case QC_RTN_DYN4_NZ: launch_quant<QC_RTN_DYN4_NZ>(lo, hi, c.bad, c.first); break;
+        case QC_RTN_LIN4_NZ: launch_quant<QC_RTN_LIN4_NZ>(lo, hi, c.bad, c.first); break;
+        case QC_FLOOR_DYN4: launch_quant<QC_FLOOR_DYN4>(lo, hi, c.bad, c.first); break;
+        case QC_FLAT_NF4: launch_quant<QC_FLAT_NF4>(lo, hi, c.bad, c.first); break;
+        case QC_FLAT_SDYN4: launch_quant<QC_FLAT_SDYN4>(lo, hi, c.bad, c.first); break;
+        case QC_FLAT_FLOOR: launch_quant<QC_FLAT_FLOOR>(lo, hi, c.bad, c.first); break;
+        case QC_RTN8_M: launch_quant<QC_RTN8_M>(lo, hi, c.bad, c.first); break;
+        case QC_RTN8_V: launch_quant<QC_RTN8_V>(lo, hi, c.bad, c.first); break;
+        default: launch_quant<QC_CONTROL_NF4_TIES_UP>(lo, hi, c.bad, c.first); break;
+        }
+        e = hipGetLastError();
+        if (e == hipSuccess) e = hipDeviceSynchronize();
+        if (e != hipSuccess) return (int)e;
+    }
+    e = hipMemcpy(mismatches, c.bad, sizeof(*mismatches), hipMemcpyDeviceToHost);
+    if (e == hipSuccess) e = hipMemcpy(first_bad, c.first, sizeof(*first_bad), hipMemcpyDeviceToHost);
     return (int)e;
 }
 

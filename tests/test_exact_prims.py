@@ -7,7 +7,12 @@
     correctly rounded 1/s for every s >= 2^-126 (through +inf) and +0 below
     that, for zero and for NaN;
   * the nibble-addressed ds_bpermute decode fetches lane row + code for
-    every nibble, and ds_bpermute ignores address bits 0-1 and 8-31.
+    every nibble, and ds_bpermute ignores address bits 0-1 and 8-31;
+  * every round-to-nearest lookup of the step kernels (q4_quant.h: compact
+    bucket tables of the five 4-bit maps, the Dyn4 floor table, the flat
+    slots of the ZIP-SR kernels, the 8-bit bucket counts) equals the plain
+    count of midpoints below x (levels at or below x for the floor) for
+    every FP32 x in the lookup's domain, [-1, 1] or [0, 1].
 
 The library checks each result against the definition of correct rounding
 (the input must lie strictly between the squares, or reciprocals, of the
@@ -24,6 +29,11 @@ from bit_adamw_update_amd import build
 SQRT, INV_SCALE = 0, 1
 FAST, BARE = 0, 1
 F32_INF = 0x7F800000
+ONE, NEG_ZERO, NEG_ONE = 0x3F800000, 0x80000000, 0xBF800000
+# (name, signed domain) in the library's check order
+QUANT_CHECKS = [("rtn_nf4", True), ("rtn_sdyn4", True), ("rtn_dyn4", False), ("rtn_dyn4_nz", False),
+                ("rtn_lin4_nz", False), ("floor_dyn4", False), ("flat_nf4", True), ("flat_sdyn4", True),
+                ("flat_floor_dyn4", False), ("rtn8_sdyn8", True), ("rtn8_dyn8", False)]
 
 
 def _lib():
@@ -36,6 +46,9 @@ def _lib():
     lib.q4st_nibble_decode.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_int,
                                        ctypes.POINTER(ctypes.c_ulonglong)]
     lib.q4st_nibble_decode.restype = ctypes.c_int
+    lib.q4st_quant_sweep.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
+                                     ctypes.POINTER(ctypes.c_ulonglong), ctypes.POINTER(ctypes.c_uint32)]
+    lib.q4st_quant_sweep.restype = ctypes.c_int
     return lib
 
 
@@ -51,7 +64,7 @@ def _sweep(lib, what, form, lo, hi):
 def test_selftest_library_exports_and_validates():
     lib = _lib()
     out = os.popen(f"nm -D --defined-only {build.SELFTEST_PATH}").read()
-    for sym in ("q4st_sweep", "q4st_nibble_decode"):
+    for sym in ("q4st_sweep", "q4st_nibble_decode", "q4st_quant_sweep"):
         assert f" T {sym}" in out
     n, first = ctypes.c_ulonglong(0), ctypes.c_uint32(0)
     # rejected before any device call
@@ -61,6 +74,11 @@ def test_selftest_library_exports_and_validates():
     assert lib.q4st_sweep(0, 0, 0, (1 << 32) + 1, ctypes.byref(n), ctypes.byref(first)) == -1
     assert lib.q4st_nibble_decode(1, 6, 0, ctypes.byref(n)) == -1
     assert lib.q4st_nibble_decode(1, 0, 0, ctypes.byref(n)) == -1
+    assert lib.q4st_quant_sweep(len(QUANT_CHECKS) + 1, 0, 1, ctypes.byref(n), ctypes.byref(first)) == -1
+    # outside [+0, 1], and the negative half for an unsigned map
+    assert lib.q4st_quant_sweep(0, 0, ONE + 2, ctypes.byref(n), ctypes.byref(first)) == -1
+    assert lib.q4st_quant_sweep(2, NEG_ZERO, NEG_ONE + 1, ctypes.byref(n), ctypes.byref(first)) == -1
+    assert lib.q4st_quant_sweep(0, ONE, NEG_ZERO, ctypes.byref(n), ctypes.byref(first)) == -1
 
 
 @pytest.mark.gpu
@@ -92,3 +110,30 @@ def test_nibble_decode(form):
         n = ctypes.c_ulonglong(0)
         assert lib.q4st_nibble_decode(seed, 1 << 16, form, ctypes.byref(n)) == 0
         assert n.value == 0, f"seed {seed}: {n.value} elements fetched the wrong lane"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("check", range(len(QUANT_CHECKS)), ids=[c[0] for c in QUANT_CHECKS])
+def test_round_to_nearest_lookups_exhaustive(check):
+    lib = _lib()
+    name, signed = QUANT_CHECKS[check]
+    ranges = [(0, ONE + 1)] + ([(NEG_ZERO, NEG_ONE + 1)] if signed else [])
+    for lo, hi in ranges:
+        n, first = ctypes.c_ulonglong(0), ctypes.c_uint32(0)
+        rc = lib.q4st_quant_sweep(check, lo, hi, ctypes.byref(n), ctypes.byref(first))
+        assert rc == 0, f"q4st_quant_sweep returned {rc}"
+        print(f"{name} [{lo:#010x}, {hi:#010x}): {n.value} mismatches, first {first.value:#010x}", flush=True)
+        assert (n.value, first.value) == (0, 0xFFFFFFFF), name
+
+
+@pytest.mark.gpu
+def test_round_to_nearest_sweep_sees_single_inputs():
+    # control: an NF4 lookup that rounds a midpoint up differs from the count
+    # at exactly the 15 midpoints, all inside [-1, 1]
+    lib = _lib()
+    total = 0
+    for lo, hi in ((0, ONE + 1), (NEG_ZERO, NEG_ONE + 1)):
+        n, first = ctypes.c_ulonglong(0), ctypes.c_uint32(0)
+        assert lib.q4st_quant_sweep(len(QUANT_CHECKS), lo, hi, ctypes.byref(n), ctypes.byref(first)) == 0
+        total += n.value
+    assert total == 15
