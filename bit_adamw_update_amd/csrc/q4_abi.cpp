@@ -231,9 +231,13 @@ size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 // Workspace layout of a step.
 
 struct Plan {
-    size_t off_tab, off_chunks, off_mats, off_tab1, off_chunks1, off_inv, off_prow, off_pcol, off_pmean, off_sqpart,
-        total;
+    size_t off_tab, off_chunks, off_mats, off_tab1, off_chunks1, off_schunks, off_inv, off_prow, off_pcol, off_pmean,
+        off_sqpart, total;
     int64_t total_chunks = 0;
+    // the quantized steps' prefix: each tensor starts at a multiple of
+    // kStepAlignChunks (the chunks between only align the next tensor)
+    std::vector<int64_t> schunks;
+    int64_t total_schunks = 0;
     int n_mats = 0;
     int64_t total_tiles = 0, total_rgroups = 0, total_cgroups = 0;
     std::vector<DevTensor> tab;
@@ -249,6 +253,8 @@ struct Plan {
 void plan_layout(const Resolved& r, const q4_tensor* t, int32_t n, Plan& P, uint8_t* ws) {
     P.tab.assign(n, DevTensor{});
     P.chunks.assign(n + 1, 0);
+    P.schunks.assign(n + 1, 0);
+    P.total_schunks = 0;
     P.mats.clear();
     int64_t prow = 0, pcol = 0, pmean = 0;
     for (int32_t i = 0; i < n; ++i) {
@@ -271,7 +277,10 @@ void plan_layout(const Resolved& r, const q4_tensor* t, int32_t n, Plan& P, uint
         d.flags = x.flags;
         d.chunk_begin = P.total_chunks;
         P.chunks[i] = P.total_chunks;
-        P.total_chunks += (x.numel + kChunkElems - 1) / kChunkElems;
+        const int64_t nch = (x.numel + kChunkElems - 1) / kChunkElems;
+        P.total_chunks += nch;
+        P.schunks[i] = P.total_schunks;
+        P.total_schunks += (nch + kStepAlignChunks - 1) / kStepAlignChunks * kStepAlignChunks;
         if (d.kind == KIND_FACTORED && x.numel > 0) {
             DevMatrix m{};
             m.grad = x.grad;
@@ -302,6 +311,7 @@ void plan_layout(const Resolved& r, const q4_tensor* t, int32_t n, Plan& P, uint
         }
     }
     P.chunks[n] = P.total_chunks;
+    P.schunks[n] = P.total_schunks;
     P.n_mats = (int)P.mats.size();
     P.tab1.clear();
     P.chunks1.clear();
@@ -321,6 +331,7 @@ void plan_layout(const Resolved& r, const q4_tensor* t, int32_t n, Plan& P, uint
     P.off_mats = o;      o = round256(o + sizeof(DevMatrix) * P.mats.size());
     P.off_tab1 = o;      o = round256(o + sizeof(DevTensor) * P.tab1.size());
     P.off_chunks1 = o;   o = round256(o + sizeof(int64_t) * P.chunks1.size());
+    P.off_schunks = o;   o = round256(o + sizeof(int64_t) * (n + 1));
     P.off_inv = o;       o = round256(o + sizeof(float) * P.mats.size());
     P.off_prow = o;      o = round256(o + sizeof(double) * prow);
     P.off_pcol = o;      o = round256(o + sizeof(double) * pcol);
@@ -382,6 +393,7 @@ q4_status upload_tables(const Plan& P, int32_t n, uint8_t* wsb, hipStream_t st) 
         std::memcpy(host.data() + (P.off_tab1 - P.off_tab), P.tab1.data(), sizeof(DevTensor) * P.tab1.size());
     if (!P.chunks1.empty())
         std::memcpy(host.data() + (P.off_chunks1 - P.off_tab), P.chunks1.data(), sizeof(int64_t) * P.chunks1.size());
+    std::memcpy(host.data() + (P.off_schunks - P.off_tab), P.schunks.data(), sizeof(int64_t) * (n + 1));
     const hipError_t e = hipMemcpyAsync(wsb + P.off_tab, host.data(), upload, hipMemcpyHostToDevice, st);
     if (e != hipSuccess) return hip_fail(e, "tensor table upload");
     return Q4_OK;
@@ -635,6 +647,7 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
 
     const DevTensor* d_tab = reinterpret_cast<const DevTensor*>(wsb + P.off_tab);
     const int64_t* d_chunks = reinterpret_cast<const int64_t*>(wsb + P.off_chunks);
+    const int64_t* d_schunks = reinterpret_cast<const int64_t*>(wsb + P.off_schunks);
     const DevMatrix* d_mats = reinterpret_cast<const DevMatrix*>(wsb + P.off_mats);
     bool stats_ready = (hp->flags & Q4_HP_GRAD_STATS) != 0;
     if (hp->max_grad_norm > 0.0f) {
@@ -661,7 +674,7 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
         return ok();
     }
     if (r.recipe == Q4_RECIPE_BLOCK8) {
-        e = launch_block8_step(sc, d_tab, d_chunks, n, P.total_chunks, st);
+        e = launch_block8_step(sc, d_tab, d_schunks, n, P.total_schunks, st);
         if (e != hipSuccess) return hip_fail(e, "8-bit step launch");
         return ok();
     }
@@ -670,7 +683,7 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
                                   clip, stats_ready, st);
         if (e != hipSuccess) return hip_fail(e, "factored statistics launch");
     }
-    e = launch_fused_step(r.var, sc, d_tab, d_chunks, n, P.total_chunks, P.n_mats > 0, st);
+    e = launch_fused_step(r.var, sc, d_tab, d_schunks, n, P.total_schunks, P.n_mats > 0, st);
     if (e != hipSuccess) return hip_fail(e, "fused step launch");
     return ok();
 }

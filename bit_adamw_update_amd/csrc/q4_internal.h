@@ -18,6 +18,13 @@ constexpr int kTileCols = 512;         // columns per tile (64 lanes x 8 BF16)
 constexpr int kGroup = 256;            // rows per finalize work-group
 constexpr int kColGroup = 64;          // columns per finalize work-group (4 band slices of 64 lanes)
 constexpr int kAccGroups = 2048;       // work-groups of the chunk-order accumulation pass (at most)
+// The quantized steps number chunks in a prefix where every tensor starts at
+// a multiple of kStepAlignChunks (8 chunks = 32 block scales = one 128-byte
+// line of each scale array); a work-group walks runs of up to kRunSlabs
+// consecutive slabs of kWavesPerGroup chunks, so each scale line is written
+// whole by one work-group.
+constexpr int64_t kStepAlignChunks = 8;
+constexpr int kRunSlabs = 8;
 
 // Gradient pass modes: read the gradient for its statistics only, copy the
 // microbatch into it, or add the microbatch to it.
@@ -95,6 +102,8 @@ struct Variant { int mcb, vcb, vrule; };
 
 // has_matrices: the tensor list holds factored matrices (their row/column
 // gathers run best at 7 work-groups per CU, which the launch then enforces).
+// The fused and 8-bit steps take the aligned step prefix (kStepAlignChunks);
+// the FP32 step takes the plain one.
 hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevTensor* d_tab,
                              const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks,
                              bool has_matrices, hipStream_t stream);

@@ -494,13 +494,17 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     if ((FULL || blk_ok) && sub == 0) vscales[lb4] = stored;
 }
 
-// The work-group's logical index: the dispatcher hands work-groups to the
-// 8 XCDs in turn, so group b runs on XCD b mod 8; numbering the groups of
-// one XCD consecutively gives each XCD a contiguous share of every sweep.
-__device__ __forceinline__ int64_t xcd_group() {
-    const uint32_t b = blockIdx.x, n = gridDim.x;
-    const uint32_t q = n >> 3, r = n & 7u, x = b & 7u;
-    return (int64_t)(x * q + (x < r ? x : r) + (b >> 3));
+// The next chunk of a wavefront in the quantized steps: work-group g walks
+// runs of R consecutive slabs (kWavesPerGroup adjacent chunks each), run k
+// being slabs (k G + g) R .. (k G + g) R + R - 1, so that each 128-byte line
+// of block scales is written whole by one work-group (a line written in
+// parts by groups on different XCDs, with their own L2 caches, costs a
+// partial write-back: 4% of the GPT-2.7B ZE-EDEN step).  j counts the
+// slabs done in the current run.
+__device__ __forceinline__ int64_t next_chunk(int64_t c, int& j, int run_slabs, int64_t groups) {
+    if (++j < run_slabs) return c + kWavesPerGroup;
+    j = 0;
+    return c + (groups * run_slabs - (run_slabs - 1)) * kWavesPerGroup;
 }
 
 // Last tensor whose first chunk is <= c (binary search over the prefix).
@@ -525,7 +529,7 @@ template <int MCB, int VCB, int VRULE, bool CLIP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves<VRULE>())))
 void k_fused_step(const DevTensor* __restrict__ tab,
                                                      const int64_t* __restrict__ chunk_begin, int n_tensors,
-                                                     int64_t total_chunks, StepScalars sc) {
+                                                     int64_t total_chunks, int run_slabs, StepScalars sc) {
     constexpr bool FLAT = flat_tables<VCB, VRULE>();
     __shared__ StepLds<MCB, VCB, FLAT> lds;
     {
@@ -559,23 +563,24 @@ void k_fused_step(const DevTensor* __restrict__ tab,
     // clipping is a separate instantiation: the unclipped kernel carries no
     // trace of it (its live values are what limits occupancy)
     const float gs = CLIP ? *clip_of_table(tab) : 1.0f;
-    // XCD-contiguous groups measured 1.5% faster for the ZIP-SR kernels and
-    // 0.6% slower for the others (GPT-2.7B set, same box)
-    const int64_t g = FLAT ? xcd_group() : (int64_t)blockIdx.x;
-    int t = first_tensor(chunk_begin, n_tensors, g * kWavesPerGroup + wave);
-    for (int64_t c = g * kWavesPerGroup + wave; c < total_chunks;
-         c += (int64_t)gridDim.x * kWavesPerGroup) {
+    const int64_t G = gridDim.x;
+    int64_t c = (int64_t)blockIdx.x * run_slabs * kWavesPerGroup + wave;
+    int t = first_tensor(chunk_begin, n_tensors, c);
+    for (int j = 0; c < total_chunks;) {
         while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
         const DevTensor T = tab[t];
-        const int64_t lc = c - T.chunk_begin;
-        const bool full = (lc + 1) * kChunkElems <= T.numel;
-        if (T.kind == KIND_PACKED) {
-            if (full) step_chunk<MCB, VCB, VRULE, true, true, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
-            else step_chunk<MCB, VCB, VRULE, false, true, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
-        } else {
-            if (full) step_chunk<MCB, VCB, VRULE, true, false, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
-            else step_chunk<MCB, VCB, VRULE, false, false, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
+        const int64_t lc = c - chunk_begin[t];
+        if (lc * kChunkElems < T.numel) {  // beyond: a chunk that only aligns the next tensor
+            const bool full = (lc + 1) * kChunkElems <= T.numel;
+            if (T.kind == KIND_PACKED) {
+                if (full) step_chunk<MCB, VCB, VRULE, true, true, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
+                else step_chunk<MCB, VCB, VRULE, false, true, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
+            } else {
+                if (full) step_chunk<MCB, VCB, VRULE, true, false, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
+                else step_chunk<MCB, VCB, VRULE, false, false, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
+            }
         }
+        c = next_chunk(c, j, run_slabs, G);
     }
 }
 
@@ -737,20 +742,24 @@ __device__ __forceinline__ void step8_chunk(const DevTensor& T, const int64_t lc
 template <bool CLIP>
 __global__ __launch_bounds__(256) void k_step8(const DevTensor* __restrict__ tab,
                                                 const int64_t* __restrict__ chunk_begin, int n_tensors,
-                                                int64_t total_chunks, StepScalars sc) {
+                                                int64_t total_chunks, int run_slabs, StepScalars sc) {
     __shared__ Step8Lds lds;
     step8_tables(lds);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float gs = CLIP ? *clip_of_table(tab) : 1.0f;
-    int t = first_tensor(chunk_begin, n_tensors, (int64_t)blockIdx.x * kWavesPerGroup + wave);
-    for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks;
-         c += (int64_t)gridDim.x * kWavesPerGroup) {
+    const int64_t G = gridDim.x;
+    int64_t c = (int64_t)blockIdx.x * run_slabs * kWavesPerGroup + wave;
+    int t = first_tensor(chunk_begin, n_tensors, c);
+    for (int j = 0; c < total_chunks;) {
         while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
         const DevTensor T = tab[t];
-        const int64_t lc = c - T.chunk_begin;
-        if ((lc + 1) * kChunkElems <= T.numel) step8_chunk<true, CLIP>(T, lc, sc, lds, lane, gs);
-        else step8_chunk<false, CLIP>(T, lc, sc, lds, lane, gs);
+        const int64_t lc = c - chunk_begin[t];
+        if (lc * kChunkElems < T.numel) {  // beyond: a chunk that only aligns the next tensor
+            if ((lc + 1) * kChunkElems <= T.numel) step8_chunk<true, CLIP>(T, lc, sc, lds, lane, gs);
+            else step8_chunk<false, CLIP>(T, lc, sc, lds, lane, gs);
+        }
+        c = next_chunk(c, j, run_slabs, G);
     }
 }
 
@@ -1191,6 +1200,23 @@ static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_ca
     return (int)(groups < cap ? (groups > 0 ? groups : 1) : cap);
 }
 
+// Grid and run length of the quantized steps: the grid of step_grid over
+// slabs, and runs of kRunSlabs slabs while the set still has a run for
+// every resident group (halved until it does, down to single slabs).
+struct RunLaunch {
+    int grid, run_slabs;
+};
+template <class K>
+static RunLaunch run_launch(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds = 0,
+                            int64_t max_mult = 4) {
+    const int cap = step_grid(kernel, total_chunks, per_cu_cache, dyn_lds, max_mult);
+    const int64_t slabs = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
+    int r = kRunSlabs;
+    while (r > 1 && slabs / r < cap) r >>= 1;
+    const int64_t runs = (slabs + r - 1) / r;
+    return {(int)(runs < cap ? (runs > 0 ? runs : 1) : cap), r};
+}
+
 #define Q4_VARIANTS(X)                                              \
     X(Q4_CB_NF4, Q4_CB_DYN4, Q4_RULE_UPDATE_SR)    /* ZIP-SR */    \
     X(Q4_CB_NF4, Q4_CB_DYN4_NZ, Q4_RULE_STATE_RTN) /* ZE-EDEN, factored */ \
@@ -1224,15 +1250,15 @@ hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevT
         if (sc.flags & SF_CLIP) {                                                                            \
             static std::atomic<int> occ[2];                                                                  \
             const size_t dl = (cap && !flat_tables<B, C>()) ? kCap7Lds : 0;                                  \
-            const int grid = step_grid(k_fused_step<A, B, C, true>, total_chunks, occ[cap], dl, cap ? 2 : 4);             \
-            k_fused_step<A, B, C, true><<<grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors,          \
-                                                                   total_chunks, sc);                        \
+            const RunLaunch L = run_launch(k_fused_step<A, B, C, true>, total_chunks, occ[cap], dl, cap ? 2 : 4); \
+            k_fused_step<A, B, C, true><<<L.grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors,        \
+                                                                     total_chunks, L.run_slabs, sc);         \
         } else {                                                                                             \
             static std::atomic<int> occ[2];                                                                  \
             const size_t dl = (cap && !flat_tables<B, C>()) ? kCap7Lds : 0;                                  \
-            const int grid = step_grid(k_fused_step<A, B, C, false>, total_chunks, occ[cap], dl, cap ? 2 : 4);            \
-            k_fused_step<A, B, C, false><<<grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors,         \
-                                                                    total_chunks, sc);                       \
+            const RunLaunch L = run_launch(k_fused_step<A, B, C, false>, total_chunks, occ[cap], dl, cap ? 2 : 4); \
+            k_fused_step<A, B, C, false><<<L.grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors,       \
+                                                                      total_chunks, L.run_slabs, sc);        \
         }                                                                                                    \
         return hipGetLastError();                                                                            \
     }
@@ -1349,12 +1375,12 @@ hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, con
     if (total_chunks <= 0) return hipSuccess;
     if (sc.flags & SF_CLIP) {
         static std::atomic<int> occ{0};
-        k_step8<true><<<step_grid(k_step8<true>, total_chunks, occ), 256, 0, stream>>>(d_tab, d_chunk_begin,
-                                                                                      n_tensors, total_chunks, sc);
+        const RunLaunch L = run_launch(k_step8<true>, total_chunks, occ);
+        k_step8<true><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     } else {
         static std::atomic<int> occ{0};
-        k_step8<false><<<step_grid(k_step8<false>, total_chunks, occ), 256, 0, stream>>>(d_tab, d_chunk_begin,
-                                                                                        n_tensors, total_chunks, sc);
+        const RunLaunch L = run_launch(k_step8<false>, total_chunks, occ);
+        k_step8<false><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     }
     return hipGetLastError();
 }
