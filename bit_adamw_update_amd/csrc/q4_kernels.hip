@@ -56,17 +56,47 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as
 // 32x32->64 multiplies with the published multipliers, the key bumped by the
 // published Weyl constants between rounds.  On gfx950 each product is one
 // v_mad_u64_u32 and each three-way XOR one v_bitop3_b32 (truth table 0x96).
+constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
+constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
 __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
     return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
 }
-__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+
+// The counter is (x, step, tensor, stream) with x the only word that differs
+// between elements.  Round 1 multiplies the tensor word and round 2 the word
+// that round 1 made from it and the step, so those two products, and the
+// words that only they and the key feed, are the same for every element of
+// a tensor; philox_fixed forms them once (scalar registers) and philox_from
+// finishes the ten rounds for one x.
+struct PhiloxFixed {
+    uint32_t y1k;   // round 1's y = lo(M1 tensor), xor round 2's k0
+    uint32_t hq0k;  // hi(M0 x1) of round 2, xor round 2's k1
+    uint32_t lq0;   // lo(M0 x1): round 2's w
+};
+__device__ __forceinline__ PhiloxFixed philox_fixed(uint32_t step, uint32_t tid, uint32_t k0, uint32_t k1) {
+    const uint64_t p1 = (uint64_t)kPhiloxM1 * tid;
+    const uint32_t x1 = (uint32_t)(p1 >> 32) ^ step ^ k0;  // round 1's x
+    const uint64_t q0 = (uint64_t)kPhiloxM0 * x1;
+    return {(uint32_t)p1 ^ (k0 + kPhiloxW0), (uint32_t)(q0 >> 32) ^ (k1 + kPhiloxW1), (uint32_t)q0};
+}
+__device__ __forceinline__ uint4 philox_from(uint32_t x, uint32_t stream, const PhiloxFixed& f, uint32_t k0,
+                                             uint32_t k1) {
+    // round 1: z = hi(M0 x) ^ stream ^ k1, w = lo(M0 x)
+    const uint64_t p0 = (uint64_t)kPhiloxM0 * x;
+    const uint32_t z1 = (uint32_t)(p0 >> 32) ^ (stream ^ k1);
+    // round 2: x = hi(M1 z) ^ y ^ k0', y = lo(M1 z), z = hi(M0 x1) ^ w ^ k1', w = lo(M0 x1)
+    const uint64_t p1 = (uint64_t)kPhiloxM1 * z1;
+    uint4 c = make_uint4((uint32_t)(p1 >> 32) ^ f.y1k, (uint32_t)p1, (uint32_t)p0 ^ f.hq0k, f.lq0);
+    // rounds 3 .. 10 with keys k + r W, r = 2 .. 9
+    k0 += 2u * kPhiloxW0;
+    k1 += 2u * kPhiloxW1;
 #pragma unroll
-    for (int r = 0; r < 10; ++r) {
-        if (r) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
-        const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
-        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
-        c = make_uint4(xor3((uint32_t)(p1 >> 32), c.y, k0), (uint32_t)p1, xor3((uint32_t)(p0 >> 32), c.w, k1),
-                       (uint32_t)p0);
+    for (int r = 2; r < 10; ++r) {
+        if (r > 2) { k0 += kPhiloxW0; k1 += kPhiloxW1; }
+        const uint64_t q0 = (uint64_t)kPhiloxM0 * c.x;
+        const uint64_t q1 = (uint64_t)kPhiloxM1 * c.z;
+        c = make_uint4(xor3((uint32_t)(q1 >> 32), c.y, k0), (uint32_t)q1, xor3((uint32_t)(q0 >> 32), c.w, k1),
+                       (uint32_t)q0);
     }
     return c;
 }
@@ -74,9 +104,9 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
 // Element i draws word i mod 4 of Philox(ctr = (i/4, step, tensor, stream)),
 // its top 24 bits scaled by 2^-24.  uniforms4 gives the 4 uniforms of
 // elements 4c .. 4c+3.
-__device__ __forceinline__ void uniforms4(uint32_t c, uint32_t step, uint32_t tid, uint32_t stream, uint32_t k0,
+__device__ __forceinline__ void uniforms4(uint32_t c, uint32_t stream, const PhiloxFixed& f, uint32_t k0,
                                           uint32_t k1, float u[4]) {
-    const uint4 a = philox4x32_10(make_uint4(c, step, tid, stream), k0, k1);
+    const uint4 a = philox_from(c, stream, f, k0, k1);
     const float s = 5.9604644775390625e-8f;  // 2^-24
     u[0] = (float)(a.x >> 8) * s; u[1] = (float)(a.y >> 8) * s;
     u[2] = (float)(a.z >> 8) * s; u[3] = (float)(a.w >> 8) * s;
@@ -199,6 +229,8 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     const gptr<float> mscales = G(T.m_scales) + lc * kBlocksPerChunk;
     const gptr<float> vscales = G(T.v_scales) + lc * kBlocksPerChunk;
     const int lb4 = lane >> 4;  // the lane's block within the chunk
+    // the element-independent part of the stochastic-rounding draws
+    const PhiloxFixed pf = philox_fixed(sc.step, T.tensor_id, sc.key0, sc.key1);
 
     // ---- loads
     float p[8], g[8];
@@ -353,7 +385,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
         float um[4];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            if ((k & 3) == 0) uniforms4((uint32_t)(e0 >> 2) + (k >> 2), sc.step, T.tensor_id, 0u, sc.key0, sc.key1, um);
+            if ((k & 3) == 0) uniforms4((uint32_t)(e0 >> 2) + (k >> 2), 0u, pf, sc.key0, sc.key1, um);
             const float x = fminf(fmaxf(m1[k] * inv_m, -1.0f), 1.0f);
             const int idx = rtn_index(m_entry(x), x);
             const float Lidx = lds.lev_m[idx];
@@ -388,13 +420,19 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     const float s_v = row_max16(av);
     const float inv_v = inv_scale(s_v);
     // lane `sub` holds sqrt(level_sub * s_v): the square root of the state
-    // each level would store, for the preconditioner-space rules
-    const float root_own = V_UPD ? sqrtf(lb.lev_v * s_v) : 0.0f;
+    // each level would store, for the preconditioner-space rules (the short
+    // IEEE form unless some product of the wave is in (0, 2^-96))
+    float root_own = 0.0f;
+    if constexpr (V_UPD) {
+        const float a = lb.lev_v * s_v;
+        if (__builtin_amdgcn_ballot_w64(__float_as_uint(a) - 1u < 0x0F800000u - 1u) != 0) root_own = sqrtf(a);
+        else root_own = sqrt_rn_normal(a);
+    }
     // uniforms of the v rule, drawn 4 at a time (elements 4h .. 4h+3)
     float uv[4];
     auto draw_v = [&](int k) {
         if (V_SR && (k & 3) == 0)
-            uniforms4((uint32_t)(e0 >> 2) + (k >> 2), sc.step, T.tensor_id, 1u, sc.key0, sc.key1, uv);
+            uniforms4((uint32_t)(e0 >> 2) + (k >> 2), 1u, pf, sc.key0, sc.key1, uv);
     };
     uint32_t vword = 0;
     float xx[8], xq[8];
