@@ -90,6 +90,32 @@ def read_traffic(workload_name: str, recipe: str):
         return None
 
 
+# After a process starts, the step runs slow for its first ~35 ms of GPU
+# work while the clocks settle (GPT-2.7B: 5 launches, Llama-1.1B: 10,
+# GPT-162M: ~100), so the untimed warm-up runs the asked-for W steps and
+# then more until WARMUP_MIN_S of steps have run.
+WARMUP_MIN_S = 0.25
+WARMUP_CAP = 4000
+
+
+def warm_up(run_one, warmup: int) -> int:
+    """Runs `warmup` steps, then more until WARMUP_MIN_S have passed on the
+    synchronized clock (at most WARMUP_CAP); returns the number run."""
+    import torch
+
+    t0 = time.perf_counter()
+    for _ in range(warmup):
+        run_one()
+    torch.cuda.synchronize()
+    done = warmup
+    while time.perf_counter() - t0 < WARMUP_MIN_S and done < WARMUP_CAP:
+        for _ in range(max(warmup, 1)):
+            run_one()
+        done += max(warmup, 1)
+        torch.cuda.synchronize()
+    return done
+
+
 def time_workload(workload, recipe: str, steps: int, warmup: int, lm_head_phase: bool = False):
     import torch
 
@@ -105,10 +131,13 @@ def time_workload(workload, recipe: str, steps: int, warmup: int, lm_head_phase:
     stream = torch.cuda.current_stream()
     hp = dict(workload.hp)
     step = 0
-    for _ in range(warmup):
+
+    def one():
+        nonlocal step
         step += 1
         state.step(params, grads, step, lm_head_sr=1 if lm_head_phase else 0, **hp)
-    torch.cuda.synchronize()
+
+    warmup_run = warm_up(one, warmup)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for k in range(steps):
@@ -119,7 +148,8 @@ def time_workload(workload, recipe: str, steps: int, warmup: int, lm_head_phase:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = [a.elapsed_time(b) for a, b in evs]
-    out = {"wall_s": wall, "launch_ms": launch_ms, "state": state, "params": params, "grads": grads}
+    out = {"wall_s": wall, "launch_ms": launch_ms, "state": state, "params": params, "grads": grads,
+           "warmup_run": warmup_run}
     return out
 
 
@@ -148,11 +178,14 @@ def time_step_before(workload, recipe: str, steps: int, warmup: int, max_grad_no
     hp = dict(workload.hp)
     stream = torch.cuda.current_stream()
     step = 0
-    for _ in range(warmup):
+
+    def one():
+        nonlocal step
         state.accumulate(params, grads, micro, first=False, last=True)
         step += 1
         state.step(params, grads, step, grad_stats=True, max_grad_norm=max_grad_norm, **hp)
-    torch.cuda.synchronize()
+
+    warm_up(one, warmup)
     # enqueued back to back, as a training loop would: the events then time
     # the GPU work, not the host's launch overhead
     ev = []
@@ -283,6 +316,7 @@ def main():
     ab = alg_bytes(wl, args.recipe)
     achieved = ab / (avg_launch * 1e-3) / 1e9
     traffic = read_traffic(wl.name, args.recipe)
+    warmup_run = r["warmup_run"]
     del r
     torch.cuda.empty_cache()
     log(f"step {ms_step:.3f} ms wall, fused launch {avg_launch:.3f} ms avg ({min(launch_ms):.3f} min), "
@@ -295,6 +329,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": warmup_run,
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -338,7 +373,7 @@ def main():
                 "gparams_per_s": w2.numel / (v["wall_s"] / args.steps) / 1e9,
                 "step_launch_ms": avg, "alg_gbs": (b2 + extra) / (avg * 1e-3) / 1e9,
                 "frac_of_peak": (b2 + extra) / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                "alg_bytes_per_param": (b2 + extra) / w2.numel}
+                "alg_bytes_per_param": (b2 + extra) / w2.numel, "warmup_run": v["warmup_run"]}
             log(f"{wname}/{rec}: {variants[f'{wname}/{rec}']}")
             del v
             torch.cuda.empty_cache()
