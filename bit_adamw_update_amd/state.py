@@ -57,7 +57,10 @@ class Q4State:
                 if self.cfg.recipe == api.RECIPE_FACTORED and len(b.shape) >= 2:
                     b.kind = "factored"
                     b.v_row = torch.empty(b.shape[0], dtype=torch.float32, device=self.device)
-                    b.v_col = torch.empty(n // b.shape[0], dtype=torch.float32, device=self.device)
+                    cols = 1
+                    for d in b.shape[1:]:
+                        cols *= int(d)
+                    b.v_col = torch.empty(cols, dtype=torch.float32, device=self.device)
                 else:
                     b.kind = "packed"
                     b.v_codes = torch.empty(nc, dtype=torch.uint8, device=self.device)

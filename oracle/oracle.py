@@ -307,7 +307,8 @@ class TensorState:
         self.flags = flags
         n, nb = self.numel, (self.numel + BLOCK - 1) // BLOCK
         self.factored = cfg.recipe == FACTORED and len(self.shape) >= 2
-        self.cols = self.numel // self.shape[0] if self.factored else 0
+        # the matrix viewed as [shape[0], -1]: its columns are the trailing dimensions
+        self.cols = int(np.prod(self.shape[1:])) if self.factored else 0
         self.m32 = self.v32 = self.m_codes = self.m_scales = self.v_codes = self.v_scales = None
         self.R = self.Cc = None
         self.inv_meanR = 0.0
@@ -331,6 +332,8 @@ class TensorState:
             self.v_scales = np.zeros(nb, np.float32)
 
     def step(self, hp: HParams, param: np.ndarray, grad: np.ndarray) -> None:
+        if self.numel == 0:  # no elements: no moments, no statistics to update
+            return
         if self.factored:
             self.inv_meanR = factored_update(hp, self.shape[0], self.cols, grad, self.R, self.Cc)
         step_window(self.cfg, hp, tensor_id=self.tensor_id, flags=self.flags, numel=self.numel, base=0,

@@ -136,7 +136,7 @@ def run(workload: inputs.Workload, recipe: str, steps: int, *, windows=None, dev
     fact = {}
     if recipe == "factored":
         for i, t in enumerate(specs):
-            if len(t.shape) >= 2:
+            if len(t.shape) >= 2 and t.numel > 0:
                 fact[i] = (np.zeros(t.shape[0], np.float32), np.zeros(t.numel // t.shape[0], np.float32))
     rep = Report()
     for step in range(1, steps + 1):

@@ -41,6 +41,19 @@ def test_ragged_shapes(recipe):
     assert rep.codes_differ == 0
 
 
+@pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden", "factored", "fp32"])
+def test_zero_size_tensors_between_others(recipe):
+    """Tensors with no elements first, between others, in a row and last (a
+    vector and a matrix with no rows): the chunk prefixes hold zero-width
+    entries that the kernels' tensor search and run walk step over."""
+    shapes = [(0,), (300,), (0,), (0,), (64, 520), (0, 5), (4097,), (0,)]
+    w = inputs.custom(shapes, grad_kind="masked", seed=24)
+    _flush(f"zero-size tensors {recipe}")
+    rep = parity.run(w, recipe, 4)
+    rep.check()
+    assert rep.codes_differ == 0
+
+
 @pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden"])
 def test_zero_gradient_blocks(recipe):
     """A tensor whose gradient is exactly zero: scales stay 0, codes stay at
