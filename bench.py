@@ -58,11 +58,15 @@ def alg_bytes(workload, recipe: str) -> int:
 
 
 def kernel_hash() -> str:
-    """Hash of the device source of the step kernels."""
+    """Hash of the device source of the step kernels, without its // comments
+    and blank space (so that a comment edit does not orphan the profiles)."""
     h = hashlib.sha256()
     for p in KERNEL_SRC:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(" ".join(code.split()).encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -282,7 +286,8 @@ def main():
                     help="time only the last microbatch's accumulation pass (with the statistics) and the step "
                          "that reuses them, on this workload and recipe (a profiling aid; prints its own JSON line)")
     ap.add_argument("--max-grad-norm", type=float, default=0.0, help="clipping for --step-before")
-    ap.add_argument("--cpu-sample", type=int, default=160_000_000, help="elements in the oracle sample")
+    ap.add_argument("--cpu-sample", type=int, default=480_000_000,
+                    help="elements in the oracle sample (about 12 s of single-threaded oracle work)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

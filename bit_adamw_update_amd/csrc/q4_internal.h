@@ -46,7 +46,7 @@ struct alignas(16) DevTensor {
     float* v32;
     int64_t numel;
     int64_t cols;          // factored matrix: numel / shape[0]; else 0
-    int64_t chunk_begin;   // first chunk of this tensor in the step kernel
+    int64_t chunk_begin;   // first chunk of this tensor in the plain prefix (512 x it = its flat offset)
     const float* inv_meanR;  // factored matrix: slot written by the finalize kernel
     uint32_t tensor_id;
     uint32_t flags;

@@ -18,8 +18,9 @@
 // row-local DPP or ds_bpermute exchange with no LDS traffic.  Each lane
 // moves its parameters as two 16-byte loads, its gradients as one 16-byte
 // load and each moment's 8 codes as one 4-byte load.  One launch covers
-// every tensor: waves walk a grid-stride sequence of tensor-aligned chunks
-// and follow a prefix table of chunk offsets.
+// every tensor: work-groups walk runs of consecutive tensor-aligned chunks
+// (so that each 128-byte line of block scales is written by one group) and
+// follow a prefix table of chunk offsets.
 //
 // Arithmetic is FP32, round-to-nearest-even, with IEEE division and square
 // root, in the order stated for each operation, so that every code decision
