@@ -44,6 +44,8 @@ def alg_bytes(workload, recipe: str) -> int:
     total = 0
     for t in workload.tensors:
         n = t.numel
+        if n == 0:
+            continue
         nb = (n + 127) // 128
         codes = (n + 1) // 2
         if recipe == "fp32":
