@@ -53,65 +53,7 @@ void codebook_table(int cb, float* out) {
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
-// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two
-// 32x32->64 multiplies with the published multipliers, the key bumped by the
-// published Weyl constants between rounds.  On gfx950 each product is one
-// v_mad_u64_u32 and each three-way XOR one v_bitop3_b32 (truth table 0x96).
-constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
-constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
-__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
-    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
-}
-
-// The counter is (x, step, tensor, stream) with x the only word that differs
-// between elements.  Round 1 multiplies the tensor word and round 2 the word
-// that round 1 made from it and the step, so those two products, and the
-// words that only they and the key feed, are the same for every element of
-// a tensor; philox_fixed forms them once (scalar registers) and philox_from
-// finishes the ten rounds for one x.
-struct PhiloxFixed {
-    uint32_t y1k;   // round 1's y = lo(M1 tensor), xor round 2's k0
-    uint32_t hq0k;  // hi(M0 x1) of round 2, xor round 2's k1
-    uint32_t lq0;   // lo(M0 x1): round 2's w
-};
-__device__ __forceinline__ PhiloxFixed philox_fixed(uint32_t step, uint32_t tid, uint32_t k0, uint32_t k1) {
-    const uint64_t p1 = (uint64_t)kPhiloxM1 * tid;
-    const uint32_t x1 = (uint32_t)(p1 >> 32) ^ step ^ k0;  // round 1's x
-    const uint64_t q0 = (uint64_t)kPhiloxM0 * x1;
-    return {(uint32_t)p1 ^ (k0 + kPhiloxW0), (uint32_t)(q0 >> 32) ^ (k1 + kPhiloxW1), (uint32_t)q0};
-}
-__device__ __forceinline__ uint4 philox_from(uint32_t x, uint32_t stream, const PhiloxFixed& f, uint32_t k0,
-                                             uint32_t k1) {
-    // round 1: z = hi(M0 x) ^ stream ^ k1, w = lo(M0 x)
-    const uint64_t p0 = (uint64_t)kPhiloxM0 * x;
-    const uint32_t z1 = (uint32_t)(p0 >> 32) ^ (stream ^ k1);
-    // round 2: x = hi(M1 z) ^ y ^ k0', y = lo(M1 z), z = hi(M0 x1) ^ w ^ k1', w = lo(M0 x1)
-    const uint64_t p1 = (uint64_t)kPhiloxM1 * z1;
-    uint4 c = make_uint4((uint32_t)(p1 >> 32) ^ f.y1k, (uint32_t)p1, (uint32_t)p0 ^ f.hq0k, f.lq0);
-    // rounds 3 .. 10 with keys k + r W, r = 2 .. 9
-    k0 += 2u * kPhiloxW0;
-    k1 += 2u * kPhiloxW1;
-#pragma unroll
-    for (int r = 2; r < 10; ++r) {
-        if (r > 2) { k0 += kPhiloxW0; k1 += kPhiloxW1; }
-        const uint64_t q0 = (uint64_t)kPhiloxM0 * c.x;
-        const uint64_t q1 = (uint64_t)kPhiloxM1 * c.z;
-        c = make_uint4(xor3((uint32_t)(q1 >> 32), c.y, k0), (uint32_t)q1, xor3((uint32_t)(q0 >> 32), c.w, k1),
-                       (uint32_t)q0);
-    }
-    return c;
-}
-
-// Element i draws word i mod 4 of Philox(ctr = (i/4, step, tensor, stream)),
-// its top 24 bits scaled by 2^-24.  uniforms4 gives the 4 uniforms of
-// elements 4c .. 4c+3.
-__device__ __forceinline__ void uniforms4(uint32_t c, uint32_t stream, const PhiloxFixed& f, uint32_t k0,
-                                          uint32_t k1, float u[4]) {
-    const uint4 a = philox_from(c, stream, f, k0, k1);
-    const float s = 5.9604644775390625e-8f;  // 2^-24
-    u[0] = (float)(a.x >> 8) * s; u[1] = (float)(a.y >> 8) * s;
-    u[2] = (float)(a.z >> 8) * s; u[3] = (float)(a.w >> 8) * s;
-}
+// Philox4x32-10 and the uniforms drawn from it are in q4_exact.h.
 
 template <int CTRL> __device__ __forceinline__ float dpp(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));

@@ -269,6 +269,19 @@ template <int C> void launch_quant(uint64_t lo, uint64_t hi, unsigned long long*
     k_quant<C><<<(unsigned)((runs + 255) / 256), 256>>>(lo, hi, bad, first);
 }
 
+__global__ void __launch_bounds__(256) k_philox(const uint32_t* __restrict__ in, uint32_t* __restrict__ out,
+                                                uint32_t n) {
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t* r = in + 6u * i;
+    const q4::PhiloxFixed f = q4::philox_fixed(r[1], r[2], r[4], r[5]);
+    const uint4 w = q4::philox_from(r[0], r[3], f, r[4], r[5]);
+    out[4u * i] = w.x;
+    out[4u * i + 1] = w.y;
+    out[4u * i + 2] = w.z;
+    out[4u * i + 3] = w.w;
+}
+
 struct DevCounters {
     unsigned long long* bad = nullptr;
     uint32_t* first = nullptr;
@@ -384,6 +397,19 @@ int q4st_quant_sweep(int check, uint64_t lo, uint64_t hi, unsigned long long* mi
     }
     e = hipMemcpy(mismatches, c.bad, sizeof(*mismatches), hipMemcpyDeviceToHost);
     if (e == hipSuccess) e = hipMemcpy(first_bad, c.first, sizeof(*first_bad), hipMemcpyDeviceToHost);
+    return (int)e;
+}
+
+// Philox4x32-10 through q4::philox_fixed / philox_from, the form the step
+// kernels use, for n (counter, key) pairs: in (device) holds n rows of
+// {ctr0, ctr1, ctr2, ctr3, key0, key1}, out (device) receives n rows of the
+// 4 output words.  Returns 0, -1 for invalid arguments, or a HIP error code.
+// Synchronous.
+int q4st_philox(const uint32_t* in, uint32_t* out, uint32_t n) {
+    if (!in || !out || n == 0 || n > (1u << 24)) return -1;
+    k_philox<<<(n + 255) / 256, 256>>>(in, out, n);
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipDeviceSynchronize();
     return (int)e;
 }
 

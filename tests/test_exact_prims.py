@@ -8,6 +8,9 @@
     that, for zero and for NaN;
   * the nibble-addressed ds_bpermute decode fetches lane row + code for
     every nibble, and ds_bpermute ignores address bits 0-1 and 8-31;
+  * the kernels' Philox4x32-10 (the element-independent products formed
+    apart, as the kernels form them) gives the published known-answer
+    vectors and the oracle's words on random counters and keys;
   * every round-to-nearest lookup of the step kernels (q4_quant.h: compact
     bucket tables of the five 4-bit maps, the Dyn4 floor table, the flat
     slots of the ZIP-SR kernels, the 8-bit bucket counts) equals the plain
@@ -49,6 +52,8 @@ def _lib():
     lib.q4st_quant_sweep.argtypes = [ctypes.c_int, ctypes.c_uint64, ctypes.c_uint64,
                                      ctypes.POINTER(ctypes.c_ulonglong), ctypes.POINTER(ctypes.c_uint32)]
     lib.q4st_quant_sweep.restype = ctypes.c_int
+    lib.q4st_philox.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32]
+    lib.q4st_philox.restype = ctypes.c_int
     return lib
 
 
@@ -64,7 +69,7 @@ def _sweep(lib, what, form, lo, hi):
 def test_selftest_library_exports_and_validates():
     lib = _lib()
     out = os.popen(f"nm -D --defined-only {build.SELFTEST_PATH}").read()
-    for sym in ("q4st_sweep", "q4st_nibble_decode", "q4st_quant_sweep"):
+    for sym in ("q4st_sweep", "q4st_nibble_decode", "q4st_quant_sweep", "q4st_philox"):
         assert f" T {sym}" in out
     n, first = ctypes.c_ulonglong(0), ctypes.c_uint32(0)
     # rejected before any device call
@@ -74,6 +79,7 @@ def test_selftest_library_exports_and_validates():
     assert lib.q4st_sweep(0, 0, 0, (1 << 32) + 1, ctypes.byref(n), ctypes.byref(first)) == -1
     assert lib.q4st_nibble_decode(1, 6, 0, ctypes.byref(n)) == -1
     assert lib.q4st_nibble_decode(1, 0, 0, ctypes.byref(n)) == -1
+    assert lib.q4st_philox(None, None, 1) == -1
     assert lib.q4st_quant_sweep(len(QUANT_CHECKS) + 1, 0, 1, ctypes.byref(n), ctypes.byref(first)) == -1
     # outside [+0, 1], and the negative half for an unsigned map
     assert lib.q4st_quant_sweep(0, 0, ONE + 2, ctypes.byref(n), ctypes.byref(first)) == -1
@@ -137,3 +143,31 @@ def test_round_to_nearest_sweep_sees_single_inputs():
         assert lib.q4st_quant_sweep(len(QUANT_CHECKS), lo, hi, ctypes.byref(n), ctypes.byref(first)) == 0
         total += n.value
     assert total == 15
+
+
+@pytest.mark.gpu
+def test_philox_known_answers_and_oracle():
+    import numpy as np
+    import torch
+
+    from oracle import oracle as O
+    golden = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.txt")
+    kat = [[int(x, 16) for x in l.split()] for l in open(golden) if l.strip() and not l.startswith("#")]
+    rng = np.random.default_rng(7)
+    rand = rng.integers(0, 2 ** 32, size=(1 << 16, 6), dtype=np.uint64).astype(np.uint32)
+    rows = np.concatenate([np.array([r[:6] for r in kat], np.uint32), rand])
+    dev_in = torch.from_numpy(rows.view(np.int32).copy()).cuda()
+    dev_out = torch.empty((rows.shape[0], 4), dtype=torch.int32, device="cuda")
+    assert lib_call(_lib().q4st_philox, dev_in.data_ptr(), dev_out.data_ptr(), rows.shape[0]) == 0
+    got = dev_out.cpu().numpy().view(np.uint32)
+    for k, r in enumerate(kat):
+        assert got[k].tolist() == r[6:10], f"known-answer vector {k}"
+    for k in range(len(kat), rows.shape[0]):
+        assert np.array_equal(got[k], O.philox(rows[k, :4], rows[k, 4:6])), f"row {k}: {rows[k]}"
+
+
+def lib_call(fn, *args):
+    import torch
+    rc = fn(*args)
+    torch.cuda.synchronize()
+    return rc
