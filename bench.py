@@ -311,9 +311,12 @@ def main():
     log(f"{wl.name}: {n:,} params in {len(wl.tensors)} tensors, recipe {args.recipe}")
     if args.step_before:
         acc_ms, st_ms = time_step_before(wl, args.recipe, args.steps, args.warmup, max_grad_norm=args.max_grad_norm)
+        torch.cuda.empty_cache()
         print(json.dumps({"workload": wl.name, "recipe": args.recipe, "params": n, "steps": args.steps,
                           "accumulate_ms": acc_ms, "accumulate_gbs": 6 * n / (acc_ms * 1e-3) / 1e9,
-                          "step_ms": st_ms, "max_grad_norm": args.max_grad_norm}), flush=True)
+                          "step_ms": st_ms, "max_grad_norm": args.max_grad_norm,
+                          # the same 4 GiB copy as the main run (counter calibration for profiles)
+                          "copy_ceiling_gbs": copy_ceiling_gbs()}), flush=True)
         return
     r = time_workload(wl, args.recipe, args.steps, args.warmup,
                       lm_head_phase=wl.lm_head_switch)
