@@ -123,7 +123,9 @@ typedef struct {
 
 #define Q4_HP_REUSE_TABLE 1u      /* the workspace already holds this exact tensor list from the previous
                                      q4adamw_step or q4adamw_accumulate with the same configuration: skip
-                                     its upload */
+                                     its upload.  The call then enqueues kernel launches only (no copy, no
+                                     allocation, no synchronization), so it may be captured in a HIP graph
+                                     once an earlier call on the device has run */
 #define Q4_HP_CHECK_POINTERS 2u   /* also check that every pointer lives on the current device */
 #define Q4_HP_GRAD_STATS 4u       /* the workspace holds the statistics of exactly these gradients, left by
                                      q4adamw_accumulate (Q4_ACC_LAST) or q4adamw_grad_stats with this
