@@ -85,6 +85,11 @@ VARIANTS = [
     (q4.CB_SDYN4, q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 1),
     (q4.CB_SDYN4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_SR, 0),
     (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_SR, q4.RULE_UPDATE_SR, 0),
+    # EDEN on the ZIP-SR kernel: its generic v branch (compact tables, EDEN
+    # sums) instead of the flat-table one
+    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_SR, 1),
+    # m by state-space SR on every tensor in a kernel with compact tables
+    (q4.CB_NF4, q4.CB_DYN4_NZ, q4.RULE_STATE_SR, q4.RULE_STATE_RTN, 1),
 ]
 
 
@@ -252,13 +257,15 @@ def test_edge_magnitudes(recipe):
     assert rep.codes_differ == 0
 
 
-def test_edge_magnitudes_lm_head_phase():
+@pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden", "factored"])
+def test_edge_magnitudes_lm_head_phase(recipe):
     """The edge-magnitude blocks on a tensor flagged as the LM head, with the
     final-phase switch: its m takes state-space SR (Philox stream 0) on the
-    last of 10 steps."""
+    last of 10 steps.  ZIP-SR finds the level through its flat table, the
+    other recipes through the compact ones."""
     w = inputs.custom([(7 * 128 * 3 + 77,), (21, 140)], grad_kind="edge", seed=53, flags=[inputs.TF_LM_HEAD, 0])
-    _flush("edge magnitudes zip_sr + LM-head phase")
-    rep = parity.run(w, "zip_sr", 10, lm_head_phase=True)
+    _flush(f"edge magnitudes {recipe} + LM-head phase")
+    rep = parity.run(w, recipe, 10, lm_head_phase=True)
     rep.check()
     assert rep.codes_differ == 0
 
