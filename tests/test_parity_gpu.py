@@ -270,6 +270,25 @@ def test_edge_magnitudes_lm_head_phase(recipe):
     assert rep.codes_differ == 0
 
 
+def test_factored_matrix_beyond_2_32_elements():
+    """A factored matrix of 65,537 x 65,539 elements (4.3e9, past 2^32) and
+    a vector: the fused step's 64-bit row division for chunks that start
+    past 2^32, K2's row/column statistics over every element (R and C
+    compared in full each step), codes and weights on windows around 2^31,
+    2^32 and both ends."""
+    rows, cols = 65537, 65539
+    n = rows * cols
+    w = inputs.custom([(rows, cols), (1000,)], grad_kind="masked", seed=28)
+    nb = (n + 127) // 128
+    lo32 = (1 << 32) // 128
+    lo31 = (1 << 31) // 128
+    wins = [(0, 0, 2), (0, lo31 - 2, lo31 + 2), (0, lo32 - 3, lo32 + 3), (0, nb - 3, nb), (1, 0, 8)]
+    _flush("factored 65537 x 65539")
+    rep = parity.run(w, "factored", 2, windows=wins, grads_on="cuda")
+    rep.check()
+    assert rep.codes_differ == 0
+
+
 def test_tensor_beyond_2_32_elements():
     """One tensor of 2^32 + 1000 elements (17 GB of FP32 masters): 64-bit
     element indices, Philox counters past 2^32 / 4, a ragged last block."""
