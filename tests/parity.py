@@ -21,6 +21,25 @@ import bit_adamw_update_amd as q4
 from bit_adamw_update_amd import inputs
 from oracle import oracle as O
 
+# The codebook/rule variants run on the GPU: (m codebook, v codebook, m rule,
+# v rule, eden).  The first eight are the component grid of [P] Tables 1, 3
+# and 8; the last two reach branches no recipe takes.
+VARIANTS = [
+    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 0),
+    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_STATE_SR, 0),
+    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_RTN, 0),
+    (q4.CB_NF4, q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 0),
+    (q4.CB_SDYN4, q4.CB_LIN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 0),
+    (q4.CB_SDYN4, q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 1),
+    (q4.CB_SDYN4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_SR, 0),
+    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_SR, q4.RULE_UPDATE_SR, 0),
+    # EDEN on the ZIP-SR kernel: its generic v branch (compact tables, EDEN
+    # sums) instead of the flat-table one
+    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_SR, 1),
+    # m by state-space SR on every tensor in a kernel with compact tables
+    (q4.CB_NF4, q4.CB_DYN4_NZ, q4.RULE_STATE_SR, q4.RULE_STATE_RTN, 1),
+]
+
 ORACLE_RECIPE = {"zip_sr": O.ZIP_SR, "ze_eden": O.ZE_EDEN, "factored": O.FACTORED, "fp32": O.FP32}
 W_TOL = 1e-6
 RC_TOL = 1e-6

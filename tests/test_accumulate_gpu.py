@@ -54,10 +54,10 @@ def host_accumulate(w, micro, offsets):
     return acc
 
 
-def setup(recipe, seed=31, shapes=SHAPES):
+def setup(recipe, seed=31, shapes=SHAPES, cfg=None):
     w = inputs.custom(shapes, grad_kind="masked", seed=seed)
     dev = torch.device("cuda")
-    st = q4.Q4State(recipe, w.tensors, dev)
+    st = q4.Q4State(recipe, w.tensors, dev, cfg=cfg)
     params = [p.to(dev).reshape(-1).contiguous() for p in w.init_params("cpu")]
     grads = [torch.full((t.numel,), 7.0, dtype=torch.bfloat16, device=dev) for t in w.tensors]  # stale values
     offsets, total = st.flat_offsets()
@@ -83,16 +83,27 @@ def test_accumulation_and_norm_match_oracle(recipe):
     assert abs(st.grad_norm() - ref) <= 1e-12 * ref
 
 
-@pytest.mark.parametrize("recipe,shapes", [("zip_sr", SHAPES), ("ze_eden", SHAPES), ("factored", SHAPES),
-                                           ("fp32", SHAPES), ("zip_sr", SHAPES_WITH_EMPTY),
-                                           ("factored", SHAPES_WITH_EMPTY)])
-def test_clipped_steps_match_oracle(recipe, shapes):
+def _variant_cfg(variant):
+    cfg = q4.q4adamw_default_config(q4.RECIPE_CUSTOM)
+    cfg.m_codebook, cfg.v_codebook, cfg.m_rule, cfg.v_rule, cfg.eden = variant
+    return cfg
+
+
+CLIP_CASES = [("zip_sr", SHAPES, None), ("ze_eden", SHAPES, None), ("factored", SHAPES, None), ("fp32", SHAPES, None),
+              ("zip_sr", SHAPES_WITH_EMPTY, None), ("factored", SHAPES_WITH_EMPTY, None)]
+# the clipped kernel of every codebook/rule variant
+CLIP_CASES += [("custom", SHAPES, v) for v in parity.VARIANTS]
+
+
+@pytest.mark.parametrize("recipe,shapes,variant", CLIP_CASES)
+def test_clipped_steps_match_oracle(recipe, shapes, variant):
     """Five steps, each: four microbatches accumulated on the GPU, then a step
     with the statistics of the last pass and clipping to a norm below the
     gradients' (so every step clips)."""
-    w, st, params, grads, offsets, total = setup(recipe, seed=32, shapes=shapes)
-    _flush(f"clipped steps {recipe} {len(shapes)} tensors")
-    ocfg = parity.oracle_config(recipe)
+    cfg = _variant_cfg(variant) if variant is not None else None
+    w, st, params, grads, offsets, total = setup(recipe, seed=32, shapes=shapes, cfg=cfg)
+    _flush(f"clipped steps {recipe} {variant} {len(shapes)} tensors")
+    ocfg = parity.oracle_config(recipe, cfg)
     ost = [O.TensorState(ocfg, t.shape, t.tensor_id, t.flags) for t in w.tensors]
     op = [p.cpu().numpy().copy() for p in params]
     max_norm = 2e-3

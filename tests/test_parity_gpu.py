@@ -76,21 +76,7 @@ def test_lm_head_switch_final_phase():
     assert rep.codes_differ == 0
 
 
-VARIANTS = [
-    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 0),
-    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_STATE_SR, 0),
-    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_RTN, 0),
-    (q4.CB_NF4, q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 0),
-    (q4.CB_SDYN4, q4.CB_LIN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 0),
-    (q4.CB_SDYN4, q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 1),
-    (q4.CB_SDYN4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_SR, 0),
-    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_SR, q4.RULE_UPDATE_SR, 0),
-    # EDEN on the ZIP-SR kernel: its generic v branch (compact tables, EDEN
-    # sums) instead of the flat-table one
-    (q4.CB_NF4, q4.CB_DYN4, q4.RULE_STATE_RTN, q4.RULE_UPDATE_SR, 1),
-    # m by state-space SR on every tensor in a kernel with compact tables
-    (q4.CB_NF4, q4.CB_DYN4_NZ, q4.RULE_STATE_SR, q4.RULE_STATE_RTN, 1),
-]
+VARIANTS = parity.VARIANTS
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
