@@ -159,16 +159,18 @@ def test_determinism_and_resume():
             assert torch.equal(getattr(a, f), getattr(d, f))
 
 
-@pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden", "factored"])
-def test_dequant_matches_oracle(recipe):
+@pytest.mark.parametrize("recipe,variant", [("zip_sr", None), ("ze_eden", None), ("factored", None)]
+                         + [("custom", v) for v in parity.VARIANTS])
+def test_dequant_matches_oracle(recipe, variant):
     w = inputs.custom([(3000,), (48, 200)], grad_kind="masked", seed=26)
     dev = torch.device("cuda")
     from oracle import oracle as O
+    cfg = _variant_cfg(variant) if variant is not None else None
     params = w.init_params("cpu")
     consts = w._tensor_consts("cpu")
     gp = [p.to(dev).reshape(-1).contiguous() for p in params]
-    st = q4.Q4State(recipe, w.tensors, dev)
-    ost = [O.TensorState(parity.oracle_config(recipe), t.shape, t.tensor_id) for t in w.tensors]
+    st = q4.Q4State(recipe, w.tensors, dev, cfg=cfg)
+    ost = [O.TensorState(parity.oracle_config(recipe, cfg), t.shape, t.tensor_id) for t in w.tensors]
     op = [p.numpy().reshape(-1).copy() for p in params]
     for s in range(1, 4):
         g = w.grads(s, "cpu", consts)
