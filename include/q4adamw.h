@@ -141,8 +141,8 @@ typedef struct {
  *   m_codes  uint8[ceil(n/2)], m_scales float[NB]   packed 4-bit m + block scales (in place)
  *   v_codes  uint8[ceil(n/2)], v_scales float[NB]   packed 4-bit v + block scales (in place;
  *                                                    NULL for a factored matrix)
- *   v_row    float[shape[0]], v_col float[n/shape[0]] factored matrix only: EMA of the row and
- *                                                    column means of g^2 (in place)
+ *   v_row    float[shape[0]], v_col float[prod(shape[1:])]  factored matrix only: EMA of the row
+ *                                                    and column means of g^2 (in place)
  *   m_fp32, v_fp32 float[n]  FP32 recipe only (in place)
  * Codes: element 2j in the low nibble of byte j, element 2j+1 in the high
  * nibble (0 when n is odd).  Q4_RECIPE_BLOCK8: m_codes and v_codes are
