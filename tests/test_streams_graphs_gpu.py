@@ -82,3 +82,27 @@ def test_step_in_a_hip_graph_replays_like_eager(recipe):
         sa.step(pa, grads, 3, **w.hp)
         torch.cuda.synchronize()
         _same(pa, sa, pb, sb, f"{recipe} replay {r}")
+
+
+def test_pointer_checks_refuse_host_memory_before_any_work():
+    """With Q4_HP_CHECK_POINTERS a step whose master weights live in host
+    memory is refused (Q4_ERR_DEVICE) before anything is enqueued: a twin
+    state that never saw the refused call stays bit-identical."""
+    w = inputs.custom([(1000,), (64, 130)], grad_kind="masked", seed=29)
+    dev = torch.device("cuda")
+    consts = w._tensor_consts("cpu")
+    pa, sa = _make(w, "zip_sr", dev)
+    pb, sb = _make(w, "zip_sr", dev)
+    g1 = [g.to(dev).reshape(-1).contiguous() for g in w.grads(1, "cpu", consts)]
+    sa.step(pa, g1, 1, flags=q4.HP_CHECK_POINTERS, **w.hp)
+    sb.step(pb, g1, 1, **w.hp)
+    torch.cuda.synchronize()
+    host = [pb[0].cpu(), pb[1]]
+    with pytest.raises(q4.Q4Error) as e:
+        sb.step(host, g1, 2, flags=q4.HP_CHECK_POINTERS, **w.hp)
+    assert e.value.status == 6
+    g2 = [g.to(dev).reshape(-1).contiguous() for g in w.grads(2, "cpu", consts)]
+    sa.step(pa, g2, 2, **w.hp)
+    sb.step(pb, g2, 2, **w.hp)
+    torch.cuda.synchronize()
+    _same(pa, sa, pb, sb, "after a refused call")
