@@ -168,6 +168,38 @@ def test_statistics_inside_the_step_equal_the_accumulated_ones(recipe):
                 assert torch.equal(getattr(a, f), getattr(b, f)), f
 
 
+@pytest.mark.parametrize("recipe", ["zip_sr", "factored"])
+def test_single_microbatch_is_first_and_last(recipe):
+    """One microbatch per step (first and last in one call): the gradients
+    equal the microbatch, the norm the oracle's, and the clipped steps that
+    reuse these statistics equal steps that gather their own, bit for bit.
+    For the factored matrices this is the tile kernel's copying mode."""
+    results = []
+    for mode in ("accumulated", "inside"):
+        w, st, params, grads, offsets, total = setup(recipe, seed=34)
+        for s in range(1, 4):
+            flat = microbatches(w, s, offsets, total, seed=4)[0]
+            m = torch.from_numpy(flat.view(np.int16)).view(torch.bfloat16).cuda()
+            st.accumulate(params, grads, m, first=True, last=(mode == "accumulated"))
+            if mode == "accumulated":
+                for i, t in enumerate(w.tensors):
+                    assert np.array_equal(grads[i].view(torch.uint16).cpu().numpy(),
+                                          flat[offsets[i]: offsets[i] + t.numel]), f"step {s} tensor {i}"
+                ref = np.sqrt(sum(O.grad_sumsq(flat[offsets[i]: offsets[i] + t.numel].copy())
+                                  for i, t in enumerate(w.tensors)))
+                assert abs(st.grad_norm() - ref) <= 1e-12 * ref
+            st.step(params, grads, s, grad_stats=(mode == "accumulated"), max_grad_norm=2e-3, **w.hp)
+        torch.cuda.synchronize()
+        results.append((params, st))
+    (pa, sa), (pb, sb) = results
+    for x, y in zip(pa, pb):
+        assert torch.equal(x.view(torch.int32), y.view(torch.int32))
+    for a, b in zip(sa.bufs, sb.bufs):
+        for f in ("m_codes", "m_scales", "v_codes", "v_scales", "v_row", "v_col"):
+            if getattr(a, f) is not None:
+                assert torch.equal(getattr(a, f), getattr(b, f)), f
+
+
 def test_gpt_2_7b_accumulation_and_clipped_step_sampled():
     """The GPT-style 2.7B set in the launch configuration the benchmark times
     for the step before: one accumulation pass with the statistics, then a
