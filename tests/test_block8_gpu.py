@@ -90,6 +90,13 @@ def test_zero_size_tensors_between_others():
     run_windows(inputs.custom(shapes, grad_kind="masked", seed=43), 4)
 
 
+def test_two_thousand_small_tensors():
+    rng = np.random.default_rng(30)
+    shapes = [(int(rng.integers(1, 1501)),) for _ in range(2000)]
+    _flush("block8 2000 small tensors")
+    run_windows(inputs.custom(shapes, grad_kind="masked", seed=44), 3)
+
+
 def test_clipped_steps():
     _flush("block8 clipped")
     run_windows(inputs.custom([(3000,), (64, 200)], grad_kind="masked", seed=42), 4, clip=2e-3)

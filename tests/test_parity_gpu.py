@@ -54,6 +54,28 @@ def test_zero_size_tensors_between_others(recipe):
     assert rep.codes_differ == 0
 
 
+@pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden", "factored", "fp32"])
+def test_two_thousand_small_tensors(recipe):
+    """2,000 tensors of 1 to 1,500 elements (vectors and small matrices):
+    most step-prefix chunks only align the next tensor, a run of slabs spans
+    dozens of tensors, and the tensor search walks a long prefix; every
+    element over 3 steps."""
+    rng = np.random.default_rng(30)
+    shapes = []
+    for k in range(2000):
+        n = int(rng.integers(1, 1501))
+        if k % 3 == 2 and n >= 4:
+            r = int(rng.integers(1, 9))
+            shapes.append((r, max(1, n // r)))
+        else:
+            shapes.append((n,))
+    w = inputs.custom(shapes, grad_kind="masked", seed=31)
+    _flush(f"2000 small tensors {recipe}")
+    rep = parity.run(w, recipe, 3)
+    rep.check()
+    assert rep.codes_differ == 0
+
+
 @pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden"])
 def test_zero_gradient_blocks(recipe):
     """A tensor whose gradient is exactly zero: scales stay 0, codes stay at
