@@ -176,6 +176,10 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     const PhiloxFixed pf = philox_fixed(sc.step, T.tensor_id, sc.key0, sc.key1);
 
     // ---- loads
+    // While a wave issues its loads it runs at raised priority, so the
+    // memory pipe is refilled before other waves' arithmetic.  Memory-bound
+    // rules gain from it; the VALU-bound flat-table (ZIP-SR) kernel does not.
+    if constexpr (!FLAT) __builtin_amdgcn_s_setprio(2);
     float p[8], g[8];
     uint32_t mc = 0, vc = 0;
     if (FULL || nv == 8) {
@@ -210,6 +214,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     }
     const float sm_old = (FULL || blk_ok) ? mscales[lb4] : 0.0f;
     const float sv_old = ((FULL || blk_ok) && packed_v) ? vscales[lb4] : 0.0f;
+    if constexpr (!FLAT) __builtin_amdgcn_s_setprio(0);
     // lane `sub` of the row holds level(sub) * old scale: decoding is one
     // ds_bpermute per element (the same product the definition forms)
     const float dm_own = lb.dec_m * sm_old;
@@ -628,6 +633,8 @@ __device__ __forceinline__ void step8_chunk(const DevTensor& T, const int64_t lc
     const gptr<float> mscales = G(T.m_scales);
     const gptr<float> vscales = G(T.v_scales);
 
+    // loads at raised wave priority, as in the 4-bit step
+    __builtin_amdgcn_s_setprio(2);
     float p[8], g[8];
     uint32_t mc[2] = {0u, 0u}, vc[2] = {0u, 0u};
     if (FULL || nv == 8) {
@@ -659,6 +666,7 @@ __device__ __forceinline__ void step8_chunk(const DevTensor& T, const int64_t lc
     }
     const float sm_old = (FULL || blk_ok) ? mscales[blk] : 0.0f;
     const float sv_old = (FULL || blk_ok) ? vscales[blk] : 0.0f;
+    __builtin_amdgcn_s_setprio(0);
 
     float m1[8], v1[8];
 #pragma unroll
