@@ -75,9 +75,13 @@ _lib = None
 
 
 def lib():
+    """The oracle library: the build above, or the file named by the
+    Q4_ORACLE_LIB environment variable (the tests point it at a build made
+    with sanitizers, or at a copy with a mistake planted in it, to show that
+    the pins catch it)."""
     global _lib
     if _lib is None:
-        L = C.CDLL(build())
+        L = C.CDLL(os.environ.get("Q4_ORACLE_LIB") or build())
         fp, vp, i32, u32, u64, i64 = (C.POINTER(C.c_float), C.c_void_p, C.c_int, C.c_uint32, C.c_uint64,
                                       C.c_int64)
         L.or_codebook.argtypes = [i32, fp]

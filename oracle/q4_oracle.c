@@ -330,12 +330,20 @@ static float or_pairwise(const float* x, int n) {
     return or_pairwise(x, h) + or_pairwise(x + h, n - h);
 }
 
-/* Inverse of a block scale for normalization, x = value * (1/s).  A zero
- * block normalizes to x = 0 (reading of zero blocks); so does a block whose
- * scale is below the smallest normal float (reading of subnormal scales:
- * its reciprocal may overflow, and 0 * inf would not be 0).  The scale
- * itself is stored as computed. */
-static float or_scale_inverse(float s) { return s >= 0x1p-126f ? 1.0f / s : 0.0f; }
+/* Inverse of a block scale for normalization, x = value * (1/s), with 1/s
+ * the IEEE quotient ([A] "State representation": absmax-normalized blocks).
+ * A zero block normalizes to x = 0 (reading of zero blocks).  A positive
+ * scale whose reciprocal overflows to +inf (s <= 2^-128, a subnormal) has
+ * no usable normalization: value * inf is infinite, and NaN for a zero
+ * value, which no level represents.  Such a block is normalized like a zero
+ * block (reading of overflowing inverses), so every slot stores the code of
+ * zero; the scale itself is stored as computed.  A subnormal scale whose
+ * reciprocal is finite normalizes as any other. */
+static float or_scale_inverse(float s) {
+    if (!(s > 0.0f)) return 0.0f;
+    const float inv = 1.0f / s;
+    return isinf(inv) ? 0.0f : inv;
+}
 
 /* First moment of one block: absmax scale, normalization, then RTN or
  * state-space SR (the LM-head rule of [P] Table 2) over the signed map.

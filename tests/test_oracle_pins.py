@@ -278,6 +278,25 @@ def test_zero_cell_update_sr_rarely_stores_zero():
 # RTN, state-space SR, EDEN, packing
 # ---------------------------------------------------------------------------
 
+@pytest.mark.parametrize("cb,moment", [(O.CB_NF4, "m"), (O.CB_SDYN4, "m"), (O.CB_DYN4, "v"),
+                                       (O.CB_DYN4_NZ, "v"), (O.CB_LIN4_NZ, "v")])
+def test_rtn_ties_go_to_the_lower_level(cb, moment):
+    """Reading of round-to-nearest ties (the pages fix none): a normalized
+    value equal to the FP32 midpoint (L_k + L_k+1) * 0.5 stores level k, and
+    the next float above it stores level k + 1."""
+    L, code, mid = O.sorted_levels(cb)
+    for k, md in enumerate(mid):
+        above = np.nextafter(md, np.float32(2))
+        vals = np.array([1.0, md, above], np.float32)   # the block max is 1, so x = value
+        if moment == "m":
+            codes, s = O.requant_m_block(cb, O.STATE_RTN, vals)
+        else:
+            codes, s = O.requant_v_block(cb, O.STATE_RTN, 0, vals)
+        assert s == 1.0
+        got = O.unpack(codes, 3)
+        assert got[1] == code[k] and got[2] == code[k + 1], (k, md)
+
+
 @pytest.mark.parametrize("cb", [O.CB_NF4, O.CB_SDYN4])
 def test_m_rtn_is_nearest_level(cb):
     rng = np.random.default_rng(0)
@@ -700,29 +719,58 @@ def test_8bit_first_step_rounds_to_the_nearest_level_and_matches_fp32():
             assert np.all(np.abs(table[codes[b * 128: b * 128 + blk.size]] - x) <= np.diff(L).max() / 2 + 1e-7)
 
 
-def test_subnormal_block_scales_normalize_to_zero():
-    """Reading of subnormal scales: a block whose scale is below the smallest
-    normal float stores the code of zero in every slot (its reciprocal may
-    overflow, and 0 * inf is not 0) and keeps the scale as computed; the next
-    block, of normal values, is quantized as usual.  4-bit and 8-bit states.
-    (Here 1/s is still finite, so a plain x = m1 * (1/s) would spread the
-    block over many codes.)"""
+def _rtn_codes(x, cb8=None, cb=None):
+    """Round to nearest by brute force: the count of FP32 midpoints strictly
+    below x (an exact midpoint goes to the lower level), as a code."""
+    if cb8 is not None:
+        L, code, mid = O.sorted_levels8(cb8)
+    else:
+        L, code, mid = O.sorted_levels(cb)
+    idx = (x[:, None] > mid[None, :]).sum(axis=1)
+    return np.asarray(code)[idx]
+
+
+def test_subnormal_block_scales_follow_the_reciprocal():
+    """Normalization divides a block by its scale through x = m1 * (1/s).
+    A subnormal scale whose IEEE reciprocal is finite (s > 2^-128) normalizes
+    exactly like any other: the codes are the nearest levels of
+    x = m1 * fl(1/s), spread over the map.  A scale whose reciprocal
+    overflows (s <= 2^-128) has no usable normalization (m1 * inf is
+    infinite, 0 * inf is NaN), so its block stores the code of zero in every
+    slot, as a zero block does.  The scale is stored as computed either way.
+    4-bit and 8-bit states; the third block, of normal values, is plain."""
     import torch
     g = torch.Generator().manual_seed(61)
-    x = torch.randn(256, generator=g)
-    grad = torch.cat([x[:128] * 2e-38, x[128:] * 1e-3]).to(torch.bfloat16).view(torch.uint16).numpy().copy()
+    x = torch.randn(384, generator=g)
+    x = x / x.abs().max()
+    # m1 = fl((1 - b1) g) at step 1 from the zero state: block 0 peaks near
+    # 6e-39 (reciprocal finite), block 1 near 1.5e-39 (reciprocal overflows)
+    grad = torch.cat([x[:128] * 6e-38, x[128:256] * 1.5e-38, x[256:] * 1e-3])
+    grad = grad.to(torch.bfloat16).view(torch.uint16).numpy().copy()
+    g32 = (grad.astype(np.uint32) << 16).view(np.float32)
     hp = O.HParams(step=1)
-    tiny = np.float32(2.0 ** -126)
+    omb1 = np.float32(1) - np.float32(hp.beta1)
+    m1 = omb1 * g32                         # FP32 products, subnormals kept
+    s = [np.float32(np.abs(m1[b * 128:(b + 1) * 128]).max()) for b in range(3)]
+    with np.errstate(over="ignore"):
+        inv = [np.float32(1) / v for v in s]
+    assert 2.0 ** -128 < s[0] < 2.0 ** -126 and np.isfinite(inv[0])
+    assert 0 < s[1] <= 2.0 ** -128 and np.isinf(inv[1])
     for recipe in (O.ZIP_SR, O.ZE_EDEN):
         cfg = O.Config.of(recipe)
-        st = O.TensorState(cfg, (256,), 3)
-        st.step(hp, np.zeros(256, np.float32), grad)
-        c = O.unpack(st.m_codes, 256)
-        assert 0 < st.m_scales[0] < tiny and np.isfinite(np.float32(1) / st.m_scales[0])
-        assert np.all(c[:128] == O.zero_code(cfg.m_cb))
-        assert len(set(c[128:].tolist())) > 4
-    st8 = O.TensorState8((256,), 3)
-    st8.step(hp, np.zeros(256, np.float32), grad)
-    assert 0 < st8.m_scales[0] < tiny
-    assert np.all(st8.m_codes[:128] == 0)
-    assert len(set(st8.m_codes[128:].tolist())) > 4
+        st = O.TensorState(cfg, (384,), 3)
+        st.step(hp, np.zeros(384, np.float32), grad)
+        c = O.unpack(st.m_codes, 384)
+        assert [f32_bits(v) for v in st.m_scales] == [f32_bits(v) for v in s]
+        x0 = np.clip(m1[:128] * inv[0], -1, 1)
+        assert np.array_equal(c[:128], _rtn_codes(x0, cb=cfg.m_cb))
+        assert len(set(c[:128].tolist())) > 4
+        assert np.all(c[128:256] == O.zero_code(cfg.m_cb))
+        assert len(set(c[256:].tolist())) > 4
+    st8 = O.TensorState8((384,), 3)
+    st8.step(hp, np.zeros(384, np.float32), grad)
+    assert [f32_bits(v) for v in st8.m_scales] == [f32_bits(v) for v in s]
+    x0 = np.clip(m1[:128] * inv[0], -1, 1)
+    assert np.array_equal(st8.m_codes[:128], _rtn_codes(x0, cb8=O.CB8_SDYN8))
+    assert np.all(st8.m_codes[128:256] == 0)
+    assert len(set(st8.m_codes[256:].tolist())) > 4
