@@ -17,7 +17,6 @@ parameter sets for context.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import statistics
@@ -29,7 +28,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "G params updated/sec for fused 4-bit AdamW step; HBM GB/s vs 8 TB/s peak"
 HBM_PEAK_GBS = 8000.0
-KERNEL_SRC = [os.path.join(ROOT, "bit_adamw_update_amd", "csrc", f) for f in ("q4_kernels.hip", "q4_exact.h", "q4_quant.h")]
+COPY_PROBE_BYTES = 4 << 30     # the hand-written copy probe (also the counters' calibration)
+READ_PROBE_BYTES = 8 << 30
+PROBE_LAUNCHES = 10
 
 
 def log(msg):
@@ -60,21 +61,14 @@ def alg_bytes(workload, recipe: str) -> int:
 
 
 def kernel_hash() -> str:
-    """Hash of the device source of the step kernels, without its // comments
-    and blank space (so that a comment edit does not orphan the profiles)."""
-    h = hashlib.sha256()
-    for p in KERNEL_SRC:
-        with open(p, encoding="utf-8") as f:
-            for line in f:
-                code = line.split("//", 1)[0].strip()
-                if code:
-                    h.update(" ".join(code.split()).encode() + b"\n")
-    return h.hexdigest()[:16]
+    from bit_adamw_update_amd.profiling import kernel_hash as h
+    return h()
 
 
 def step_kernel(recipe: str) -> str:
     """The kernel that dominates a recipe's step."""
-    return {"block8": "k_step8", "fp32": "k_fp32_step"}.get(recipe, "k_fused_step")
+    from bit_adamw_update_amd.profiling import step_kernel as k
+    return k(recipe)
 
 
 def read_traffic(workload_name: str, recipe: str):
@@ -210,56 +204,89 @@ def time_step_before(workload, recipe: str, steps: int, warmup: int, max_grad_no
     return sum(acc_ms) / len(acc_ms), sum(step_ms) / len(step_ms)
 
 
-def copy_ceiling_gbs(nbytes: int = 4 << 30) -> float:
-    """A plain device copy of the same order of bytes: the practical ceiling."""
+def _time_launches(fn, launches: int) -> float:
+    """Average ms of `launches` back-to-back calls on the current stream
+    (HIP events), after two untimed calls."""
     import torch
-    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-    b = torch.empty_like(a)
-    for _ in range(3):
-        b.copy_(a)
+    for _ in range(2):
+        fn()
     torch.cuda.synchronize()
     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     s.record()
-    for _ in range(10):
-        b.copy_(a)
+    for _ in range(launches):
+        fn()
     e.record()
     torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / 10
+    return s.elapsed_time(e) / launches
+
+
+def probe_ceilings(n_elems: int) -> dict:
+    """The practical ceilings of this machine, from the hand-written probes of
+    libq4probe.so: the step's byte mix (12.125 B per element, the step's lane
+    layout and work-group walk, trivial arithmetic) over as many elements as
+    the workload has (rounded up to 512), a plain copy and a read."""
+    import torch
+
+    from bit_adamw_update_amd import probe
+    n = (n_elems + 511) // 512 * 512
+    bm = probe.ByteMix(n)
+    ms = _time_launches(bm.run, PROBE_LAUNCHES)
+    out = {"byte_mix_ceiling_gbs": probe.byte_mix_bytes(n) / (ms * 1e-3) / 1e9, "byte_mix_elems": n,
+           "byte_mix_ms": ms}
+    del bm
+    torch.cuda.empty_cache()
+    a = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ms = _time_launches(lambda: probe.copy(b, a), PROBE_LAUNCHES)
+    out["copy_ceiling_gbs"] = 2 * COPY_PROBE_BYTES / (ms * 1e-3) / 1e9
     del a, b
-    return 2 * nbytes / (ms * 1e-3) / 1e9
+    torch.cuda.empty_cache()
+    r = torch.ones(READ_PROBE_BYTES // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(probe.load_library().q4probe_read_sink_words(), dtype=torch.int32, device="cuda")
+    ms = _time_launches(lambda: probe.read(r, sink), PROBE_LAUNCHES)
+    out["read_ceiling_gbs"] = READ_PROBE_BYTES / (ms * 1e-3) / 1e9
+    del r, sink
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(workload, recipe: str, max_elems: int):
-    """The CPU oracle (single thread, as written) on the leading tensors of the
-    same workload, one step from the zero state, on this host."""
-    import numpy as np
+    """The CPU oracle (single thread, as written) on the leading tensors of
+    the same workload: step 1 from the zero state (untimed), then step 2
+    (timed), so the timed step decodes a real state.  The leading tensors
+    get exactly the values the full workload gives them (the generators draw
+    tensor after tensor)."""
+    import dataclasses
+
     import torch
 
     from oracle import oracle as O
     orec = {"zip_sr": O.ZIP_SR, "ze_eden": O.ZE_EDEN, "factored": O.FACTORED, "fp32": O.FP32}.get(recipe)
     picked, n = [], 0
-    for i, t in enumerate(workload.tensors):
+    for t in workload.tensors:
         if n + t.numel > max_elems and picked:
             break
-        picked.append(i)
+        picked.append(t)
         n += t.numel
-    g = torch.Generator(device="cpu")
-    g.manual_seed(12345)
-    host = []
-    for i in picked:
-        t = workload.tensors[i]
-        p = (torch.randn(t.numel, generator=g) * 0.02).numpy()
-        gr = (torch.randn(t.numel, generator=g) * 1e-3).to(torch.bfloat16).view(torch.uint16).numpy().copy()
-        host.append((t, p, gr, O.TensorState8(t.shape, t.tensor_id, t.flags) if recipe == "block8"
-                     else O.TensorState(O.Config.of(orec), t.shape, t.tensor_id, t.flags)))
-    hp = O.HParams(step=1, **workload.hp)
-    t0 = time.perf_counter()
-    for t, p, gr, st in host:
-        st.step(hp, p, gr)
-    dt = time.perf_counter() - t0
-    names = ", ".join(f"{workload.tensors[i].name} {list(workload.tensors[i].shape)}" for i in picked)
+    sub = dataclasses.replace(workload, tensors=picked)
+    params = [p.reshape(-1).numpy().copy() for p in sub.init_params("cpu")]
+    consts = sub._tensor_consts("cpu")
+    states = [O.TensorState8(t.shape, t.tensor_id, t.flags) if recipe == "block8"
+              else O.TensorState(O.Config.of(orec), t.shape, t.tensor_id, t.flags) for t in picked]
+    dt = 0.0
+    for step in (1, 2):
+        grads = [g.reshape(-1).view(torch.uint16).numpy().copy() for g in sub.grads(step, "cpu", consts)]
+        hp = O.HParams(step=step, **workload.hp)
+        t0 = time.perf_counter()
+        for st, p, g in zip(states, params, grads):
+            st.step(hp, p, g)
+        if step == 2:
+            dt = time.perf_counter() - t0
+        del grads
+    names = ", ".join(f"{t.name} {list(t.shape)}" for t in picked)
     return {"value": n / dt / 1e9, "unit": "G params/s", "cores": 1, "kind": "oracle",
-            "sample": f"one {recipe} step over {n:,} parameters ({names}) of {workload.name}, "
+            "sample": f"step 2 (state from an untimed step 1) of {recipe} over the leading {n:,} parameters "
+                      f"({names}) of {workload.name}, with the workload's own seeded gradients; "
                       f"single-threaded C oracle, {dt:.1f} s",
             "host_cpu": host_cpu_model(), "host_nproc": os.cpu_count(), "oracle_threads": 1}
 
@@ -288,8 +315,8 @@ def main():
                     help="time only the last microbatch's accumulation pass (with the statistics) and the step "
                          "that reuses them, on this workload and recipe (a profiling aid; prints its own JSON line)")
     ap.add_argument("--max-grad-norm", type=float, default=0.0, help="clipping for --step-before")
-    ap.add_argument("--cpu-sample", type=int, default=480_000_000,
-                    help="elements in the oracle sample (about 12 s of single-threaded oracle work)")
+    ap.add_argument("--cpu-sample", type=int, default=300_000_000,
+                    help="elements in the oracle sample (about 8 s of single-threaded oracle work per step)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -315,8 +342,8 @@ def main():
         print(json.dumps({"workload": wl.name, "recipe": args.recipe, "params": n, "steps": args.steps,
                           "accumulate_ms": acc_ms, "accumulate_gbs": 6 * n / (acc_ms * 1e-3) / 1e9,
                           "step_ms": st_ms, "max_grad_norm": args.max_grad_norm,
-                          # the same 4 GiB copy as the main run (counter calibration for profiles)
-                          "copy_ceiling_gbs": copy_ceiling_gbs()}), flush=True)
+                          # the same probes as the main run (the copy calibrates the counters)
+                          **probe_ceilings(n)}), flush=True)
         return
     r = time_workload(wl, args.recipe, args.steps, args.warmup,
                       lm_head_phase=wl.lm_head_switch)
@@ -357,10 +384,11 @@ def main():
                      "launch_ms": {"mean": avg_launch, "median": statistics.median(launch_ms),
                                    "min": min(launch_ms), "max": max(launch_ms)}},
     }
-    try:
-        result["copy_ceiling_gbs"] = copy_ceiling_gbs()
-    except Exception as e:  # pragma: no cover
-        log(f"copy probe failed: {e}")
+    ceil = probe_ceilings(n)
+    log(f"probes: {ceil}")
+    result["roofline"]["byte_mix_ceiling_gbs"] = ceil["byte_mix_ceiling_gbs"]
+    result["roofline"]["frac_of_ceiling"] = achieved / ceil["byte_mix_ceiling_gbs"]
+    result["ceilings"] = ceil
 
     if not args.no_variants:
         variants = {}

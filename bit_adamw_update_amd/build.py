@@ -1,6 +1,7 @@
 """Build the HIP library (libq4adamw.so) for gfx950, in-tree, and beside it
 the self-test library of its exact primitives (libq4selftest.so, loaded only
-by the tests).
+by the tests) and the bandwidth probes (libq4probe.so, loaded by the
+benchmark and the tests).
 
 hipcc flags: -ffp-contract=off (no FMA contraction, so every FP32 operation
 rounds where it is written); HIP's default IEEE division and square root;
@@ -21,6 +22,9 @@ SOURCES = [os.path.join(CSRC, "q4_kernels.hip"), os.path.join(CSRC, "q4_abi.cpp"
 DEPS = SOURCES + [os.path.join(CSRC, "q4_internal.h"), os.path.join(CSRC, "q4_exact.h"),
                   os.path.join(CSRC, "q4_quant.h"), os.path.join(CSRC, "q4_codebooks.inc"),
                   os.path.join(ROOT, "include", "q4adamw.h")]
+PROBE_PATH = os.path.join(BUILD_DIR, "libq4probe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "q4_probe.hip")]
+PROBE_DEPS = PROBE_SOURCES + [os.path.join(ROOT, "include", "q4probe.h")]
 SELFTEST_PATH = os.path.join(BUILD_DIR, "libq4selftest.so")
 SELFTEST_SOURCES = [os.path.join(CSRC, "q4_selftest.hip")]
 SELFTEST_DEPS = SELFTEST_SOURCES + [os.path.join(CSRC, "q4_exact.h"), os.path.join(CSRC, "q4_quant.h"),
@@ -57,8 +61,9 @@ def _build_one(path: str, sources: list, deps: list, force: bool, verbose: bool)
 
 
 def build(force: bool = True, verbose: bool = False) -> str:
-    """Builds both libraries; returns the optimizer library's path."""
+    """Builds the three libraries; returns the optimizer library's path."""
     _build_one(SELFTEST_PATH, SELFTEST_SOURCES, SELFTEST_DEPS, force, verbose)
+    _build_one(PROBE_PATH, PROBE_SOURCES, PROBE_DEPS, force, verbose)
     return _build_one(LIB_PATH, SOURCES, DEPS, force, verbose)
 
 

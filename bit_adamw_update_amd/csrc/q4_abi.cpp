@@ -381,8 +381,20 @@ q4_status hip_fail(hipError_t e, const char* what) {
 // From pageable host memory HIP performs the copy synchronously, so the
 // temporary source may go away on return; the cost (a host wait for the
 // stream) is why callers that pass the same tensor list again set
-// Q4_HP_REUSE_TABLE / Q4_ACC_REUSE_TABLE.
+// Q4_HP_REUSE_TABLE / Q4_ACC_REUSE_TABLE.  A stream under graph capture
+// would record the copy with a pointer to that temporary, which is gone by
+// the time the graph replays, so the upload is refused there: a captured
+// call must reuse a table that an eager call left in the workspace.
 q4_status upload_tables(const Plan& P, int32_t n, uint8_t* wsb, hipStream_t st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        cs = hipStreamCaptureStatusNone;  // the copy below reports whatever is wrong with the stream
+    }
+    if (cs != hipStreamCaptureStatusNone)
+        return fail(Q4_ERR_INVALID_ARG,
+                    "the stream is capturing a graph: the tensor table upload cannot be captured; run one eager "
+                    "call first and capture with Q4_HP_REUSE_TABLE / Q4_ACC_REUSE_TABLE");
     const size_t upload = P.off_inv - P.off_tab;
     std::vector<uint8_t> host(upload, 0);
     std::memcpy(host.data(), P.tab.data(), sizeof(DevTensor) * n);
@@ -606,24 +618,13 @@ q4_status q4adamw_init_state(const q4_config* cfg, const q4_tensor* t, int32_t n
     return ok();
 }
 
-q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tensor* t, int32_t n, void* ws,
-                       size_t ws_bytes, void* stream) {
-    Resolved r;
-    q4_status s = resolve(cfg, &r);
-    if (s != Q4_OK) return s;
-    if ((s = check_hp(hp)) != Q4_OK) return s;
-    if ((s = check_tensors(r, t, n, true)) != Q4_OK) return s;
-    int dev = 0;
-    if ((s = check_device(&dev)) != Q4_OK) return s;
-    if ((hp->flags & Q4_HP_CHECK_POINTERS) && (s = check_all_pointers(t, n)) != Q4_OK) return s;
-    if (!ws) return fail(Q4_ERR_WORKSPACE, "workspace is NULL");
-    if (!aligned16(ws)) return fail(Q4_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
-    Plan P;
-    uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
-    plan_layout(r, t, n, P, wsb);
-    if (ws_bytes < P.total)
-        return fail(Q4_ERR_WORKSPACE, "workspace has %zu bytes, the step needs %zu", ws_bytes, P.total);
+}  // extern "C"
 
+namespace {
+
+// The step after validation and layout, on workspace `wsb` (planned in P).
+q4_status run_step(const Resolved& r, const q4_hparams* hp, int32_t n, const Plan& P, uint8_t* wsb, void* stream) {
+    q4_status s;
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e;
     if (!(hp->flags & Q4_HP_REUSE_TABLE) && (s = upload_tables(P, n, wsb, st)) != Q4_OK) return s;
@@ -686,6 +687,30 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
     e = launch_fused_step(r.var, sc, d_tab, d_schunks, n, P.total_schunks, P.n_mats > 0, st);
     if (e != hipSuccess) return hip_fail(e, "fused step launch");
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tensor* t, int32_t n, void* ws,
+                       size_t ws_bytes, void* stream) {
+    Resolved r;
+    q4_status s = resolve(cfg, &r);
+    if (s != Q4_OK) return s;
+    if ((s = check_hp(hp)) != Q4_OK) return s;
+    if ((s = check_tensors(r, t, n, true)) != Q4_OK) return s;
+    int dev = 0;
+    if ((s = check_device(&dev)) != Q4_OK) return s;
+    if ((hp->flags & Q4_HP_CHECK_POINTERS) && (s = check_all_pointers(t, n)) != Q4_OK) return s;
+    if (!ws) return fail(Q4_ERR_WORKSPACE, "workspace is NULL");
+    if (!aligned16(ws)) return fail(Q4_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+    Plan P;
+    uint8_t* wsb = reinterpret_cast<uint8_t*>(ws);
+    plan_layout(r, t, n, P, wsb);
+    if (ws_bytes < P.total)
+        return fail(Q4_ERR_WORKSPACE, "workspace has %zu bytes, the step needs %zu", ws_bytes, P.total);
+    return run_step(r, hp, n, P, wsb, stream);
 }
 
 q4_status q4adamw_dequant_state(const q4_config* cfg, const q4_tensor* t, float* m_out, float* v_out, void* ws,

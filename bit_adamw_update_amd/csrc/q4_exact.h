@@ -29,21 +29,24 @@ __device__ __forceinline__ float sqrt_rn_normal(float x) {
 }
 
 // The inverse that normalizes a block, x = value * (1/s), for a block scale
-// s >= 0: 0 for a zero scale and for one below the smallest normal float
-// (whose reciprocal may overflow; 0 * inf would not be 0), so such blocks
-// store the code of zero.  For s in [2^-126, 2^126) the hardware reciprocal
-// refined by one FMA Newton step equals the IEEE quotient; a wave with a
-// larger scale divides.
+// s >= 0: the IEEE reciprocal, or 0 for a zero scale and for a scale whose
+// reciprocal overflows (s <= 2^-128), which has no usable normalization
+// (value * inf is infinite, 0 * inf is NaN), so such blocks store the code of
+// zero.  For s in [2^-126, 2^126) the hardware reciprocal refined by one FMA
+// Newton step equals the IEEE quotient; a wave holding any other non-zero
+// scale (subnormal, or 2^126 and up) divides.
 __device__ __forceinline__ float inv_scale(float s) {
-    const bool normal = s >= 0x1p-126f;
+    const bool fast = (s >= 0x1p-126f && s < 0x1p126f) || s == 0.0f;
     float r;
-    if (__builtin_amdgcn_ballot_w64(s >= 0x1p126f) == 0) {
+    if (__builtin_amdgcn_ballot_w64(!fast) == 0) {
         const float y = __builtin_amdgcn_rcpf(s);
         r = __builtin_fmaf(__builtin_fmaf(-s, y, 1.0f), y, y);
     } else {
         r = 1.0f / s;
     }
-    return normal ? r : 0.0f;
+    // +inf (overflow, or s = 0 divided) and NaN (s = 0 through the Newton
+    // step) both fail the compare
+    return r <= 0x1.fffffep127f ? r : 0.0f;
 }
 
 // ds_bpermute byte addresses of the 8 nibbles of `codes` for lane row + code,

@@ -1,0 +1,160 @@
+// q4_probe.hip -- bandwidth probes that give the fused step's practical
+// ceiling on the machine they run on (libq4probe.so, loaded by the
+// benchmark and its tests; the optimizer library does not use it).
+//
+// k_byte_mix moves exactly the bytes the packed 4-bit step moves per element
+// (FP32 master read and written, BF16 gradient read, two 4-bit code streams
+// read and written, two FP32 block-scale streams read and written: 12.125
+// bytes per element), with the step's lane layout (8 consecutive elements
+// per lane, a 128-element block per 16-lane row, 16-byte accesses for
+// masters and gradients, 4 bytes per moment's codes, the row's scale read by
+// all its lanes and written by one) and its work distribution (4-wavefront
+// groups walking runs of consecutive slabs of 4 chunks, at most 4x the
+// resident groups), but only trivial arithmetic.  Its time is what this byte
+// mix costs on the memory system, whatever the optimizer computes.
+//
+// k_copy is a plain 16-byte-per-lane copy (known bytes read and written),
+// which also calibrates the HBM traffic counters; k_read reads only.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <stdint.h>
+
+#include "../../include/q4probe.h"
+
+namespace {
+
+constexpr int kChunk = 512, kWaves = 4, kRun = 8;
+
+template <class T> using gptr = __attribute__((address_space(1))) T*;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int64_t next_chunk(int64_t c, int& j, int run, int64_t groups) {
+    if (++j < run) return c + kWaves;
+    j = 0;
+    return c + (groups * run - (run - 1)) * kWaves;
+}
+
+__global__ __launch_bounds__(256) void k_byte_mix(float* __restrict__ param, const uint16_t* __restrict__ grad,
+                                                   uint8_t* __restrict__ mcodes, uint8_t* __restrict__ vcodes,
+                                                   float* __restrict__ mscales, float* __restrict__ vscales,
+                                                   int64_t chunks, int run, float a) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t groups = gridDim.x;
+    int64_t c = (int64_t)blockIdx.x * run * kWaves + wave;
+    for (int j = 0; c < chunks; c = next_chunk(c, j, run, groups)) {
+        const int64_t c0 = c * kChunk;
+        const gptr<float> p = (gptr<float>)param + c0 + lane * 8;
+        const gptr<const uint16_t> g = (gptr<const uint16_t>)grad + c0 + lane * 8;
+        const gptr<uint32_t> mc = (gptr<uint32_t>)(mcodes + (c0 >> 1)) + lane;
+        const gptr<uint32_t> vc = (gptr<uint32_t>)(vcodes + (c0 >> 1)) + lane;
+        const int64_t blk = c * 4 + (lane >> 4);
+        f32x4 x = *reinterpret_cast<const gptr<const f32x4>>(p);
+        f32x4 y = *reinterpret_cast<const gptr<const f32x4>>(p + 4);
+        const u32x4 q = *reinterpret_cast<const gptr<const u32x4>>(g);
+        const uint32_t m = *mc, v = *vc;
+        const float sm = ((gptr<float>)mscales)[blk], sv = ((gptr<float>)vscales)[blk];
+        // trivial, data-dependent arithmetic: nothing can be elided
+        const float gq = __uint_as_float(q.x << 16) + __uint_as_float(q.w & 0xFFFF0000u);
+        x = x * a + gq;
+        y = y * a + gq;
+        *reinterpret_cast<gptr<f32x4>>(p) = x;
+        *reinterpret_cast<gptr<f32x4>>(p + 4) = y;
+        *mc = m ^ q.y;
+        *vc = v ^ q.z;
+        if ((lane & 15) == 0) {
+            ((gptr<float>)mscales)[blk] = sm * a;
+            ((gptr<float>)vscales)[blk] = sv * a;
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_copy(u32x4* __restrict__ dst, const u32x4* __restrict__ src, int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        ((gptr<u32x4>)dst)[i] = ((gptr<const u32x4>)src)[i];
+}
+
+__global__ __launch_bounds__(256) void k_read(const u32x4* __restrict__ src, int64_t n16, uint32_t* __restrict__ sink) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    uint32_t acc = 0;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride) {
+        const u32x4 v = ((gptr<const u32x4>)src)[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    // one store per thread whose value is never 0 for data the caller made
+    // non-zero, so the loads stay; a sink of gridDim.x * 256 words
+    sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+int resident_groups(const void* kernel) {
+    static std::atomic<int> cus{0};
+    if (cus.load() == 0) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        const bool ok = hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess;
+        cus.store(ok && prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256);
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1) per_cu = 1;
+    return per_cu * cus.load();
+}
+
+bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int64_t q4probe_byte_mix_bytes(int64_t n) { return n <= 0 ? 0 : 10 * n + 2 * n + (n / 128) * 16; }
+
+int q4probe_byte_mix(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
+                     float* v_scales, int64_t n, void* stream) {
+    if (n <= 0 || n % kChunk != 0) return Q4PROBE_ERR_ARG;
+    if (!param || !grad || !m_codes || !v_codes || !m_scales || !v_scales) return Q4PROBE_ERR_ARG;
+    if (!a16(param) || !a16(grad) || !a16(m_codes) || !a16(v_codes) || !a16(m_scales) || !a16(v_scales))
+        return Q4PROBE_ERR_ARG;
+    const int64_t chunks = n / kChunk;
+    const int64_t slabs = (chunks + kWaves - 1) / kWaves;
+    static std::atomic<int> resident{0};
+    if (resident.load() == 0) resident.store(resident_groups(reinterpret_cast<const void*>(k_byte_mix)));
+    const int64_t cap = 4 * (int64_t)resident.load();
+    int run = kRun;
+    while (run > 1 && slabs / run < cap) run >>= 1;
+    const int64_t runs = (slabs + run - 1) / run;
+    const int grid = (int)(runs < cap ? runs : cap);
+    k_byte_mix<<<grid, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(param, grad, m_codes, v_codes, m_scales,
+                                                                       v_scales, chunks, run, 0.999f);
+    return hipGetLastError() == hipSuccess ? Q4PROBE_OK : Q4PROBE_ERR_HIP;
+}
+
+int q4probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
+    if (!dst || !src || bytes == 0 || bytes % 16 != 0 || !a16(dst) || !a16(src)) return Q4PROBE_ERR_ARG;
+    static std::atomic<int> resident{0};
+    if (resident.load() == 0) resident.store(resident_groups(reinterpret_cast<const void*>(k_copy)));
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int64_t need = (n16 + 255) / 256;
+    const int64_t cap = 4 * (int64_t)resident.load();
+    k_copy<<<(unsigned)(need < cap ? need : cap), 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+        reinterpret_cast<u32x4*>(dst), reinterpret_cast<const u32x4*>(src), n16);
+    return hipGetLastError() == hipSuccess ? Q4PROBE_OK : Q4PROBE_ERR_HIP;
+}
+
+int64_t q4probe_read_sink_words(void) { return 4 * 1024 * 256; }
+
+int q4probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    if (!src || !sink || bytes == 0 || bytes % 16 != 0 || !a16(src)) return Q4PROBE_ERR_ARG;
+    static std::atomic<int> resident{0};
+    if (resident.load() == 0) resident.store(resident_groups(reinterpret_cast<const void*>(k_read)));
+    const int64_t n16 = (int64_t)(bytes / 16);
+    const int64_t need = (n16 + 255) / 256;
+    int64_t cap = 4 * (int64_t)resident.load();
+    if (cap > q4probe_read_sink_words() / 256) cap = q4probe_read_sink_words() / 256;
+    k_read<<<(unsigned)(need < cap ? need : cap), 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
+        reinterpret_cast<const u32x4*>(src), n16, sink);
+    return hipGetLastError() == hipSuccess ? Q4PROBE_OK : Q4PROBE_ERR_HIP;
+}
+
+}  // extern "C"

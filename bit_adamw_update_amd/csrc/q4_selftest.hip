@@ -36,12 +36,17 @@ __device__ bool is_sqrt_rn(uint32_t x, uint32_t y) {
     const double lo = mid_below(y), hi = mid_above(y), xd = (double)__uint_as_float(x);
     return lo * lo < xd && xd < hi * hi;
 }
-// y == (s >= 2^-126 ? RN(1/s) : +0) for every s >= +0, NaN included (-> +0)
+// y == RN(1/s) when s > 0 and RN(1/s) is finite, else +0, for every s >= +0,
+// +inf and NaN included (-> +0).  RN(1/s) overflows iff 1/s reaches the
+// midpoint 2^128 - 2^103 between the largest float and 2^128, i.e. iff
+// s * (2^128 - 2^103) <= 1 (exact in binary64: 24 x 25 significant bits).
 __device__ bool is_inv_scale(uint32_t s, uint32_t y) {
     const float sf = __uint_as_float(s);
-    if (!(sf >= 0x1p-126f) || s == 0x7F800000u) return y == 0u;
+    if (!(sf > 0.0f) || s == 0x7F800000u) return y == 0u;
+    const double sd = (double)sf;
+    if (sd * (0x1p128 - 0x1p103) <= 1.0) return y == 0u;
     if (!finite_positive(y)) return false;
-    const double lo = mid_below(y), hi = mid_above(y), sd = (double)sf;
+    const double lo = mid_below(y), hi = mid_above(y);
     return lo * sd < 1.0 && 1.0 < hi * sd;
 }
 

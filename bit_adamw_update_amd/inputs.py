@@ -90,12 +90,14 @@ class Workload:
         return z.div_(c.div_(3.0).sqrt_())
 
     # magnitude classes of the "edge" kind, one per 128-block in turn
-    EDGE_SCALES = (1e-3, 1e-16, 1e-39, 0.0, 1e-3, 1e-25, 1e-20)
+    EDGE_SCALES = (1e-3, 1e-16, 1e-39, 0.0, 1e-3, 1e-25, 1e-20, 8e-39)
 
     def _edge(self, shape, g, device) -> torch.Tensor:
-        """Blocks of normal, tiny (squares below 2^-96), BF16-subnormal,
-        signed-zero, mixed (exact zeros and values 10^6 times larger), and
-        vanishing (squares underflow to zero or to subnormals) gradients."""
+        """Blocks of normal, tiny (squares below 2^-96), BF16-subnormal
+        (first-moment scales below 2^-128, whose reciprocal overflows, and
+        between 2^-128 and 2^-126, whose reciprocal is finite), signed-zero,
+        mixed (exact zeros and values 10^6 times larger), and vanishing
+        (squares underflow to zero or to subnormals) gradients."""
         x = self._student_t3(shape, g, device).reshape(-1)
         cls = (torch.arange(x.numel(), device=device) // 128) % len(self.EDGE_SCALES)
         y = x * torch.tensor(self.EDGE_SCALES, device=device, dtype=torch.float32)[cls]

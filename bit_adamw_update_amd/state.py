@@ -123,7 +123,16 @@ class Q4State:
         if grad_stats:
             flags |= api.HP_GRAD_STATS
         h = self.hparams(step, flags=flags, **hp)
-        api.q4adamw_step(self.cfg, h, self._desc, self.ws, self.ws_bytes, stream)
+        self._call(api.q4adamw_step, self.cfg, h, self._desc, self.ws, self.ws_bytes, stream)
+
+    def _call(self, fn, *args) -> None:
+        """A call that may upload the tensor table: if it is refused, the
+        workspace may not hold the table, so the next call uploads it."""
+        try:
+            fn(*args)
+        except Exception:
+            self._last_key = None
+            raise
 
     def flat_offsets(self) -> tuple[list, int]:
         """Element offsets of each tensor in a flat microbatch gradient buffer, and its length."""
@@ -143,11 +152,11 @@ class Q4State:
         flags = (api.ACC_FIRST if first else 0) | (api.ACC_LAST if last else 0)
         if self._table(params, grads):
             flags |= api.ACC_REUSE_TABLE
-        api.q4adamw_accumulate(self.cfg, self._desc, micro, flags, self.ws, self.ws_bytes, stream)
+        self._call(api.q4adamw_accumulate, self.cfg, self._desc, micro, flags, self.ws, self.ws_bytes, stream)
 
     def grad_stats(self, params, grads, stream=None) -> None:
         self._table(params, grads)
-        api.q4adamw_grad_stats(self.cfg, self._desc, self.ws, self.ws_bytes, stream)
+        self._call(api.q4adamw_grad_stats, self.cfg, self._desc, self.ws, self.ws_bytes, stream)
 
     def grad_norm(self, stream=None) -> float:
         return api.q4adamw_grad_norm(self.ws, self.ws_bytes, stream)

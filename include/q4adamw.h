@@ -125,7 +125,10 @@ typedef struct {
                                      q4adamw_step or q4adamw_accumulate with the same configuration: skip
                                      its upload.  The call then enqueues kernel launches only (no copy, no
                                      allocation, no synchronization), so it may be captured in a HIP graph
-                                     once an earlier call on the device has run */
+                                     once an earlier call on the device has run.  Without it, a call on a
+                                     stream that is capturing a graph returns Q4_ERR_INVALID_ARG and
+                                     enqueues nothing (the upload's host source would not outlive the
+                                     call, so a replay could not read it) */
 #define Q4_HP_CHECK_POINTERS 2u   /* also check that every pointer lives on the current device */
 #define Q4_HP_GRAD_STATS 4u       /* the workspace holds the statistics of exactly these gradients, left by
                                      q4adamw_accumulate (Q4_ACC_LAST) or q4adamw_grad_stats with this
@@ -230,10 +233,11 @@ q4_status q4adamw_init_state(const q4_config* cfg, const q4_tensor* t, int32_t n
  * and C take their own EMA of this step's row/column means of g^2), update
  * the weight p <- p decay - step_size m1 / (sqrt(v1) rsbc2 + eps) from the
  * unquantized m1, v1, then requantize: absmax scales, the m rule (RTN, or
- * SR for the LM head in the final phase), the v rule, EDEN.  A block whose
- * scale is 0 or below the smallest normal float (2^-126) stores the code of
- * zero in every slot and keeps its scale as computed (the reciprocal of a
- * subnormal scale may overflow).
+ * SR for the LM head in the final phase), the v rule, EDEN.  A block is
+ * normalized by the IEEE reciprocal of its scale (subnormal scales
+ * included); a block whose scale is 0, or so small that its reciprocal
+ * overflows (s <= 2^-128), stores the code of zero in every slot and keeps
+ * its scale as computed.
  * Clipping (hp->max_grad_norm > 0): s = min(1, max_grad_norm / (norm +
  * 1e-6)) in binary64, rounded to FP32, from the global norm of the
  * gradients (the statistics in ws with Q4_HP_GRAD_STATS, else gathered

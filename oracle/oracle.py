@@ -68,7 +68,7 @@ class _Win(C.Structure):
                 ("m_codes", C.c_void_p), ("m_scales", C.c_void_p),
                 ("v_codes", C.c_void_p), ("v_scales", C.c_void_p),
                 ("R", C.c_void_p), ("C", C.c_void_p), ("inv_meanR", C.c_float),
-                ("m32", C.c_void_p), ("v32", C.c_void_p)]
+                ("m32", C.c_void_p), ("v32", C.c_void_p), ("m1_out", C.c_void_p), ("v1_out", C.c_void_p)]
 
 
 _lib = None
@@ -249,12 +249,17 @@ def factored_update(hp: HParams, rows: int, cols: int, grad: np.ndarray, R: np.n
 
 def step_window(cfg: Config, hp: HParams, *, tensor_id: int, flags: int, numel: int, base: int,
                 param, grad, m_codes=None, m_scales=None, v_codes=None, v_scales=None,
-                cols: int = 0, R=None, Cc=None, inv_meanR: float = 0.0, m32=None, v32=None) -> None:
-    """Step elements [base, base + len(param)) of a tensor in place."""
+                cols: int = 0, R=None, Cc=None, inv_meanR: float = 0.0, m32=None, v32=None,
+                m1_out=None, v1_out=None) -> None:
+    """Step elements [base, base + len(param)) of a tensor in place.  With
+    m1_out / v1_out (float32, the window's length) the unquantized moments
+    of the step are written there too."""
     length = param.size
     assert grad.size == length and grad.dtype == np.uint16 and param.dtype == np.float32
+    for o in (m1_out, v1_out):
+        assert o is None or (o.dtype == np.float32 and o.size == length)
     w = _Win(tensor_id, flags, numel, cols, base, length, _p(param), _p(grad), _p(m_codes), _p(m_scales),
-             _p(v_codes), _p(v_scales), _p(R), _p(Cc), inv_meanR, _p(m32), _p(v32))
+             _p(v_codes), _p(v_scales), _p(R), _p(Cc), inv_meanR, _p(m32), _p(v32), _p(m1_out), _p(v1_out))
     c, h = cfg.c(), hp.c()
     rc = lib().or_step_window(C.byref(c), C.byref(h), C.byref(w))
     if rc != 0:

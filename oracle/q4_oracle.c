@@ -527,6 +527,9 @@ typedef struct {
     uint8_t* v_codes; float* v_scales;
     const float* R; const float* C; float inv_meanR;
     float* m32; float* v32;
+    /* optional (NULL: not written): the unquantized m1, v1 of the window,
+     * which the parity harness reads to audit a differing code */
+    float* m1_out; float* v1_out;
 } or_window;
 
 /* One AdamW step over a window ([N] AdamW paragraph; [A] "State
@@ -582,6 +585,8 @@ int or_step_window(const or_config* cfg, const or_hparams* hp, const or_window* 
             w->param[j] = fmaf(-step_size, mm / denom, w->param[j] * decay);
             m1[k] = mm;
             v1[k] = vv;
+            if (w->m1_out) w->m1_out[j] = mm;
+            if (w->v1_out) w->v1_out[j] = vv;
         }
         if (fp32) {
             for (int k = 0; k < n; ++k) { w->m32[off + k] = m1[k]; w->v32[off + k] = v1[k]; }

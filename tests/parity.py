@@ -8,7 +8,15 @@ compares, per tensor window:
   * master weights: |w_gpu - w_ora| / max(|w_ora|, rms(w_ora)) <= 1e-6,
   * factored row/column vectors within 1e-6 relative (binary64 sums in a
     different order on the two sides, rounded to FP32).
-The fraction of differing codes must stay <= 1e-6 of all codes compared.
+The fraction of differing codes must stay <= 1e-6 of all codes compared,
+and every differing code must be an audited stochastic-rounding tie: from
+the oracle's unquantized moment of that step, the harness recomputes the
+rule's two sides in binary64 and accepts the difference only if
+|u * den - num| <= 2 ulp(num) in FP32 and both codes bracket the value
+(round-to-nearest and EDEN codes involve no square root and must match).
+The weight tolerance is relative to max(|w|, rms of the tensor's window):
+near a weight that crosses zero FP32 is accurate relative to the terms of
+the update, not to the tiny result.
 """
 from __future__ import annotations
 
@@ -77,6 +85,8 @@ class Window:
     v32: np.ndarray = None
     m_bad: np.ndarray = None
     v_bad: np.ndarray = None
+    m1: np.ndarray = None       # the oracle's unquantized moments of the last step
+    v1: np.ndarray = None
 
 
 @dataclass
@@ -90,10 +100,14 @@ class Report:
     max_w_err: float = 0.0
     max_rc_err: float = 0.0
     padding_nonzero: int = 0
+    ties_audited: int = 0
+    untied_differ: int = 0
     notes: list = field(default_factory=list)
 
     def check(self):
         assert self.padding_nonzero == 0, "a nibble past the end of an odd-length tensor is not 0"
+        assert self.untied_differ == 0, \
+            f"{self.untied_differ} differing codes are not stochastic-rounding ties: {self.notes[:5]}"
         assert self.scales_differ == 0, f"{self.scales_differ} of {self.scales_compared} scales differ"
         assert self.codes_differ <= CODE_FRAC * max(self.codes_compared, 1), \
             f"{self.codes_differ} of {self.codes_compared} codes differ"
@@ -108,9 +122,11 @@ def _rms(x):
 
 def run(workload: inputs.Workload, recipe: str, steps: int, *, windows=None, device="cuda",
         cfg: q4.Q4Config | None = None, grads_on: str = "cpu", lm_head_phase: bool = False,
-        hp: dict | None = None, check_every_step: bool = True) -> Report:
+        hp: dict | None = None, check_every_step: bool = True, step_offset: int = 0) -> Report:
     """Run `steps` steps on both sides and compare.  windows=None compares
-    every element of every tensor; otherwise a list of (i, b0, b1)."""
+    every element of every tensor; otherwise a list of (i, b0, b1).  The
+    step counts are step_offset + 1 .. step_offset + steps (the gradients
+    are those of steps 1 .. steps)."""
     dev = torch.device(device)
     hpk = dict(workload.hp)
     if hp:
@@ -150,6 +166,8 @@ def run(workload: inputs.Workload, recipe: str, steps: int, *, windows=None, dev
                 w.v_scales = np.zeros(nb, np.float32)
         w.m_bad = np.zeros(n, bool)
         w.v_bad = np.zeros(n, bool)
+        w.m1 = np.zeros(n, np.float32)
+        w.v1 = np.zeros(n, np.float32)
         wins.append(w)
     # factored matrices: the oracle keeps full R and C
     fact = {}
@@ -158,9 +176,10 @@ def run(workload: inputs.Workload, recipe: str, steps: int, *, windows=None, dev
             if len(t.shape) >= 2 and t.numel > 0:
                 fact[i] = (np.zeros(t.shape[0], np.float32), np.zeros(t.numel // t.shape[0], np.float32))
     rep = Report()
-    for step in range(1, steps + 1):
-        phase = inputs.lm_head_sr_on(step, steps) if lm_head_phase else 0
-        grads = workload.grads(step, grads_on, consts)
+    for k in range(1, steps + 1):
+        step = step_offset + k
+        phase = inputs.lm_head_sr_on(k, steps) if lm_head_phase else 0
+        grads = workload.grads(k, grads_on, consts)
         gg = [g.to(dev).reshape(-1).contiguous() for g in grads]
         st.step(gp, gg, step, lm_head_sr=phase, **hpk)
         ohp = O.HParams(step=step, lm_head_sr=phase, **hpk)
@@ -174,18 +193,80 @@ def run(workload: inputs.Workload, recipe: str, steps: int, *, windows=None, dev
             gw = grads[w.i].reshape(-1)[w.lo:w.hi].view(torch.uint16).cpu().numpy().copy()
             kw = dict(tensor_id=t.tensor_id, flags=t.flags, numel=t.numel, base=w.lo, param=w.param, grad=gw,
                       m_codes=w.m_codes, m_scales=w.m_scales, v_codes=w.v_codes, v_scales=w.v_scales,
-                      m32=w.m32, v32=w.v32)
+                      m32=w.m32, v32=w.v32, m1_out=w.m1, v1_out=w.v1)
             if w.i in fact:
                 R, Cc = fact[w.i]
                 kw.update(cols=t.numel // t.shape[0], R=R, Cc=Cc, inv_meanR=inv[w.i])
             O.step_window(ocfg, ohp, **kw)
-        if check_every_step or step == steps:
+        if check_every_step or k == steps:
             torch.cuda.synchronize()
-            _compare(st, gp, wins, fact, rep, fp32)
+            _compare(st, gp, wins, fact, rep, fp32, Audit(ocfg, ohp, specs))
     return rep
 
 
-def _compare(st, gp, wins, fact, rep: Report, fp32: bool):
+def _ulp32(x: float) -> float:
+    return float(np.spacing(np.float32(abs(x))))
+
+
+class Audit:
+    """Decides whether a code that differs between the GPU and the oracle is
+    a stochastic-rounding tie, from the oracle's unquantized moment m1 or v1
+    of the step just compared (recomputed in binary64 here)."""
+
+    def __init__(self, ocfg: O.Config, ohp: O.HParams, specs):
+        self.cfg, self.hp, self.specs = ocfg, ohp, specs
+        self.eps_sr = ohp.eps if ohp.eps_sr is None else ohp.eps_sr
+
+    def _rule(self, moment: str, ti: int) -> int:
+        if moment == "v":
+            return self.cfg.v_rule
+        lm_sr = (self.specs[ti].flags & O.TF_LM_HEAD) and self.hp.lm_head_sr
+        return O.STATE_SR if (lm_sr or self.cfg.m_rule == O.STATE_SR) else O.STATE_RTN
+
+    def is_tie(self, moment: str, ti: int, elem: int, vals: np.ndarray, j: int, code_gpu: int,
+               code_ora: int) -> bool:
+        """vals: the window's unquantized moments (FP32), j the element's
+        index in the window, elem its index in the tensor."""
+        rule = self._rule(moment, ti)
+        if rule in (O.STATE_RTN, O.UPDATE_RTN):
+            return False
+        b0 = (j // 128) * 128
+        blk = vals[b0:b0 + 128].astype(np.float32)
+        s = np.float32(np.abs(blk).max()) if moment == "m" else np.float32(blk.max())
+        with np.errstate(over="ignore", divide="ignore"):
+            inv = np.float32(1) / s if s > 0 else np.float32(0)
+        if not np.isfinite(inv):
+            return False
+        x = np.float32(vals[j]) * inv
+        x = np.float32(min(max(x, -1.0), 1.0)) if moment == "m" else np.float32(min(x, 1.0))
+        L, code, _ = O.sorted_levels(self.cfg.m_cb if moment == "m" else self.cfg.v_cb)
+        lo = int(np.max(np.nonzero(L <= x)[0])) if np.any(L <= x) else 0
+        if lo + 1 >= L.size or L[lo] == x:
+            return False
+        if {code_gpu, code_ora} != {int(code[lo]), int(code[lo + 1])}:
+            return False   # not the two levels that bracket the value
+        u = O.uniform(self.hp.seed, self.hp.step, self.specs[ti].tensor_id, 0 if moment == "m" else 1, elem)
+        if rule == O.STATE_SR:
+            num, den = float(x) - float(L[lo]), float(L[lo + 1]) - float(L[lo])
+        else:   # preconditioner-space SR, in binary64 from the FP32 inputs
+            a_lo, a_hi = np.float32(L[lo]) * s, np.float32(L[lo + 1]) * s
+            rlo, rhi, sv = np.sqrt(float(a_lo)), np.sqrt(float(a_hi)), np.sqrt(float(vals[j]))
+            num = (sv - rlo) * (rhi + self.eps_sr)
+            den = (rhi - rlo) * (sv + self.eps_sr)
+        return abs(u * den - num) <= 2 * _ulp32(num)
+
+
+def _audit(rep: Report, audit: Audit, moment: str, w: "Window", gcodes, ocodes, diff):
+    vals = w.m1 if moment == "m" else w.v1
+    for j in np.nonzero(diff)[0]:
+        if audit.is_tie(moment, w.i, w.lo + int(j), vals, int(j), int(gcodes[j]), int(ocodes[j])):
+            rep.ties_audited += 1
+        else:
+            rep.untied_differ += 1
+            rep.notes.append((moment, w.i, w.lo + int(j), int(gcodes[j]), int(ocodes[j])))
+
+
+def _compare(st, gp, wins, fact, rep: Report, fp32: bool, audit: Audit):
     for w in wins:
         b = st.bufs[w.i]
         n = w.hi - w.lo
@@ -208,6 +289,8 @@ def _compare(st, gp, wins, fact, rep: Report, fp32: bool):
             w.m_bad |= dm
             rep.codes_compared += n
             rep.codes_differ += int(dm.sum())
+            if dm.any():
+                _audit(rep, audit, "m", w, gm, om, dm)
             gs = b.m_scales[w.b0:w.b1].cpu().numpy()
             rep.scales_compared += gs.size
             rep.scales_differ += int((gs.view(np.uint32) != w.m_scales.view(np.uint32)).sum())
@@ -218,6 +301,8 @@ def _compare(st, gp, wins, fact, rep: Report, fp32: bool):
                 w.v_bad |= dv
                 rep.codes_compared += n
                 rep.codes_differ += int(dv.sum())
+                if dv.any():
+                    _audit(rep, audit, "v", w, gv, ov, dv)
                 gs = b.v_scales[w.b0:w.b1].cpu().numpy()
                 rep.scales_compared += gs.size
                 rep.scales_differ += int((gs.view(np.uint32) != w.v_scales.view(np.uint32)).sum())

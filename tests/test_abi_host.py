@@ -40,6 +40,25 @@ def test_exports_every_declared_symbol(lib):
         assert re.search(rf"\bT {n}\b", out), n
 
 
+def test_every_header_is_served_by_a_library():
+    """Each header under include/ names the functions of one library, which
+    loads on this host and exports all of them."""
+    import ctypes
+    libs = {"q4adamw.h": build.LIB_PATH, "q4probe.h": build.PROBE_PATH}
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == sorted(libs), headers
+    for h in headers:
+        if not os.path.exists(libs[h]):
+            build.build(force=False)
+        src = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", h)).read(), flags=re.S)
+        names = sorted(set(re.findall(r"\b(q4[a-z]+_[a-z0-9_]+)\s*\(", src)))
+        assert names, h
+        so = ctypes.CDLL(libs[h])
+        out = os.popen(f"nm -D --defined-only {libs[h]}").read()
+        for n in names:
+            assert hasattr(so, n) and re.search(rf"\bT {n}\b", out), (h, n)
+
+
 def test_abi_version_and_status_strings():
     assert q4.q4adamw_abi_version() == 2 == q4.api.ABI_VERSION
     assert q4.q4adamw_status_string(0) == "ok"

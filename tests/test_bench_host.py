@@ -38,16 +38,17 @@ def _write(path, text):
 
 
 def test_kernel_hash_ignores_comments_and_blank_space(tmp_path, monkeypatch):
+    from bit_adamw_update_amd import profiling
     a, b = tmp_path / "a.hip", tmp_path / "b.hip"
     _write(a, "int f(int x) {\n    return x + 1;  // one more\n}\n")
-    monkeypatch.setattr(bench, "KERNEL_SRC", [str(a)])
+    monkeypatch.setattr(profiling, "KERNEL_SRC", [str(a)])
     h0 = bench.kernel_hash()
     _write(a, "// a new comment line\nint f(int x)   {\n\n    return x + 1;\n}\n")
     assert bench.kernel_hash() == h0
     _write(a, "int f(int x) {\n    return x + 2;\n}\n")
     assert bench.kernel_hash() != h0
     _write(b, "int g();\n")
-    monkeypatch.setattr(bench, "KERNEL_SRC", [str(a), str(b)])
+    monkeypatch.setattr(profiling, "KERNEL_SRC", [str(a), str(b)])
     assert bench.kernel_hash() != h0
 
 

@@ -26,9 +26,12 @@ def _check_weights(p, ref, what):
     assert err <= parity.W_TOL, f"{what}: weight error {err:.3e}"
 
 
-def run_windows(w, steps, windows=None, grads_on="cpu", clip=0.0):
+def run_windows(w, steps, windows=None, grads_on="cpu", clip=0.0, hp=None, step_offset=0):
     """Step the GPU state over the whole workload and the oracle over
-    block windows [(i, b0, b1)] (all of every tensor when None); compare."""
+    block windows [(i, b0, b1)] (all of every tensor when None); compare.
+    hp overrides the workload's hyper-parameters; the step counts are
+    step_offset + 1 .. step_offset + steps."""
+    hpk = dict(w.hp, **(hp or {}))
     dev = torch.device("cuda")
     consts = w._tensor_consts(grads_on)
     params = [p.reshape(-1) for p in w.init_params(grads_on)]
@@ -50,15 +53,15 @@ def run_windows(w, steps, windows=None, grads_on="cpu", clip=0.0):
             st.grad_stats(gp, gg)
             scale = O.clip_factor(sum(O.grad_sumsq(x.view(torch.uint16).cpu().numpy().reshape(-1)) for x in g),
                                   clip)
-        st.step(gp, gg, s, max_grad_norm=clip, **w.hp)
-        hp = O.HParams(step=s, grad_scale=scale, **w.hp)
+        st.step(gp, gg, step_offset + s, max_grad_norm=clip, **hpk)
+        ohp = O.HParams(step=step_offset + s, grad_scale=scale, **hpk)
         for k, (i, b0, b1) in enumerate(windows):
             t = w.tensors[i]
             lo, hi = b0 * 128, min(b1 * 128, t.numel)
             # the window is its own tensor for the oracle: the tensor id and
             # the block-aligned offset are all the 8-bit step depends on
             gw = g[i].reshape(-1)[lo:hi].view(torch.uint16).cpu().numpy().copy()
-            ost[k].step(hp, op[k], gw)
+            ost[k].step(ohp, op[k], gw)
     torch.cuda.synchronize()
     for k, (i, b0, b1) in enumerate(windows):
         b = st.bufs[i]
@@ -76,6 +79,20 @@ def run_windows(w, steps, windows=None, grads_on="cpu", clip=0.0):
 def test_tiny_workload_10_steps():
     _flush("block8 tiny")
     run_windows(inputs.tiny(), 10)
+
+
+@pytest.mark.parametrize("name,hpk,offset", [
+    ("b0.9_0.95", dict(beta1=0.9, beta2=0.95), 0),
+    ("b0_0.99_wd0", dict(beta1=0.0, beta2=0.99, weight_decay=0.0), 0),
+    ("lr1e-4_eps1e-6", dict(lr=1e-4, eps=1e-6), 0),
+    ("lr3e-3_step2^32", dict(lr=3e-3), 2 ** 32 - 3),
+], ids=lambda x: x if isinstance(x, str) else "")
+def test_hyperparameter_grid(name, hpk, offset):
+    """Other betas, no decay, other learning rates and eps, and step counts
+    past 2^32 (the bias correction in binary64), every element."""
+    _flush(f"block8 hparams {name}")
+    shapes = [(1,), (129,), (1000,), (4097,), (7, 129), (64, 520)]
+    run_windows(inputs.custom(shapes, grad_kind="masked", seed=71), 5, hp=hpk, step_offset=offset)
 
 
 def test_ragged_shapes():

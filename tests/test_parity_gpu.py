@@ -98,6 +98,51 @@ def test_lm_head_switch_final_phase():
     assert rep.codes_differ == 0
 
 
+# Points of the hyper-parameter and seed space besides the workloads' own
+# (lr 1e-3, betas (0.9, 0.999), eps 1e-8, wd 0.1, seed 0, eps_sr = eps):
+# Philox keys with a non-zero high word, a separate eps_sr, other betas
+# (beta1 = 0 included), no decay, other learning rates.
+HP_GRID = [
+    ("seed1", dict(seed=1)),
+    ("seed9E3779B9", dict(seed=0x9E3779B9)),
+    ("seed2^32+7", dict(seed=2 ** 32 + 7)),
+    ("seed2^64-1", dict(seed=2 ** 64 - 1)),
+    ("eps_sr1e-6", dict(eps_sr=1e-6, seed=5)),
+    ("b0.9_0.95", dict(beta1=0.9, beta2=0.95, seed=3)),
+    ("b0_0.99", dict(beta1=0.0, beta2=0.99, seed=4)),
+    ("wd0", dict(weight_decay=0.0, seed=6)),
+    ("lr1e-4", dict(lr=1e-4, seed=7)),
+    ("lr3e-3", dict(lr=3e-3, seed=8)),
+]
+GRID_SHAPES = [(1,), (129,), (1000,), (4097,), (7, 129), (64, 520), (2, 1031)]
+
+
+@pytest.mark.parametrize("hpk", [h for _, h in HP_GRID], ids=[n for n, _ in HP_GRID])
+@pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden", "factored", "fp32"])
+def test_hyperparameter_and_seed_grid(recipe, hpk):
+    """Ragged tensors, one flagged as the LM head with its final-phase SR on
+    the last step, 5 steps, every element, at each point of the grid."""
+    w = inputs.custom(GRID_SHAPES, grad_kind="masked", seed=41,
+                      flags=[0, 0, inputs.TF_LM_HEAD, 0, 0, 0, 0])
+    _flush(f"grid {recipe} {hpk}")
+    rep = parity.run(w, recipe, 5, hp=hpk, lm_head_phase=True)
+    rep.check()
+    assert rep.codes_differ == 0
+
+
+@pytest.mark.parametrize("offset", [2 ** 32 - 3, 10 ** 6, 2 ** 40 + 5], ids=["2^32-3", "1e6", "2^40+5"])
+@pytest.mark.parametrize("recipe", ["zip_sr", "ze_eden", "factored"])
+def test_step_counts_past_the_counter_word(recipe, offset):
+    """Steps offset+1 .. offset+5: the Philox counter takes the step's low
+    32 bits (crossing 2^32 at the first offset), the bias correction the
+    full count; the LM-head SR phase on the last step."""
+    w = inputs.custom(GRID_SHAPES, grad_kind="masked", seed=42, flags=[0, 0, inputs.TF_LM_HEAD, 0, 0, 0, 0])
+    _flush(f"steps from {offset} {recipe}")
+    rep = parity.run(w, recipe, 5, hp=dict(seed=2 ** 64 - 1), lm_head_phase=True, step_offset=offset)
+    rep.check()
+    assert rep.codes_differ == 0
+
+
 VARIANTS = parity.VARIANTS
 
 
@@ -115,6 +160,20 @@ def _variant_cfg(variant):
     cfg = q4.q4adamw_default_config(q4.RECIPE_CUSTOM)
     cfg.m_codebook, cfg.v_codebook, cfg.m_rule, cfg.v_rule, cfg.eden = variant
     return cfg
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_rule_and_codebook_variants_other_hyperparameters(variant):
+    """The grid at another point of the hyper-parameter space: the all-ones
+    seed, eps_sr = 1e-6, beta1 = 0, beta2 = 0.99, no decay, lr 3e-3, steps
+    crossing 2^32."""
+    cfg = _variant_cfg(variant)
+    w = inputs.custom([(3000,), (40, 300)], grad_kind="masked", seed=43, flags=[inputs.TF_LM_HEAD, 0])
+    hpk = dict(seed=2 ** 64 - 1, eps_sr=1e-6, beta1=0.0, beta2=0.99, weight_decay=0.0, lr=3e-3)
+    _flush(f"variant {variant} other hparams")
+    rep = parity.run(w, "custom", 6, cfg=cfg, hp=hpk, lm_head_phase=True, step_offset=2 ** 32 - 3)
+    rep.check()
+    assert rep.codes_differ == 0
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -257,7 +316,8 @@ def test_qwen3_factored_full_rc():
 def test_edge_magnitudes(recipe):
     """Blocks whose v falls below 2^-96 (the square root's wave-level IEEE
     fallback), BF16-subnormal blocks (block scales below 2^-126: the
-    reciprocal's division fallback), signed zeros (the negative half of the
+    reciprocal's division fallback, finite between 2^-128 and 2^-126 and
+    overflowing below), signed zeros (the negative half of the
     flat bucket table), mixed zeros and large values, and squares that
     underflow; every element, 6 steps."""
     w = inputs.custom([(7 * 128 * 3 + 77,), (21, 140)], grad_kind="edge", seed=51)

@@ -1,0 +1,52 @@
+"""The bandwidth probes (libq4probe.so) do the memory work they claim: the
+byte-mix probe reads and rewrites every byte of its mix (masters, codes and
+scales changed as its arithmetic says, nothing outside touched), the copy
+copies and the read probe reads everything."""
+import numpy as np
+import pytest
+import torch
+
+from bit_adamw_update_amd import probe
+
+pytestmark = pytest.mark.gpu
+
+
+def test_byte_mix_touches_exactly_its_bytes():
+    n = 512 * 37
+    bm = probe.ByteMix(n)
+    before = {f: getattr(bm, f).clone() for f in ("param", "grad", "m_codes", "v_codes", "m_scales", "v_scales")}
+    guard = torch.full((4096,), 7, dtype=torch.uint8, device="cuda")
+    print("byte mix probe", n, flush=True)
+    bm.run()
+    torch.cuda.synchronize()
+    assert probe.byte_mix_bytes(n) == 12 * n + n // 8
+    a = np.float32(0.999)
+    p0 = before["param"].cpu().numpy()
+    q = before["grad"].view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32).reshape(-1, 8)
+    # lane l's gradient term: low half of its first word plus high half of its fourth
+    gq = ((q[:, 0] << 16).view(np.float32) + ((q[:, 7] << 16) & 0xFFFF0000).view(np.float32)).astype(np.float32)
+    expect = (p0.reshape(-1, 8) * a + gq[:, None]).reshape(-1)
+    assert np.array_equal(bm.param.cpu().numpy().view(np.uint32), expect.view(np.uint32))
+    for codes, word in (("m_codes", 1), ("v_codes", 2)):
+        c0 = before[codes].cpu().numpy().view(np.uint32)
+        g32 = before["grad"].view(torch.int16).cpu().numpy().view(np.uint32).reshape(-1, 4)[:, word]
+        assert np.array_equal(getattr(bm, codes).cpu().numpy().view(np.uint32), c0 ^ g32)
+    for sc in ("m_scales", "v_scales"):
+        assert np.array_equal(getattr(bm, sc).cpu().numpy(), before[sc].cpu().numpy() * a)
+    assert torch.equal(bm.grad.view(torch.int16), before["grad"].view(torch.int16))
+    assert int((guard != 7).sum()) == 0
+
+
+def test_copy_and_read():
+    n = (1 << 20) + 16
+    src = torch.randint(1, 1 << 30, (n,), dtype=torch.int32, device="cuda")
+    dst = torch.zeros_like(src)
+    sink = torch.zeros(probe.load_library().q4probe_read_sink_words(), dtype=torch.int32, device="cuda")
+    print("copy and read probes", flush=True)
+    probe.copy(dst, src)
+    probe.read(src, sink)
+    torch.cuda.synchronize()
+    assert torch.equal(dst, src)
+    # the XOR over all threads' partial XORs is the XOR of every word read
+    ref = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
+    assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == ref

@@ -97,7 +97,9 @@ def test_pointer_checks_refuse_host_memory_before_any_work():
     sa.step(pa, g1, 1, flags=q4.HP_CHECK_POINTERS, **w.hp)
     sb.step(pb, g1, 1, **w.hp)
     torch.cuda.synchronize()
-    host = [pb[0].cpu(), pb[1]]
+    # pinned host memory: refused by the check as host memory, and harmless
+    # host RAM (not an unmapped page) should the check ever let it through
+    host = [pb[0].cpu().pin_memory(), pb[1]]
     with pytest.raises(q4.Q4Error) as e:
         sb.step(host, g1, 2, flags=q4.HP_CHECK_POINTERS, **w.hp)
     assert e.value.status == 6
@@ -106,3 +108,34 @@ def test_pointer_checks_refuse_host_memory_before_any_work():
     sb.step(pb, g2, 2, **w.hp)
     torch.cuda.synchronize()
     _same(pa, sa, pb, sb, "after a refused call")
+
+
+@pytest.mark.parametrize("recipe", ["zip_sr", "factored"])
+def test_capture_refuses_a_table_upload(recipe):
+    """A step whose tensor table is not yet in the workspace needs a host
+    upload, which a graph cannot replay safely: under capture it is refused
+    (Q4_ERR_INVALID_ARG) before anything is recorded.  The capture is ended
+    and never replayed; the state is untouched, and the same step then runs
+    eagerly and equals a twin's."""
+    w = inputs.custom(SHAPES, grad_kind="masked", seed=27)
+    dev = torch.device("cuda")
+    consts = w._tensor_consts("cpu")
+    grads = [g.to(dev).reshape(-1).contiguous() for g in w.grads(1, "cpu", consts)]
+    pa, sa = _make(w, recipe, dev)
+    pb, sb = _make(w, recipe, dev)      # never stepped: its workspace holds no table
+    torch.cuda.synchronize()
+    _flush(f"capture refusal {recipe}")
+    graph = torch.cuda.CUDAGraph()
+    refused = None
+    with torch.cuda.graph(graph):
+        try:
+            sb.step(pb, grads, 1, **w.hp)
+        except q4.Q4Error as e:
+            refused = e
+    torch.cuda.synchronize()
+    assert refused is not None and refused.status == 1, refused
+    _same(pa, sa, pb, sb, f"{recipe} after the refused capture")
+    sa.step(pa, grads, 1, **w.hp)
+    sb.step(pb, grads, 1, **w.hp)
+    torch.cuda.synchronize()
+    _same(pa, sa, pb, sb, f"{recipe} eager after the refusal")
