@@ -13,8 +13,10 @@
 // resident groups), but only trivial arithmetic.  Its time is what this byte
 // mix costs on the memory system, whatever the optimizer computes.
 //
-// k_copy is a plain 16-byte-per-lane copy (known bytes read and written),
-// which also calibrates the HBM traffic counters; k_read reads only.
+// k_copy is a plain copy (known bytes read and written, 16 bytes per lane
+// access), which also calibrates the HBM traffic counters; k_read reads
+// only.  Each takes the fastest of the forms measured on gfx950, since it
+// stands for what the memory system can do.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -71,10 +73,21 @@ __global__ __launch_bounds__(256) void k_byte_mix(float* __restrict__ param, con
     }
 }
 
+// Eight 16-byte loads in flight per lane before their stores: the fastest of
+// the copy forms measured on gfx950 (1, 4 or 8 per lane; 2x to 8x the
+// resident work-groups).
 __global__ __launch_bounds__(256) void k_copy(u32x4* __restrict__ dst, const u32x4* __restrict__ src, int64_t n16) {
+    constexpr int U = 8;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
-        ((gptr<u32x4>)dst)[i] = ((gptr<const u32x4>)src)[i];
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + (U - 1) * stride < n16; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = ((gptr<const u32x4>)src)[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < U; ++u) ((gptr<u32x4>)dst)[i + u * stride] = v[u];
+    }
+    for (; i < n16; i += stride) ((gptr<u32x4>)dst)[i] = ((gptr<const u32x4>)src)[i];
 }
 
 __global__ __launch_bounds__(256) void k_read(const u32x4* __restrict__ src, int64_t n16, uint32_t* __restrict__ sink) {
@@ -136,7 +149,7 @@ int q4probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
     if (resident.load() == 0) resident.store(resident_groups(reinterpret_cast<const void*>(k_copy)));
     const int64_t n16 = (int64_t)(bytes / 16);
     const int64_t need = (n16 + 255) / 256;
-    const int64_t cap = 4 * (int64_t)resident.load();
+    const int64_t cap = 8 * (int64_t)resident.load();
     k_copy<<<(unsigned)(need < cap ? need : cap), 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
         reinterpret_cast<u32x4*>(dst), reinterpret_cast<const u32x4*>(src), n16);
     return hipGetLastError() == hipSuccess ? Q4PROBE_OK : Q4PROBE_ERR_HIP;
@@ -148,9 +161,12 @@ int q4probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
     if (!src || !sink || bytes == 0 || bytes % 16 != 0 || !a16(src)) return Q4PROBE_ERR_ARG;
     static std::atomic<int> resident{0};
     if (resident.load() == 0) resident.store(resident_groups(reinterpret_cast<const void*>(k_read)));
+    // one round of resident groups sweeping the buffer together: the
+    // fastest read form measured on gfx950 (more groups, queued behind the
+    // first round, start elsewhere in the buffer and read slower)
     const int64_t n16 = (int64_t)(bytes / 16);
     const int64_t need = (n16 + 255) / 256;
-    int64_t cap = 4 * (int64_t)resident.load();
+    int64_t cap = (int64_t)resident.load();
     if (cap > q4probe_read_sink_words() / 256) cap = q4probe_read_sink_words() / 256;
     k_read<<<(unsigned)(need < cap ? need : cap), 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(
         reinterpret_cast<const u32x4*>(src), n16, sink);

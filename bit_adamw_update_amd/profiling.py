@@ -119,9 +119,14 @@ def _get(row: dict, *keys):
 
 
 def _short(name: str) -> str:
-    """Kernel name without its template arguments and parameter list."""
-    base = name.split("(", 1)[0]
-    return base.replace("(anonymous namespace)::", "").replace("q4::", "").strip()
+    """Kernel name without its return type, namespaces, template arguments
+    and parameter list ("void q4::k_fused_step<0, 2, 3, false>(...)" ->
+    "k_fused_step")."""
+    base = name.replace("(anonymous namespace)::", "").strip()
+    if base.startswith("void "):
+        base = base[5:]
+    base = base.split("(", 1)[0].split("<", 1)[0]
+    return base.rsplit("::", 1)[-1].strip()
 
 
 def trace_durations(out: str) -> dict:
