@@ -81,6 +81,8 @@ _SIGNATURES = {
     "q4adamw_init_state": ([C.POINTER(Q4Config), C.POINTER(Q4Tensor), C.c_int32, C.c_void_p], C.c_int),
     "q4adamw_step": ([C.POINTER(Q4Config), C.POINTER(Q4HParams), C.POINTER(Q4Tensor), C.c_int32, C.c_void_p,
                       C.c_size_t, C.c_void_p], C.c_int),
+    "q4adamw_step_noalloc": ([C.POINTER(Q4Config), C.POINTER(Q4HParams), C.POINTER(Q4Tensor), C.c_int32,
+                              C.c_void_p], C.c_int),
     "q4adamw_dequant_state": ([C.POINTER(Q4Config), C.POINTER(Q4Tensor), C.c_void_p, C.c_void_p, C.c_void_p,
                                C.c_size_t, C.c_void_p], C.c_int),
     "q4adamw_flat_offsets": ([C.POINTER(Q4Tensor), C.c_int32, C.POINTER(C.c_int64), C.POINTER(C.c_int64)], C.c_int),
@@ -211,6 +213,11 @@ def q4adamw_step(cfg: Q4Config, hp: Q4HParams, tensors, ws, ws_bytes: int | None
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
     _check(load_library().q4adamw_step(C.byref(cfg), C.byref(hp), arr, n, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def q4adamw_step_noalloc(cfg: Q4Config, hp: Q4HParams, tensors, stream=None) -> None:
+    arr, n = _tensors(tensors)
+    _check(load_library().q4adamw_step_noalloc(C.byref(cfg), C.byref(hp), arr, n, _stream(stream)))
 
 
 def q4adamw_dequant_state(cfg: Q4Config, tensor: Q4Tensor, m_out, v_out, ws=None, ws_bytes: int | None = None,

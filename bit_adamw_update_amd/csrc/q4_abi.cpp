@@ -713,6 +713,34 @@ q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tens
     return run_step(r, hp, n, P, wsb, stream);
 }
 
+q4_status q4adamw_step_noalloc(const q4_config* cfg, const q4_hparams* hp, const q4_tensor* t, int32_t n,
+                               void* stream) {
+    Resolved r;
+    q4_status s = resolve(cfg, &r);
+    if (s != Q4_OK) return s;
+    if ((s = check_hp(hp)) != Q4_OK) return s;
+    if ((s = check_tensors(r, t, n, true)) != Q4_OK) return s;
+    {
+        Plan sizing;
+        plan_layout(r, t, n, sizing, nullptr);
+        if (sizing.total > kScratchBytes)
+            return fail(Q4_ERR_WORKSPACE,
+                        "the step needs %zu workspace bytes, the library's static scratch holds %zu; use "
+                        "q4adamw_step with a workspace of q4adamw_workspace_bytes",
+                        sizing.total, kScratchBytes);
+    }
+    int dev = 0;
+    if ((s = check_device(&dev)) != Q4_OK) return s;
+    if ((hp->flags & Q4_HP_CHECK_POINTERS) && (s = check_all_pointers(t, n)) != Q4_OK) return s;
+    void* ptr = nullptr;
+    const hipError_t e = scratch_address(&ptr);
+    if (e != hipSuccess) return hip_fail(e, "scratch address");
+    Plan P;
+    uint8_t* wsb = reinterpret_cast<uint8_t*>(ptr);
+    plan_layout(r, t, n, P, wsb);
+    return run_step(r, hp, n, P, wsb, stream);
+}
+
 q4_status q4adamw_dequant_state(const q4_config* cfg, const q4_tensor* t, float* m_out, float* v_out, void* ws,
                                 size_t ws_bytes, void* stream) {
     Resolved r;

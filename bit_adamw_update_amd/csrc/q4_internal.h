@@ -133,6 +133,11 @@ hipError_t launch_fill(void* p, size_t bytes, uint8_t value, hipStream_t stream)
 hipError_t launch_dequant(int mcb, int vcb, const DevTensor& t, int64_t rows, float* m_out, float* v_out,
                           double* ws_partials, float* ws_inv, hipStream_t stream);
 bool variant_supported(const Variant& v);
+// The static device scratch of q4adamw_step_noalloc: kScratchBytes on every
+// device, its address on the current device in *ptr (looked up once per
+// device).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+hipError_t scratch_address(void** ptr);
 void codebook_table(int cb, float* out);  // 16 entries, 256 for the 8-bit maps
 
 }  // namespace q4

@@ -29,6 +29,7 @@
 // out: the two moment recurrences, the denominator and the weight update.
 
 #include <atomic>
+#include <mutex>
 
 #include "q4_internal.h"
 #include "q4_exact.h"
@@ -1383,6 +1384,34 @@ hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, con
         k_step8<false><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     }
     return hipGetLastError();
+}
+
+// Workspace of q4adamw_step_noalloc, for callers that cannot allocate: a
+// static device array, one per device the library runs on, held until the
+// process ends.  Every such call on a device shares it, so calls that
+// overlap on one device race.  Host code never passes the array's name to a
+// kernel or a copy (on the host it only stands for the symbol): it takes
+// the device address that hipGetSymbolAddress gives, once per device with
+// that device current.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_address(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static void* addr[64] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_dequant(int mcb, int vcb, const DevTensor& t, int64_t rows, float* m_out, float* v_out,

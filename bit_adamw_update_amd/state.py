@@ -125,6 +125,16 @@ class Q4State:
         h = self.hparams(step, flags=flags, **hp)
         self._call(api.q4adamw_step, self.cfg, h, self._desc, self.ws, self.ws_bytes, stream)
 
+    def step_noalloc(self, params, grads, step: int, stream=None, **hp) -> None:
+        """One q4adamw_step_noalloc: the workspace is the library's static
+        scratch, which every such call on the device shares, so the table is
+        always uploaded (no Q4_HP_REUSE_TABLE)."""
+        flags = hp.pop("flags", 0) & ~api.HP_REUSE_TABLE
+        self._table(params, grads)
+        self._last_key = None   # the state's own workspace does not hold this call's table
+        h = self.hparams(step, flags=flags, **hp)
+        api.q4adamw_step_noalloc(self.cfg, h, self._desc, stream)
+
     def _call(self, fn, *args) -> None:
         """A call that may upload the tensor table: if it is refused, the
         workspace may not hold the table, so the next call uploads it."""

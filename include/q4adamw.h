@@ -251,6 +251,25 @@ q4_status q4adamw_init_state(const q4_config* cfg, const q4_tensor* t, int32_t n
 q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tensor* t, int32_t n_tensors,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * step as q4adamw_step, with the workspace in a static device array of the
+ * library (Q4ADAMW_NOALLOC_SCRATCH_BYTES on each device it runs on, held
+ * until the process ends) instead of a caller's buffer.  It calls no
+ * hipMalloc, hipFree or other allocating routine.  A tensor list whose
+ * workspace (q4adamw_workspace_bytes) exceeds the array is refused with
+ * Q4_ERR_WORKSPACE before anything is enqueued: every packed and 8-bit set
+ * fits (the tensor table takes 128 bytes per tensor), a factored set fits
+ * while its row/column partial sums do (e.g. Qwen3-0.6B, 27 MiB).  Every
+ * call on a device shares that device's array and leaves the last call's
+ * contents there: two calls that overlap on one device (different streams
+ * without ordering, or host threads) race.  Q4_HP_REUSE_TABLE means "the
+ * previous call on this device, of either entry point's workspace kind,
+ * left this exact tensor list in the array". */
+#define Q4ADAMW_NOALLOC_SCRATCH_BYTES (32u << 20)
+q4_status q4adamw_step_noalloc(const q4_config* cfg, const q4_hparams* hp, const q4_tensor* t, int32_t n_tensors,
+                               void* stream);
+
 /* ---- the step before: gradient accumulation, norm, clipping ------------
  * [A] "State representation": microbatches stream into BF16 gradient shards
  * (no FP32 main gradient), and the gradient norm and clipping work on those
