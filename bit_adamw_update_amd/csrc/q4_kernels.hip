@@ -123,7 +123,7 @@ template <int MCB, int VCB, bool FLAT> struct StepLds {
     BucketEntry enc_m[FLAT ? 1 : Enc<MCB>::SIZE];
     BucketEntry enc_v[Enc<VCB>::SIZE];
     FloorEntry floor_v[(VCB == Q4_CB_DYN4 && !FLAT) ? Enc<VCB>::NPOS : 1];
-    BucketEntry flat[FLAT ? kFlatSlots : 1];  // m entries; v floor entries as {thr, lo}
+    alignas(16) BucketEntry flat[FLAT ? kFlatAlloc : 1];  // m entries; v floor entries as {thr, lo}
     float lev_m[16], lev_v[16];  // sorted levels (rare SR paths)
 };
 
@@ -526,7 +526,8 @@ void k_fused_step(const DevTensor* __restrict__ tab,
         for (int i = threadIdx.x; i < Enc<VCB>::SIZE; i += blockDim.x) lds.enc_v[i] = gv[i];
         if constexpr (FLAT) {
             // each flat slot takes the compact entry of a value inside it
-            for (int i = threadIdx.x; i < kFlatSlots; i += blockDim.x) lds.flat[i] = flat_slot<MCB>(i);
+            // (built at compile time, copied in 16-byte pieces)
+            copy_flat_table<MCB>(lds.flat);
         } else {
             for (int i = threadIdx.x; i < Enc<MCB>::SIZE; i += blockDim.x) lds.enc_m[i] = gm[i];
             if constexpr (VCB == Q4_CB_DYN4)

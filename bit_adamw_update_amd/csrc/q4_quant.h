@@ -225,6 +225,7 @@ __device__ __forceinline__ int floor_index(float thr, int lo, float x) { return 
 constexpr int kFlatPos = (127 << 3) + 1;          // bits >> 20 of x in [+0, 1]
 constexpr int kFlatNeg = 2048;                     // bits >> 20 of x in [-1, -0]
 constexpr int kFlatSlots = kFlatNeg + kFlatPos;
+constexpr int kFlatAlloc = (kFlatSlots + 1) & ~1;  // slots held, a whole number of 16-byte pieces
 static_assert(2 * kFlatPos <= kFlatNeg, "the floor entries must fit between the two halves");
 
 template <int VCB, int VRULE> constexpr bool flat_tables() {
@@ -237,20 +238,56 @@ __device__ __forceinline__ uint32_t flat_m_slot(float x) { return __float_as_uin
 __device__ __forceinline__ uint32_t flat_floor_slot(float x) {
     return kFlatPos + __builtin_amdgcn_ubfe(__float_as_uint(x), 20, 11);
 }
-// Flat slot i: the compact entry of a value inside it (m entries of MCB,
-// Dyn4 floor entries as {thr, lo}, unused slots never exceeded).
-template <int MCB> __device__ __forceinline__ BucketEntry flat_slot(int i) {
-    BucketEntry d{3.0f, 0};
-    if (i < kFlatPos) {
-        d = enc_table_global<MCB>()[bucket_index<MCB>(bits2f((uint32_t)i << 20))];
-    } else if (i >= kFlatNeg) {
-        d = enc_table_global<MCB>()[bucket_index<MCB>(bits2f(0x80000000u | ((uint32_t)(i - kFlatNeg) << 20)))];
-    } else if (i - kFlatPos < kFlatPos) {
-        const FloorEntry& f = c_floor_dyn4.e[bucket_index<Q4_CB_DYN4>(bits2f((uint32_t)(i - kFlatPos) << 20))];
-        d.thr = f.thr;
-        d.base = f.lo;
+// The compact bucket index of x, as bucket_index computes it, for building
+// tables at compile time.
+template <int CB> constexpr uint32_t bucket_index_c(float x) {
+    using E = Enc<CB>;
+    const uint32_t u = f2bits(x);
+    uint32_t raw = (u >> (23 - E::MB)) & ((1u << (8 + E::MB)) - 1u);
+    raw = raw < (uint32_t)(E::EMIN << E::MB) ? (uint32_t)(E::EMIN << E::MB) : raw;
+    raw = raw > (uint32_t)(127 << E::MB) ? (uint32_t)(127 << E::MB) : raw;
+    uint32_t idx = raw - (uint32_t)(E::EMIN << E::MB);
+    if (E::SIGNED) idx += (u >> 31) * (uint32_t)E::PAD;
+    return idx;
+}
+
+// The whole flat table of an m map, built at compile time: slot i takes the
+// compact entry of a value inside it (m entries of MCB, Dyn4 floor entries
+// as {thr, lo}, unused slots never exceeded).  A work-group copies it into
+// LDS with 16-byte loads instead of forming its 3,065 slots itself.
+template <int MCB> struct alignas(16) FlatTable {
+    BucketEntry e[kFlatAlloc];
+    constexpr FlatTable() : e() {
+        constexpr EncTable<MCB> enc{};
+        constexpr FloorTable<Q4_CB_DYN4> fl{};
+        for (int i = 0; i < kFlatAlloc; ++i) {
+            BucketEntry d{3.0f, 0};
+            if (i < kFlatPos) {
+                d = enc.e[bucket_index_c<MCB>(bits2f((uint32_t)i << 20))];
+            } else if (i >= kFlatNeg) {
+                d = enc.e[bucket_index_c<MCB>(bits2f(0x80000000u | ((uint32_t)(i - kFlatNeg) << 20)))];
+            } else if (i - kFlatPos < kFlatPos) {
+                const FloorEntry& f = fl.e[bucket_index_c<Q4_CB_DYN4>(bits2f((uint32_t)(i - kFlatPos) << 20))];
+                d.thr = f.thr;
+                d.base = f.lo;
+            }
+            if (i < kFlatSlots) e[i] = d;
+            else e[i] = BucketEntry{3.0f, 0};
+        }
     }
-    return d;
+};
+static_assert(sizeof(BucketEntry) * kFlatAlloc % 16 == 0, "the flat table is copied in 16-byte pieces");
+__device__ const FlatTable<Q4_CB_NF4> c_flat_nf4 = FlatTable<Q4_CB_NF4>();
+__device__ const FlatTable<Q4_CB_SDYN4> c_flat_sdyn4 = FlatTable<Q4_CB_SDYN4>();
+
+// Copies the flat table of MCB into `dst` (LDS, 16-byte aligned, kFlatAlloc
+// entries); every thread of the work-group takes part.
+template <int MCB> __device__ __forceinline__ void copy_flat_table(BucketEntry* dst) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(MCB == Q4_CB_NF4 ? c_flat_nf4.e : c_flat_sdyn4.e);
+    u32x4_t* d = reinterpret_cast<u32x4_t*>(dst);
+    constexpr int n16 = (int)(sizeof(BucketEntry) * kFlatAlloc / 16);
+    for (int i = threadIdx.x; i < n16; i += blockDim.x) d[i] = src[i];
 }
 
 // ---------------------------------------------------------------------------

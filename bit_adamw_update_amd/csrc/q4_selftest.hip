@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kWhatSqrt = 0, kWhatInvScale = 1;
+constexpr int kWhatSqrt = 0, kWhatInvScale = 1, kWhatSqrtFaithful = 2, kWhatSqrtSmall = 3;
 constexpr int kFormFast = 0, kFormHardware = 1;
 
 __device__ __forceinline__ double mid_below(uint32_t y) {
@@ -36,6 +36,27 @@ __device__ bool is_sqrt_rn(uint32_t x, uint32_t y) {
     const double lo = mid_below(y), hi = mid_above(y), xd = (double)__uint_as_float(x);
     return lo * lo < xd && xd < hi * hi;
 }
+// y is one of the two floats around sqrt(x) (a faithful square root): x = +0
+// and +inf give themselves, and otherwise sqrt(x) lies strictly between the
+// float neighbours of y, i.e. prev(y)^2 < x < next(y)^2 (exact in binary64).
+// Every sqrt(x) of a positive float is a normal float, so prev(y) is too.
+__device__ bool is_sqrt_faithful(uint32_t x, uint32_t y) {
+    if (x == 0u || x == 0x7F800000u) return y == x;
+    if (!finite_positive(y) || y <= 0x00800000u) return false;
+    const double lo = (double)__uint_as_float(y - 1u);
+    const double hi = y + 1u == 0x7F800000u ? 0x1p128 : (double)__uint_as_float(y + 1u);
+    const double xd = (double)__uint_as_float(x);
+    return lo * lo < xd && xd < hi * hi;
+}
+
+// For a subnormal x: 0 <= y <= 2^-63 (every root of a subnormal is below
+// 2^-63), i.e. the hardware root is off by less than 2^-63 in absolute terms.
+__device__ bool is_sqrt_small(uint32_t x, uint32_t y) {
+    (void)x;
+    const float yf = __uint_as_float(y);
+    return yf >= 0.0f && yf <= 0x1p-63f;
+}
+
 // y == RN(1/s) when s > 0 and RN(1/s) is finite, else +0, for every s >= +0,
 // +inf and NaN included (-> +0).  RN(1/s) overflows iff 1/s reaches the
 // midpoint 2^128 - 2^103 between the largest float and 2^128, i.e. iff
@@ -62,6 +83,10 @@ __global__ void __launch_bounds__(256) k_sweep(uint64_t lo, uint64_t hi, unsigne
         if constexpr (WHAT == kWhatSqrt) {
             const float r = FORM == kFormFast ? q4::sqrt_rn_normal(x) : __builtin_amdgcn_sqrtf(x);
             ok = is_sqrt_rn(b, __float_as_uint(r));
+        } else if constexpr (WHAT == kWhatSqrtFaithful) {
+            ok = is_sqrt_faithful(b, __float_as_uint(__builtin_amdgcn_sqrtf(x)));
+        } else if constexpr (WHAT == kWhatSqrtSmall) {
+            ok = is_sqrt_small(b, __float_as_uint(__builtin_amdgcn_sqrtf(x)));
         } else {
             const float r = FORM == kFormFast ? q4::inv_scale(x) : (x >= 0x1p-126f ? __builtin_amdgcn_rcpf(x) : 0.0f);
             ok = is_inv_scale(b, __float_as_uint(r));
@@ -151,7 +176,7 @@ struct QuantLds {
     q4::BucketEntry enc[q4::Enc<Q4_CB_NF4>::SIZE > q4::Enc<Q4_CB_SDYN4>::SIZE ? q4::Enc<Q4_CB_NF4>::SIZE
                                                                                 : q4::Enc<Q4_CB_SDYN4>::SIZE];
     q4::FloorEntry floor[q4::Enc<Q4_CB_DYN4>::NPOS];
-    q4::BucketEntry flat[q4::kFlatSlots];
+    alignas(16) q4::BucketEntry flat[q4::kFlatAlloc];
     q4::Step8Lds t8;
     float mids8[256];  // the 8-bit map's midpoints ascending, from its decoded levels
 };
@@ -199,9 +224,9 @@ __global__ void __launch_bounds__(256) k_quant(uint64_t lo, uint64_t hi, unsigne
     } else if constexpr (CHECK == QC_FLOOR_DYN4) {
         for (int i = t; i < q4::Enc<Q4_CB_DYN4>::NPOS; i += blockDim.x) L.floor[i] = q4::c_floor_dyn4.e[i];
     } else if constexpr (CHECK == QC_FLAT_NF4 || CHECK == QC_FLAT_FLOOR) {
-        for (int i = t; i < q4::kFlatSlots; i += blockDim.x) L.flat[i] = q4::flat_slot<Q4_CB_NF4>(i);
+        q4::copy_flat_table<Q4_CB_NF4>(L.flat);     // the copy the step kernels make
     } else if constexpr (CHECK == QC_FLAT_SDYN4) {
-        for (int i = t; i < q4::kFlatSlots; i += blockDim.x) L.flat[i] = q4::flat_slot<Q4_CB_SDYN4>(i);
+        q4::copy_flat_table<Q4_CB_SDYN4>(L.flat);
     }
     constexpr bool EIGHT = CHECK == QC_RTN8_M || CHECK == QC_RTN8_V;
     constexpr int NMID = CHECK == QC_RTN8_M ? 254 : 255;
@@ -312,20 +337,26 @@ extern "C" {
 // Checks q4::sqrt_rn_normal (what 0) or q4::inv_scale (what 1) on every
 // float bit pattern in [lo, hi) (hi <= 2^32) against the definition above;
 // form 1 checks the bare hardware square root or reciprocal instead, which
-// is not correctly rounded.  Writes the number of inputs whose result
+// is not correctly rounded.  What 2 checks that the bare hardware square
+// root is faithful, what 3 that it is in [0, 2^-63] (for subnormal inputs;
+// form ignored).  Writes the number of inputs whose result
 // differs and the smallest such bit pattern (0xFFFFFFFF if none) to host
 // memory.  Returns 0, -1 for invalid arguments, or a HIP error code.
 // Synchronous, on the current device's null stream.
 int q4st_sweep(int what, int form, uint64_t lo, uint64_t hi, unsigned long long* mismatches,
                uint32_t* first_bad) {
-    if (what < 0 || what > 1 || form < 0 || form > 1 || lo > hi || hi > (1ull << 32) || !mismatches ||
+    if (what < 0 || what > 3 || form < 0 || form > 1 || lo > hi || hi > (1ull << 32) || !mismatches ||
         !first_bad)
         return -1;
     DevCounters c;
     hipError_t e = c.init();
     if (e != hipSuccess) return (int)e;
     if (hi > lo) {
-        if (what == kWhatSqrt && form == kFormFast)
+        if (what == kWhatSqrtFaithful)
+            k_sweep<kWhatSqrtFaithful, kFormHardware><<<kGrid, kThreads>>>(lo, hi, c.bad, c.first);
+        else if (what == kWhatSqrtSmall)
+            k_sweep<kWhatSqrtSmall, kFormHardware><<<kGrid, kThreads>>>(lo, hi, c.bad, c.first);
+        else if (what == kWhatSqrt && form == kFormFast)
             k_sweep<kWhatSqrt, kFormFast><<<kGrid, kThreads>>>(lo, hi, c.bad, c.first);
         else if (what == kWhatSqrt)
             k_sweep<kWhatSqrt, kFormHardware><<<kGrid, kThreads>>>(lo, hi, c.bad, c.first);

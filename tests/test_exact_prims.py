@@ -29,7 +29,7 @@ import pytest
 
 from bit_adamw_update_amd import build
 
-SQRT, INV_SCALE = 0, 1
+SQRT, INV_SCALE, SQRT_FAITHFUL, SQRT_SMALL = 0, 1, 2, 3
 FAST, BARE = 0, 1
 F32_INF = 0x7F800000
 ONE, NEG_ZERO, NEG_ONE = 0x3F800000, 0x80000000, 0xBF800000
@@ -73,7 +73,7 @@ def test_selftest_library_exports_and_validates():
         assert f" T {sym}" in out
     n, first = ctypes.c_ulonglong(0), ctypes.c_uint32(0)
     # rejected before any device call
-    assert lib.q4st_sweep(2, 0, 0, 1, ctypes.byref(n), ctypes.byref(first)) == -1
+    assert lib.q4st_sweep(4, 0, 0, 1, ctypes.byref(n), ctypes.byref(first)) == -1
     assert lib.q4st_sweep(0, 2, 0, 1, ctypes.byref(n), ctypes.byref(first)) == -1
     assert lib.q4st_sweep(0, 0, 5, 4, ctypes.byref(n), ctypes.byref(first)) == -1
     assert lib.q4st_sweep(0, 0, 0, (1 << 32) + 1, ctypes.byref(n), ctypes.byref(first)) == -1
@@ -97,6 +97,20 @@ def test_sqrt_rn_normal_exhaustive():
     # below 2^-96 the residuals underflow and the correction fails, which is
     # why a wave with such an input takes the IEEE square root instead
     assert _sweep(lib, SQRT, FAST, 1, 0x0F800000)[0] > 0
+
+
+@pytest.mark.gpu
+def test_hardware_sqrt_bounds():
+    """Where a rule does not decide codes from sqrt(v1), the weight update's
+    denominator sqrt(v1) rsbc2 + eps takes the bare hardware square root.
+    It is faithful (one of the two floats around sqrt(x)) for +0, every
+    normal float and +inf; for every subnormal input it is not, but it stays
+    in [0, 2^-63], so the denominator moves by at most 2^-63 rsbc2 there."""
+    lib = _lib()
+    assert _sweep(lib, SQRT_FAITHFUL, BARE, 0, 1) == (0, 0xFFFFFFFF)
+    assert _sweep(lib, SQRT_FAITHFUL, BARE, 0x00800000, F32_INF + 1) == (0, 0xFFFFFFFF)
+    assert _sweep(lib, SQRT_FAITHFUL, BARE, 1, 0x00800000)[0] > 0
+    assert _sweep(lib, SQRT_SMALL, BARE, 1, 0x00800000) == (0, 0xFFFFFFFF)
 
 
 @pytest.mark.gpu
