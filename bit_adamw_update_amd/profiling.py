@@ -23,9 +23,9 @@ The summaries carry a hash of the step kernels' device source (without
 comments and blank space); ``bench.py`` reports the counted traffic only while
 that hash matches the current source.
 
-Usage (on a machine with the GPU; the box writes under gpurun_out/):
-  python -m bit_adamw_update_amd.profiling collect --workload gpt-2.7b --recipe zip_sr --out gpurun_out/prof
-  python -m bit_adamw_update_amd.profiling summarize --workload gpt-2.7b --recipe zip_sr --out gpurun_out/prof
+Usage (on a machine with the GPU; summaries go to --dest, raw CSV to --out):
+  python -m bit_adamw_update_amd.profiling both --workload gpt-2.7b --recipe zip_sr --dest profiles
+  python -m bit_adamw_update_amd.profiling both --workload gpt-2.7b --recipe zip_sr --step-before --passes trace
 """
 from __future__ import annotations
 
@@ -67,14 +67,19 @@ def step_kernel(recipe: str) -> str:
     return {"block8": "k_step8", "fp32": "k_fp32_step"}.get(recipe, "k_fused_step")
 
 
+STEP_BEFORE = False   # set by --step-before: profile bench.py --step-before instead
+
+
 def bench_args(workload: str, recipe: str, steps: int, warmup: int) -> list:
     """The benchmark command, relative to the repository root."""
+    extra = ["--step-before", "--max-grad-norm", "1.0"] if STEP_BEFORE else []
     return ["python3", "bench.py", "--workload", workload, "--recipe", recipe, "--steps", str(steps), "--warmup",
-            str(warmup), "--no-variants", "--no-cpu-baseline"]
+            str(warmup), "--no-variants", "--no-cpu-baseline", *extra]
 
 
 def pass_command(name: str, out: str, workload: str, recipe: str, steps: int, warmup: int) -> list:
-    d = os.path.join(os.path.relpath(out, ROOT), name)
+    rel = os.path.relpath(out, ROOT)
+    d = os.path.join(out if rel.startswith("..") else rel, name)
     return ["rocprofv3", *PASSES[name], "--output-format", "csv", "-d", d, "-o", name, "--",
             *bench_args(workload, recipe, steps, warmup)]
 
@@ -91,7 +96,7 @@ def collect(workload: str, recipe: str, out: str, steps: int, warmup: int, passe
         # rocprofv3 itself may end with a segmentation fault after the program
         # finished and its files are complete: accept that when the bench's
         # JSON line was printed
-        if rc != 0 and not any(l.startswith("{\"metric\"") for l in open(os.path.join(out, f"{name}.log"))):
+        if rc != 0 and not any(l.startswith("{") for l in open(os.path.join(out, f"{name}.log"))):
             print("\n".join(tail), flush=True)
             return rc
     return 0
@@ -165,7 +170,8 @@ def summarize(workload: str, recipe: str, out: str, steps: int, warmup: int, des
     wl = inputs.WORKLOADS[workload]()
     kern = step_kernel(recipe)
     alg = bench.alg_bytes(wl, recipe)
-    head = [f"# rocprofv3 summary: {kern}, {workload}, recipe {recipe}"]
+    what = "the last microbatch's accumulation pass and the clipped step after it" if STEP_BEFORE else "the step"
+    head = [f"# rocprofv3 summary: {kern}, {workload}, recipe {recipe} ({what})"]
     src = [f"kernel_source_sha256_16: {kernel_hash()}"]
     # -- trace
     dur = trace_durations(out)
@@ -182,7 +188,7 @@ def summarize(workload: str, recipe: str, out: str, steps: int, warmup: int, des
         avg = sum(timed) / len(timed) / 1e9
         lines.append(f"step_kernel: {kern}")
         lines.append(f"step_launches_timed: {len(timed)}")
-        lines.append(f"step_avg_ms_timed: {avg * 1e3:.4f}")
+        lines.append(f"step_avg_ms_timed: {avg * 1e3:.6f}")
         lines.append(f"alg_bytes_per_launch: {alg}")
         lines.append(f"alg_gbs: {alg / avg / 1e9:.1f}")
         lines.append(f"frac_of_8tbs: {alg / avg / 8e12:.4f}")
@@ -190,7 +196,8 @@ def summarize(workload: str, recipe: str, out: str, steps: int, warmup: int, des
     if bm:
         v = dur[bm[0]]
         lines.append(f"byte_mix_probe_avg_ms: {sum(v[-steps:]) / len(v[-steps:]) / 1e6:.4f}")
-    trace_file = os.path.join(dest, f"{kern}_{workload}_{recipe}_trace.txt")
+    prefix = f"accumulate_{workload}_{recipe}" if STEP_BEFORE else f"{kern}_{workload}_{recipe}"
+    trace_file = os.path.join(dest, f"{prefix}_trace.txt")
     os.makedirs(dest, exist_ok=True)
     with open(trace_file, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -235,7 +242,9 @@ def summarize(workload: str, recipe: str, out: str, steps: int, warmup: int, des
     v = per_dispatch(cs, kern, "SQ_INSTS_LDS")
     if v:
         lines.append(f"lds_insts_per_element: {sum(v) / len(v) * 64 / wl.numel:.3f}")
-    counters_file = os.path.join(dest, f"{kern}_{workload}_{recipe}_counters.txt")
+    if not (cf or cw or cs):   # a trace-only run: no counter summary
+        return trace_file, None
+    counters_file = os.path.join(dest, f"{prefix}_counters.txt")
     with open(counters_file, "w") as f:
         f.write("\n".join(lines) + "\n")
     return trace_file, counters_file
@@ -246,22 +255,27 @@ def main():
     ap.add_argument("action", choices=["collect", "summarize", "both"])
     ap.add_argument("--workload", default="gpt-2.7b")
     ap.add_argument("--recipe", default="zip_sr")
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--out", default="/tmp/q4prof", help="raw rocprofv3 output (large; kept out of the repository)")
     ap.add_argument("--dest", default=os.path.join(ROOT, "gpurun_out", "profiles"),
                     help="where the text summaries go (copied into profiles/ afterwards)")
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--passes", default="trace,fetch,write,sq")
     ap.add_argument("--limit", type=int, default=180, help="seconds per pass")
+    ap.add_argument("--step-before", action="store_true",
+                    help="profile the accumulation pass and the clipped step after it (bench.py --step-before)")
     a = ap.parse_args()
-    out = os.path.join(a.out, f"{a.workload}_{a.recipe}")
+    global STEP_BEFORE
+    STEP_BEFORE = a.step_before
+    out = os.path.join(a.out, f"{a.workload}_{a.recipe}" + ("_accumulate" if a.step_before else ""))
     if a.action in ("collect", "both"):
         rc = collect(a.workload, a.recipe, out, a.steps, a.warmup, a.passes.split(","), a.limit)
         if rc != 0:
             sys.exit(rc)
     if a.action in ("summarize", "both"):
         for f in summarize(a.workload, a.recipe, out, a.steps, a.warmup, a.dest):
-            print(f"[profiling] wrote {f}", flush=True)
+            if f:
+                print(f"[profiling] wrote {f}", flush=True)
 
 
 if __name__ == "__main__":
