@@ -45,7 +45,7 @@ class TensorSpec:
 class Workload:
     name: str
     tensors: list
-    grad_kind: str            # "masked" | "logscale" | "microbatch4" | "edge"
+    grad_kind: str            # "masked" | "logscale" | "microbatch4" | "edge" | "nonfinite"
     steps: int
     recipes: tuple
     seed: int = 0
@@ -109,6 +109,35 @@ class Workload:
         y = torch.where(mixed & (idx % 61 == 0), x * 1e3, y)
         return y.to(torch.bfloat16).reshape(shape)
 
+    # non-finite classes of the "nonfinite" kind, one per 128-block in turn:
+    # (offset in the block, value) pairs written over Student-t gradients;
+    # None in place of a list sets the whole block
+    NONFINITE_CLASSES = (
+        [],                                                   # finite
+        [(37, float("nan"))],                                 # one NaN
+        [(5, float("inf"))],                                  # one +inf
+        [(100, float("-inf"))],                               # one -inf
+        [(64, 1e30)],                                         # finite, its square overflows FP32
+        None,                                                 # every element NaN
+        [(0, float("nan")), (127, float("-inf"))],            # NaN and -inf
+        [],                                                   # finite
+    )
+
+    def _nonfinite(self, shape, g, device) -> torch.Tensor:
+        """Student-t gradients (scale 1e-3) with NaN, +-inf and overflowing
+        values at fixed places of each block class, the same every step."""
+        x = (self._student_t3(shape, g, device) * 1e-3).reshape(-1)
+        n = x.numel()
+        for b in range((n + 127) // 128):
+            cls = self.NONFINITE_CLASSES[b % len(self.NONFINITE_CLASSES)]
+            if cls is None:
+                x[128 * b:min(n, 128 * b + 128)] = float("nan")
+                continue
+            for off, val in cls:
+                if 128 * b + off < n:
+                    x[128 * b + off] = val
+        return x.to(torch.bfloat16).reshape(shape)
+
     def grads(self, step: int, device="cpu", consts=None) -> list:
         """BF16 gradients of `step` (1-based), one tensor per parameter."""
         if consts is None:
@@ -122,6 +151,8 @@ class Workload:
                 out.append(x.mul_(scale).to(torch.bfloat16))
             elif self.grad_kind == "edge":
                 out.append(self._edge(t.shape, g, device))
+            elif self.grad_kind == "nonfinite":
+                out.append(self._nonfinite(t.shape, g, device))
             elif self.grad_kind == "logscale":
                 out.append(self._student_t3(t.shape, g, device).mul_(c).to(torch.bfloat16))
             else:  # four microbatches, accumulated in BF16 in order

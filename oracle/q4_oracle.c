@@ -48,6 +48,13 @@
  *     folded into the stored scale.
  *   - RTN ties go to the lower code; SR draws from Philox4x32-10 keyed on
  *     (seed, step, tensor id, stream, element index).
+ *   - Non-finite moments (NaN or infinite gradients): the IEEE operations
+ *     written here decide.  Block maxima take a value only when it compares
+ *     greater (NaN skipped, +inf kept); an infinite scale has the inverse
+ *     1/inf = 0; normalized values are clamped by comparison, which a NaN
+ *     fails, and a NaN then lies above no midpoint and no level, so it takes
+ *     sorted index 0 under every rule; EDEN's ratio over a block holding one
+ *     is 1 (its sums are NaN); the weight follows IEEE arithmetic.
  */
 #include <math.h>
 #include <stdint.h>
@@ -345,6 +352,22 @@ static float or_scale_inverse(float s) {
     return isinf(inv) ? 0.0f : inv;
 }
 
+/* Clamps of a normalized value to the range of the levels, [-1, 1] for a
+ * signed map and at most 1 for an unsigned one: x = value * (1/s) can pass
+ * the end of the range by a rounding.  Written as comparisons, which a NaN
+ * fails, so a NaN (a NaN moment, or an infinite one normalized by 1/inf =
+ * 0) passes through and takes sorted index 0 in the quantizers (reading of
+ * non-finite moments). */
+static float or_clamp_signed(float x) {
+    if (x > 1.0f) x = 1.0f;
+    if (x < -1.0f) x = -1.0f;
+    return x;
+}
+static float or_clamp_unsigned(float x) {
+    if (x > 1.0f) x = 1.0f;
+    return x;
+}
+
 /* First moment of one block: absmax scale, normalization, then RTN or
  * state-space SR (the LM-head rule of [P] Table 2) over the signed map.
  * m1[0..n) are the unquantized values; writes n nibbles starting at
@@ -356,9 +379,7 @@ static float or_requant_m_levels(const or_levels* lvp, int rule, const float* m1
     for (int k = 0; k < n; ++k) { float a = fabsf(m1[k]); if (a > s) s = a; }
     float inv = or_scale_inverse(s);
     for (int k = 0; k < n; ++k) {
-        float x = m1[k] * inv;
-        if (x > 1.0f) x = 1.0f;
-        if (x < -1.0f) x = -1.0f;
+        float x = or_clamp_signed(m1[k] * inv);
         float u = rule == OR_STATE_SR ? or_uniform(seed, step, tensor_id, 0, elem0 + (uint64_t)k) : 0.0f;
         int idx = or_choose(&lv, rule, x, s, 0.0f, 0.0f, u);
         or_put_nibble(codes, j0 + k, lv.code[idx]);
@@ -379,8 +400,7 @@ static float or_requant_v_levels(const or_levels* lvp, int rule, int eden, const
     float xx[OR_BLOCK], xq[OR_BLOCK];
     for (int k = 0; k < OR_BLOCK; ++k) { xx[k] = 0.0f; xq[k] = 0.0f; }
     for (int k = 0; k < n; ++k) {
-        float x = v1[k] * inv;
-        if (x > 1.0f) x = 1.0f;
+        float x = or_clamp_unsigned(v1[k] * inv);
         float sv = sqrtf(v1[k]);
         int needs_u = rule == OR_STATE_SR || rule == OR_UPDATE_SR;
         float u = needs_u ? or_uniform(seed, step, tensor_id, 1, elem0 + (uint64_t)k) : 0.0f;
@@ -744,8 +764,8 @@ int or_step8_window(const or_hparams* hp, const or_window* w) {
         }
         float im = or_scale_inverse(sm), iv = or_scale_inverse(sv);
         for (int k = 0; k < n; ++k) {
-            float xm = fminf(fmaxf(m1[k] * im, -1.0f), 1.0f);
-            float xv = fminf(v1[k] * iv, 1.0f);
+            float xm = or_clamp_signed(m1[k] * im);
+            float xv = or_clamp_unsigned(v1[k] * iv);
             w->m_codes[off + k] = (uint8_t)or_rtn8(&lvm, xm);
             w->v_codes[off + k] = (uint8_t)or_rtn8(&lvv, xv);
         }

@@ -2,7 +2,7 @@
 
 Each case plants one mistake in a copy of ``oracle/q4_oracle.c`` (a swapped
 nibble order, a decode without its block scale, a dropped term, a wrong sign,
-a transposed operand, a wrong Philox word ...), builds that copy with the
+a transposed operand, a wrong Philox word, NaN handled another way ...), builds that copy with the
 oracle's own flags, and runs the pin suites against it in a child process
 (the oracle loads the library that Q4_ORACLE_LIB names).  The pins must fail
 for every mutant.  The mistakes are planted in the CPU oracle only.
@@ -17,7 +17,7 @@ import pytest
 from oracle import oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PIN_FILES = ["tests/test_oracle_decode_pins.py", "tests/test_oracle_pins.py"]
+PIN_FILES = ["tests/test_oracle_decode_pins.py", "tests/test_oracle_pins.py", "tests/test_oracle_nonfinite.py"]
 
 # (name, text in q4_oracle.c, replacement); the first occurrence is replaced
 MUTANTS = [
@@ -60,6 +60,12 @@ MUTANTS = [
      "for (int j = 0; j + 1 < lv->n; ++j) if (x >= lv->mid[j]) ++k;"),
     ("absmax without the absolute value", "for (int k = 0; k < n; ++k) { float a = fabsf(m1[k]); if (a > s) s = a; }",
      "for (int k = 0; k < n; ++k) { float a = m1[k]; if (a > s) s = a; }"),
+    # non-finite moments: a clamp that sends NaN to the top of the v range,
+    # and a block maximum that lets NaN through
+    ("v clamp sends NaN to 1", "static float or_clamp_unsigned(float x) {\n    if (x > 1.0f) x = 1.0f;",
+     "static float or_clamp_unsigned(float x) {\n    x = fminf(x, 1.0f);"),
+    ("v maximum keeps NaN", "for (int k = 0; k < n; ++k) if (v1[k] > s) s = v1[k];",
+     "for (int k = 0; k < n; ++k) if (!(v1[k] <= s)) s = v1[k];"),
 ]
 
 

@@ -17,7 +17,7 @@ import pytest
 from oracle import oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-PIN_FILES = ["tests/test_oracle_decode_pins.py", "tests/test_oracle_pins.py"]
+PIN_FILES = ["tests/test_oracle_decode_pins.py", "tests/test_oracle_pins.py", "tests/test_oracle_nonfinite.py"]
 SAN_FLAGS = ["-O1", "-g", "-std=c11", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
              "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
 
