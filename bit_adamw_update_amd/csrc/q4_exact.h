@@ -49,6 +49,19 @@ __device__ __forceinline__ float inv_scale(float s) {
     return r <= 0x1.fffffep127f ? r : 0.0f;
 }
 
+// The clamp of a normalized second moment, v * (1/s) (+0 or more, or NaN),
+// to the level range [0, 1], with NaN sent to 0: the stored second moment
+// takes sorted index 0 for a NaN under every rule, and 0 has sorted index 0
+// in every unsigned map.  v_med3_f32 with a NaN operand returns the smallest
+// of the others, and the compiler folds med3(x, 0, 1) into the clamp bit of
+// the multiply that forms x (NaN to 0 in the kernels' clamp mode); checked
+// in that form over every input.
+__device__ __forceinline__ float clamp_unit(float x) { return __builtin_amdgcn_fmed3f(x, 0.0f, 1.0f); }
+// v * inv clamped as above.  Written as v * inv + 0, which rounds as the
+// product does (v * inv >= +0, so adding +0 changes no bit), so that the
+// multiply-add carries the clamp even where the plain product is shared.
+__device__ __forceinline__ float normalize_v(float v, float inv) { return clamp_unit(__builtin_fmaf(v, inv, 0.0f)); }
+
 // ds_bpermute byte addresses of the 8 nibbles of `codes` for lane row + code,
 // rb4x4 = 4 * row (the row's first lane) in every byte: byte j of `ev` is
 // 4 * nibble(2j) + 4 * row, of `od` 4 * nibble(2j + 1) + 4 * row (the two

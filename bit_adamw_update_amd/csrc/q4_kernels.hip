@@ -396,7 +396,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             draw_v(k);
-            const float x = fminf(v1[k] * inv_v, 1.0f);
+            const float x = normalize_v(v1[k], inv_v);
             // lower level: the floor bucket gives it directly; an exact level
             // hit needs no draw (the top level 1 can only be hit exactly)
             float fthr;
@@ -427,7 +427,11 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         draw_v(k);
-        const float x = fminf(v1[k] * inv_v, 1.0f);
+        // x is the clamped value (a NaN becomes 0, of sorted index 0); the
+        // EDEN sums take the unclamped one's NaN through nan0 (+0 or NaN)
+        const float xr = v1[k] * inv_v;
+        const float x = clamp_unit(xr);
+        const float nan0 = xr - xr;
         int idx = rtn_index(bucket_of<VCB>(lds.enc_v, x), x);
         float q = lds.lev_v[idx];  // level(idx)
         if constexpr (VRULE != Q4_RULE_STATE_RTN) {
@@ -458,8 +462,8 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
             if (eden) q = lds.lev_v[idx];
         }
         vword |= (uint32_t)idx << (4 * k);
-        xx[k] = x * x;
-        xq[k] = x * q;
+        xx[k] = __builtin_fmaf(x, x, nan0);
+        xq[k] = __builtin_fmaf(x, q, nan0);
     }
     }
     if (FULL || nv == 8) {
@@ -708,7 +712,7 @@ __device__ __forceinline__ void step8_chunk(const DevTensor& T, const int64_t lc
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
         const float xm = fminf(fmaxf(m1[k] * inv_m, -1.0f), 1.0f);
-        const float xv = fminf(v1[k] * inv_v, 1.0f);
+        const float xv = normalize_v(v1[k], inv_v);
         mw[k >> 2] |= rtn8_m(lds, xm) << (8 * (k & 3));
         vw[k >> 2] |= rtn8_v(lds, xv) << (8 * (k & 3));
     }

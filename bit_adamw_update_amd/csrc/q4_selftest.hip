@@ -17,7 +17,7 @@
 
 namespace {
 
-constexpr int kWhatSqrt = 0, kWhatInvScale = 1, kWhatSqrtFaithful = 2, kWhatSqrtSmall = 3;
+constexpr int kWhatSqrt = 0, kWhatInvScale = 1, kWhatSqrtFaithful = 2, kWhatSqrtSmall = 3, kWhatClampUnit = 4;
 constexpr int kFormFast = 0, kFormHardware = 1;
 
 __device__ __forceinline__ double mid_below(uint32_t y) {
@@ -57,6 +57,15 @@ __device__ bool is_sqrt_small(uint32_t x, uint32_t y) {
     return yf >= 0.0f && yf <= 0x1p-63f;
 }
 
+// The clamp of a normalized second moment: y = x for x in (0, 1], 1 above,
+// a zero for x <= 0 and for every NaN (the kernels send NaN to 0).
+__device__ bool is_clamp_unit(uint32_t x, uint32_t y) {
+    const float xf = __uint_as_float(x), yf = __uint_as_float(y);
+    if (xf != xf || xf <= 0.0f) return yf == 0.0f;
+    if (xf >= 1.0f) return y == 0x3F800000u;
+    return y == x;
+}
+
 // y == RN(1/s) when s > 0 and RN(1/s) is finite, else +0, for every s >= +0,
 // +inf and NaN included (-> +0).  RN(1/s) overflows iff 1/s reaches the
 // midpoint 2^128 - 2^103 between the largest float and 2^128, i.e. iff
@@ -87,6 +96,13 @@ __global__ void __launch_bounds__(256) k_sweep(uint64_t lo, uint64_t hi, unsigne
             ok = is_sqrt_faithful(b, __float_as_uint(__builtin_amdgcn_sqrtf(x)));
         } else if constexpr (WHAT == kWhatSqrtSmall) {
             ok = is_sqrt_small(b, __float_as_uint(__builtin_amdgcn_sqrtf(x)));
+        } else if constexpr (WHAT == kWhatClampUnit) {
+            // in the kernels' forms: the clamp of a product and of the
+            // multiply-add (one = 1.0f at run time; the multiply cannot
+            // fold away)
+            const float one = __uint_as_float(0x3F800000u | (uint32_t)(lo >> 63));
+            ok = is_clamp_unit(b, __float_as_uint(q4::clamp_unit(x * one))) &&
+                 is_clamp_unit(b, __float_as_uint(q4::normalize_v(x, one)));
         } else {
             const float r = FORM == kFormFast ? q4::inv_scale(x) : (x >= 0x1p-126f ? __builtin_amdgcn_rcpf(x) : 0.0f);
             ok = is_inv_scale(b, __float_as_uint(r));
@@ -345,14 +361,16 @@ extern "C" {
 // Synchronous, on the current device's null stream.
 int q4st_sweep(int what, int form, uint64_t lo, uint64_t hi, unsigned long long* mismatches,
                uint32_t* first_bad) {
-    if (what < 0 || what > 3 || form < 0 || form > 1 || lo > hi || hi > (1ull << 32) || !mismatches ||
+    if (what < 0 || what > 4 || form < 0 || form > 1 || lo > hi || hi > (1ull << 32) || !mismatches ||
         !first_bad)
         return -1;
     DevCounters c;
     hipError_t e = c.init();
     if (e != hipSuccess) return (int)e;
     if (hi > lo) {
-        if (what == kWhatSqrtFaithful)
+        if (what == kWhatClampUnit)
+            k_sweep<kWhatClampUnit, kFormFast><<<kGrid, kThreads>>>(lo, hi, c.bad, c.first);
+        else if (what == kWhatSqrtFaithful)
             k_sweep<kWhatSqrtFaithful, kFormHardware><<<kGrid, kThreads>>>(lo, hi, c.bad, c.first);
         else if (what == kWhatSqrtSmall)
             k_sweep<kWhatSqrtSmall, kFormHardware><<<kGrid, kThreads>>>(lo, hi, c.bad, c.first);

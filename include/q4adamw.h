@@ -238,11 +238,18 @@ q4_status q4adamw_init_state(const q4_config* cfg, const q4_tensor* t, int32_t n
  * included); a block whose scale is 0, or so small that its reciprocal
  * overflows (s <= 2^-128), stores the code of zero in every slot and keeps
  * its scale as computed.
+ * Non-finite gradients (the pages are silent; IEEE operations decide): the
+ * block maxima skip NaN and keep +inf; an infinite scale normalizes by 0;
+ * a NaN normalized value (a NaN moment, or inf * 0) takes the lowest level
+ * of its map; EDEN's ratio over a block holding one is 1; weights follow
+ * IEEE arithmetic (NaN where the Adam term is NaN).  Such a block stays
+ * poisoned (infinite or zero scales) while its gradients do.
  * Clipping (hp->max_grad_norm > 0): s = min(1, max_grad_norm / (norm +
  * 1e-6)) in binary64, rounded to FP32, from the global norm of the
  * gradients (the statistics in ws with Q4_HP_GRAD_STATS, else gathered
  * first by one read of the gradients); every gradient element is multiplied
- * by s before use and the factored row/column sums of g^2 by s^2.
+ * by s before use and the factored row/column sums of g^2 by s^2.  A NaN
+ * norm gives s = 1 (the comparison with 1 fails), an infinite norm s = 0.
  * Stochastic rounding draws Philox4x32-10 with counter (i/4, step,
  * tensor_id, stream 0 for m / 1 for v), key (seed), word i mod 4.
  * `ws` (device, ws_bytes >= q4adamw_workspace_bytes) holds the tensor table

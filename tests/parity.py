@@ -16,7 +16,8 @@ rule's two sides in binary64 and accepts the difference only if
 (round-to-nearest and EDEN codes involve no square root and must match).
 The weight tolerance is relative to max(|w|, rms of the tensor's window):
 near a weight that crosses zero FP32 is accurate relative to the terms of
-the update, not to the tiny result.
+the update, not to the tiny result.  A non-finite value (NaN, an infinity)
+must be matched exactly, by NaN or by the same infinity.
 """
 from __future__ import annotations
 
@@ -102,6 +103,7 @@ class Report:
     padding_nonzero: int = 0
     ties_audited: int = 0
     untied_differ: int = 0
+    nonfinite_weights: int = 0   # oracle weights that are NaN or infinite (matched exactly)
     notes: list = field(default_factory=list)
 
     def check(self):
@@ -117,7 +119,24 @@ class Report:
 
 
 def _rms(x):
+    x = x[np.isfinite(x)]
     return float(np.sqrt(np.mean(x.astype(np.float64) ** 2))) if x.size else 0.0
+
+
+def _rel_err(mine: np.ndarray, ref: np.ndarray, floor: float | None = None) -> np.ndarray:
+    """|mine - ref| / max(|ref|, floor) per element (floor: the rms of ref's
+    finite values unless given).  A non-finite ref must be matched exactly
+    (NaN by NaN, an infinity by the same infinity) and a finite ref by a
+    finite value: otherwise the error is inf."""
+    x, r = mine.astype(np.float64), ref.astype(np.float64)
+    fin_r, fin_x = np.isfinite(r), np.isfinite(x)
+    same = (np.isnan(x) & np.isnan(r)) | (np.isinf(r) & (x == r))
+    sc = np.maximum(np.abs(r), _rms(ref) if floor is None else floor)
+    sc[~(sc > 0)] = 1.0
+    with np.errstate(invalid="ignore", over="ignore"):
+        err = np.where(fin_r & fin_x, np.abs(x - r) / sc, 0.0)
+    err[~same & ~(fin_r & fin_x)] = np.inf
+    return err
 
 
 def run(workload: inputs.Workload, recipe: str, steps: int, *, windows=None, device="cuda",
@@ -232,6 +251,9 @@ class Audit:
             return False
         b0 = (j // 128) * 128
         blk = vals[b0:b0 + 128].astype(np.float32)
+        blk = blk[~np.isnan(blk)]   # the block maximum skips NaN
+        if blk.size == 0 or not np.isfinite(vals[j]):
+            return False
         s = np.float32(np.abs(blk).max()) if moment == "m" else np.float32(blk.max())
         with np.errstate(over="ignore", divide="ignore"):
             inv = np.float32(1) / s if s > 0 else np.float32(0)
@@ -273,9 +295,7 @@ def _compare(st, gp, wins, fact, rep: Report, fp32: bool, audit: Audit):
         if fp32:
             for mine, ref in ((b.m32[w.lo:w.hi], w.m32), (b.v32[w.lo:w.hi], w.v32)):
                 x = mine.cpu().numpy()
-                sc = np.maximum(np.abs(ref), _rms(ref))
-                sc[sc == 0] = 1.0
-                rep.max_w_err = max(rep.max_w_err, float((np.abs(x - ref) / sc).max()) if n else 0.0)
+                rep.max_w_err = max(rep.max_w_err, float(_rel_err(x, ref).max()) if n else 0.0)
         else:
             cl, ch = w.lo // 2, (w.hi + 1) // 2
             if w.hi == b.numel and b.numel % 2 == 1:
@@ -307,22 +327,18 @@ def _compare(st, gp, wins, fact, rep: Report, fp32: bool, audit: Audit):
                 rep.scales_compared += gs.size
                 rep.scales_differ += int((gs.view(np.uint32) != w.v_scales.view(np.uint32)).sum())
         pw = gp[w.i][w.lo:w.hi].cpu().numpy()
+        rep.nonfinite_weights += int((~np.isfinite(w.param)).sum())
         ok = ~(w.m_bad | w.v_bad)
         rep.weights_compared += n
         rep.weights_excluded += int((~ok).sum())
         if ok.any():
-            ref = w.param
-            sc = np.maximum(np.abs(ref), _rms(ref))
-            sc[sc == 0] = 1.0
-            err = (np.abs(pw.astype(np.float64) - ref) / sc)[ok]
+            err = _rel_err(pw, w.param)[ok]
             rep.max_w_err = max(rep.max_w_err, float(err.max()))
     for i, (R, Cc) in fact.items():
         b = st.bufs[i]
         for mine, ref in ((b.v_row, R), (b.v_col, Cc)):
-            x = mine.cpu().numpy().astype(np.float64)
-            r = ref.astype(np.float64)
-            sc = np.maximum(np.abs(r), 1e-30)
-            rep.max_rc_err = max(rep.max_rc_err, float((np.abs(x - r) / sc).max()))
+            x = mine.cpu().numpy()
+            rep.max_rc_err = max(rep.max_rc_err, float(_rel_err(x, ref, floor=1e-30).max()))
 
 
 def sample_windows(workload: inputs.Workload, n_random: int = 48, seed: int = 0, blocks_per_window: int = 8):

@@ -18,11 +18,10 @@ def _flush(msg):
 
 
 def _check_weights(p, ref, what):
+    """Within 1e-6 of max(|w|, rms(w)); NaN and infinities matched exactly."""
     if p.size == 0:
         return
-    scale = np.maximum(np.abs(ref), np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
-    scale[scale == 0] = 1.0
-    err = float((np.abs(p - ref) / scale).max())
+    err = float(parity._rel_err(p, ref).max())
     assert err <= parity.W_TOL, f"{what}: weight error {err:.3e}"
 
 

@@ -6,6 +6,9 @@
   * inv_scale, the hardware reciprocal plus one Newton step, returns the
     correctly rounded 1/s for every s >= 2^-126 (through +inf) and +0 below
     that, for zero and for NaN;
+  * clamp_unit, the clamp of a normalized second moment as the kernels form
+    it (folded into the multiply), returns x on (0, 1], 1 above, and a zero
+    for x <= 0 and for every NaN;
   * the nibble-addressed ds_bpermute decode fetches lane row + code for
     every nibble, and ds_bpermute ignores address bits 0-1 and 8-31;
   * the kernels' Philox4x32-10 (the element-independent products formed
@@ -29,7 +32,7 @@ import pytest
 
 from bit_adamw_update_amd import build
 
-SQRT, INV_SCALE, SQRT_FAITHFUL, SQRT_SMALL = 0, 1, 2, 3
+SQRT, INV_SCALE, SQRT_FAITHFUL, SQRT_SMALL, CLAMP_UNIT = 0, 1, 2, 3, 4
 FAST, BARE = 0, 1
 F32_INF = 0x7F800000
 ONE, NEG_ZERO, NEG_ONE = 0x3F800000, 0x80000000, 0xBF800000
@@ -73,7 +76,7 @@ def test_selftest_library_exports_and_validates():
         assert f" T {sym}" in out
     n, first = ctypes.c_ulonglong(0), ctypes.c_uint32(0)
     # rejected before any device call
-    assert lib.q4st_sweep(4, 0, 0, 1, ctypes.byref(n), ctypes.byref(first)) == -1
+    assert lib.q4st_sweep(5, 0, 0, 1, ctypes.byref(n), ctypes.byref(first)) == -1
     assert lib.q4st_sweep(0, 2, 0, 1, ctypes.byref(n), ctypes.byref(first)) == -1
     assert lib.q4st_sweep(0, 0, 5, 4, ctypes.byref(n), ctypes.byref(first)) == -1
     assert lib.q4st_sweep(0, 0, 0, (1 << 32) + 1, ctypes.byref(n), ctypes.byref(first)) == -1
@@ -111,6 +114,14 @@ def test_hardware_sqrt_bounds():
     assert _sweep(lib, SQRT_FAITHFUL, BARE, 0x00800000, F32_INF + 1) == (0, 0xFFFFFFFF)
     assert _sweep(lib, SQRT_FAITHFUL, BARE, 1, 0x00800000)[0] > 0
     assert _sweep(lib, SQRT_SMALL, BARE, 1, 0x00800000) == (0, 0xFFFFFFFF)
+
+
+@pytest.mark.gpu
+def test_clamp_unit_exhaustive():
+    """The second moment's clamp over every bit pattern: NaN (and anything
+    <= 0) to a zero, so a NaN takes sorted index 0 in every unsigned map."""
+    lib = _lib()
+    assert _sweep(lib, CLAMP_UNIT, FAST, 0, 1 << 32) == (0, 0xFFFFFFFF)
 
 
 @pytest.mark.gpu
