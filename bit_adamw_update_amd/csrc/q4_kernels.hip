@@ -1168,13 +1168,28 @@ __global__ __launch_bounds__(256) void k_dequant(DevTensor T, float* __restrict_
 // Launchers
 // ---------------------------------------------------------------------------
 
-// Grid-stride grid sized from the kernel's occupancy and the number of
-// compute units, never more groups than there are chunk groups.
-constexpr int64_t kMinChunksPerWave = 20;
+// Grid of the chunk-walking steps: up to max_mult times the resident
+// work-groups (the queued groups even out the finishing times of the
+// resident ones), but no more than leave every wavefront some
+// min_chunks_per_wave chunks, since each group sets up its tables once; at
+// least the resident groups, never more groups than chunk groups.  The
+// best settings differ by kernel (gfx950, alternating processes on one box,
+// GPT-162M / GPT-2.7B sets):
+//   memory-bound steps (compact tables, 8-bit, FP32): 8x and 5 chunks;
+//     against 4x and 20: ZE-EDEN 0.320 -> 0.3125 ms and 6.371 -> 6.343 ms,
+//     8-bit 0.369 -> 0.360 ms, FP32 1.808 -> 1.762 ms;
+//   the ZIP-SR kernel, whose groups each copy a 24.5 KB table: 4x and 10
+//     chunks, 0.338 -> 0.332 ms (8x and 5 chunks: 0.341 ms);
+//   steps with factored matrices: 2x (Qwen3-0.6B set: 4x 1.83 ms, 2x
+//     1.76 ms, 8x 2.05 ms).
+struct GridPolicy {
+    int64_t max_mult, min_chunks_per_wave;
+};
+constexpr GridPolicy kGridMemory{8, 5}, kGridFlat{4, 10}, kGridMatrices{2, 10};
 
 template <class K>
-static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds = 0,
-                     int64_t max_mult = 4) {
+static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds,
+                     const GridPolicy& pol) {
     static std::atomic<int> cus{0};
     if (cus.load() == 0) {
         int dev = 0;
@@ -1189,14 +1204,9 @@ static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_ca
         per_cu_cache.store(per_cu);
     }
     const int64_t groups = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
-    // max_mult (4) times the resident groups: the queued groups balance the
-    // uneven finishing times of the first wave of groups (measured best on
-    // gfx950 for the large sets); but every wavefront should get some 20
-    // chunks, or each group's table setup dominates (GPT-162M set: 0.45 ms at
-    // 4x, 0.40 ms at 2x the resident groups)
     const int64_t resident = (int64_t)per_cu * cus.load();
-    int64_t cap = total_chunks / (kWavesPerGroup * kMinChunksPerWave);
-    cap = cap < resident ? resident : (cap > max_mult * resident ? max_mult * resident : cap);
+    int64_t cap = total_chunks / (kWavesPerGroup * pol.min_chunks_per_wave);
+    cap = cap < resident ? resident : (cap > pol.max_mult * resident ? pol.max_mult * resident : cap);
     return (int)(groups < cap ? (groups > 0 ? groups : 1) : cap);
 }
 
@@ -1207,9 +1217,9 @@ struct RunLaunch {
     int grid, run_slabs;
 };
 template <class K>
-static RunLaunch run_launch(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds = 0,
-                            int64_t max_mult = 4) {
-    const int cap = step_grid(kernel, total_chunks, per_cu_cache, dyn_lds, max_mult);
+static RunLaunch run_launch(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds,
+                            const GridPolicy& pol) {
+    const int cap = step_grid(kernel, total_chunks, per_cu_cache, dyn_lds, pol);
     const int64_t slabs = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
     int r = kRunSlabs;
     while (r > 1 && slabs / r < cap) r >>= 1;
@@ -1236,8 +1246,7 @@ bool variant_supported(const Variant& v) {
 
 // Reserved (unused) LDS that caps a 4-wave work-group of the step at 7 per
 // CU (160 KiB of LDS): with factored matrices the kernel that fits 8 ran the
-// Qwen3-0.6B set 3% slower than at 7 (same box).  Those launches also take
-// at most 2x the resident groups (4x: 1.83 ms, 2x: 1.76 ms, 8x: 2.05 ms).
+// Qwen3-0.6B set 3% slower than at 7 (same box).
 constexpr size_t kCap7Lds = 19456;
 
 hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevTensor* d_tab,
@@ -1247,16 +1256,17 @@ hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevT
     const int cap = has_matrices ? 1 : 0;
 #define Q4_LAUNCH(A, B, C)                                                                                   \
     if (v.mcb == A && v.vcb == B && v.vrule == C) {                                                          \
+        const GridPolicy& pol = cap ? kGridMatrices : (flat_tables<B, C>() ? kGridFlat : kGridMemory);       \
         if (sc.flags & SF_CLIP) {                                                                            \
             static std::atomic<int> occ[2];                                                                  \
             const size_t dl = (cap && !flat_tables<B, C>()) ? kCap7Lds : 0;                                  \
-            const RunLaunch L = run_launch(k_fused_step<A, B, C, true>, total_chunks, occ[cap], dl, cap ? 2 : 4); \
+            const RunLaunch L = run_launch(k_fused_step<A, B, C, true>, total_chunks, occ[cap], dl, pol); \
             k_fused_step<A, B, C, true><<<L.grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors,        \
                                                                      total_chunks, L.run_slabs, sc);         \
         } else {                                                                                             \
             static std::atomic<int> occ[2];                                                                  \
             const size_t dl = (cap && !flat_tables<B, C>()) ? kCap7Lds : 0;                                  \
-            const RunLaunch L = run_launch(k_fused_step<A, B, C, false>, total_chunks, occ[cap], dl, cap ? 2 : 4); \
+            const RunLaunch L = run_launch(k_fused_step<A, B, C, false>, total_chunks, occ[cap], dl, pol); \
             k_fused_step<A, B, C, false><<<L.grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors,       \
                                                                       total_chunks, L.run_slabs, sc);        \
         }                                                                                                    \
@@ -1271,8 +1281,8 @@ hipError_t launch_fp32_step(const StepScalars& sc, const DevTensor* d_tab, const
                             int n_tensors, int64_t total_chunks, hipStream_t stream) {
     if (total_chunks <= 0) return hipSuccess;
     static std::atomic<int> occ{0};
-    k_fp32_step<<<step_grid(k_fp32_step, total_chunks, occ), 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors,
-                                                                               total_chunks, sc);
+    const int grid = step_grid(k_fp32_step, total_chunks, occ, 0, kGridMemory);
+    k_fp32_step<<<grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, sc);
     return hipGetLastError();
 }
 
@@ -1381,11 +1391,11 @@ hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, con
     if (total_chunks <= 0) return hipSuccess;
     if (sc.flags & SF_CLIP) {
         static std::atomic<int> occ{0};
-        const RunLaunch L = run_launch(k_step8<true>, total_chunks, occ);
+        const RunLaunch L = run_launch(k_step8<true>, total_chunks, occ, 0, kGridMemory);
         k_step8<true><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     } else {
         static std::atomic<int> occ{0};
-        const RunLaunch L = run_launch(k_step8<false>, total_chunks, occ);
+        const RunLaunch L = run_launch(k_step8<false>, total_chunks, occ, 0, kGridMemory);
         k_step8<false><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     }
     return hipGetLastError();
