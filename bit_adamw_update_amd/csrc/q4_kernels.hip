@@ -516,7 +516,17 @@ template <int VRULE> constexpr int step_waves() {
     return (VRULE == Q4_RULE_UPDATE_SR || VRULE == Q4_RULE_UPDATE_RTN) ? 6 : 7;
 }
 
-template <int MCB, int VCB, int VRULE, bool CLIP>
+// Factored matrices come only with the factored recipe, whose maps are
+// fixed (NF4 m, Dyn4-NZ v by State-RTN).  MATS: the tensor list holds
+// factored matrices; only that recipe's maps are instantiated with it, and
+// every other instantiation carries no factored branch (its scalar
+// registers then fit without spilling to vector lanes: ZIP-SR 13 -> 5
+// spilled, ZE-EDEN 26 -> 0).
+template <int MCB, int VCB, int VRULE> constexpr bool factored_maps() {
+    return MCB == Q4_CB_NF4 && VCB == Q4_CB_DYN4_NZ && VRULE == Q4_RULE_STATE_RTN;
+}
+
+template <int MCB, int VCB, int VRULE, bool CLIP, bool MATS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves<VRULE>())))
 void k_fused_step(const DevTensor* __restrict__ tab,
                                                      const int64_t* __restrict__ chunk_begin, int n_tensors,
@@ -564,7 +574,7 @@ void k_fused_step(const DevTensor* __restrict__ tab,
         const int64_t lc = c - chunk_begin[t];
         if (lc * kChunkElems < T.numel) {  // beyond: a chunk that only aligns the next tensor
             const bool full = (lc + 1) * kChunkElems <= T.numel;
-            if (T.kind == KIND_PACKED) {
+            if (!MATS || T.kind == KIND_PACKED) {
                 if (full) step_chunk<MCB, VCB, VRULE, true, true, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
                 else step_chunk<MCB, VCB, VRULE, false, true, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
             } else {
@@ -1249,29 +1259,42 @@ bool variant_supported(const Variant& v) {
 // Qwen3-0.6B set 3% slower than at 7 (same box).
 constexpr size_t kCap7Lds = 19456;
 
+template <int A, int B, int C, bool CLIP, bool MATS>
+static hipError_t launch_step_kernel(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
+                                     int n_tensors, int64_t total_chunks, hipStream_t stream) {
+    static std::atomic<int> occ{0};
+    const GridPolicy& pol = MATS ? kGridMatrices : (flat_tables<B, C>() ? kGridFlat : kGridMemory);
+    const size_t dl = (MATS && !flat_tables<B, C>()) ? kCap7Lds : 0;
+    const RunLaunch L = run_launch(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ, dl, pol);
+    k_fused_step<A, B, C, CLIP, MATS><<<L.grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks,
+                                                                   L.run_slabs, sc);
+    return hipGetLastError();
+}
+
+template <int A, int B, int C>
+static hipError_t launch_variant(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
+                                 int n_tensors, int64_t total_chunks, bool has_matrices, hipStream_t stream) {
+    const bool clip = (sc.flags & SF_CLIP) != 0;
+    if constexpr (factored_maps<A, B, C>()) {
+        if (has_matrices)
+            return clip ? launch_step_kernel<A, B, C, true, true>(sc, d_tab, d_chunk_begin, n_tensors, total_chunks,
+                                                                  stream)
+                        : launch_step_kernel<A, B, C, false, true>(sc, d_tab, d_chunk_begin, n_tensors, total_chunks,
+                                                                   stream);
+    } else {
+        if (has_matrices) return hipErrorInvalidValue;  // only the factored recipe's maps take matrices
+    }
+    return clip ? launch_step_kernel<A, B, C, true, false>(sc, d_tab, d_chunk_begin, n_tensors, total_chunks, stream)
+                : launch_step_kernel<A, B, C, false, false>(sc, d_tab, d_chunk_begin, n_tensors, total_chunks, stream);
+}
+
 hipError_t launch_fused_step(const Variant& v, const StepScalars& sc, const DevTensor* d_tab,
                              const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks, bool has_matrices,
                              hipStream_t stream) {
     if (total_chunks <= 0) return hipSuccess;
-    const int cap = has_matrices ? 1 : 0;
-#define Q4_LAUNCH(A, B, C)                                                                                   \
-    if (v.mcb == A && v.vcb == B && v.vrule == C) {                                                          \
-        const GridPolicy& pol = cap ? kGridMatrices : (flat_tables<B, C>() ? kGridFlat : kGridMemory);       \
-        if (sc.flags & SF_CLIP) {                                                                            \
-            static std::atomic<int> occ[2];                                                                  \
-            const size_t dl = (cap && !flat_tables<B, C>()) ? kCap7Lds : 0;                                  \
-            const RunLaunch L = run_launch(k_fused_step<A, B, C, true>, total_chunks, occ[cap], dl, pol); \
-            k_fused_step<A, B, C, true><<<L.grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors,        \
-                                                                     total_chunks, L.run_slabs, sc);         \
-        } else {                                                                                             \
-            static std::atomic<int> occ[2];                                                                  \
-            const size_t dl = (cap && !flat_tables<B, C>()) ? kCap7Lds : 0;                                  \
-            const RunLaunch L = run_launch(k_fused_step<A, B, C, false>, total_chunks, occ[cap], dl, pol); \
-            k_fused_step<A, B, C, false><<<L.grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors,       \
-                                                                      total_chunks, L.run_slabs, sc);        \
-        }                                                                                                    \
-        return hipGetLastError();                                                                            \
-    }
+#define Q4_LAUNCH(A, B, C)                                                                            \
+    if (v.mcb == A && v.vcb == B && v.vrule == C)                                                     \
+        return launch_variant<A, B, C>(sc, d_tab, d_chunk_begin, n_tensors, total_chunks, has_matrices, stream);
     Q4_VARIANTS(Q4_LAUNCH)
 #undef Q4_LAUNCH
     return hipErrorInvalidValue;
