@@ -392,8 +392,10 @@ def main():
 
     if not args.no_variants:
         variants = {}
+        # the other recipes and sets; FP32 AdamW (quantization off) on the
+        # same set as the reference point the 4-bit state is measured against
         plan = [("gpt-2.7b", "ze_eden"), ("llama-1.1b", "zip_sr"), ("qwen3-0.6b-factored", "factored"),
-                ("gpt-162m", "zip_sr"), ("gpt-2.7b", "block8")]
+                ("gpt-162m", "zip_sr"), ("gpt-2.7b", "block8"), ("gpt-2.7b", "fp32")]
         for wname, rec in plan:
             if (wname, rec) == (args.workload, args.recipe):
                 continue
