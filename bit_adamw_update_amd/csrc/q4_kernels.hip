@@ -1229,7 +1229,8 @@ __global__ __launch_bounds__(256) void k_dequant(DevTensor T, float* __restrict_
 // GPT-162M / GPT-2.7B sets):
 //   memory-bound steps (compact tables, 8-bit, FP32): 8x and 5 chunks;
 //     against 4x and 20: ZE-EDEN 0.320 -> 0.3125 ms and 6.371 -> 6.343 ms,
-//     8-bit 0.369 -> 0.360 ms, FP32 1.808 -> 1.762 ms;
+//     8-bit 0.369 -> 0.360 ms, FP32 (in a form with per-element loads)
+//     1.808 -> 1.762 ms;
 //   the ZIP-SR kernel, whose groups each copy a 24.5 KB table: 4x and 10
 //     chunks, 0.338 -> 0.332 ms (8x and 5 chunks: 0.341 ms);
 //   steps with factored matrices: 2x (Qwen3-0.6B set: 4x 1.83 ms, 2x
