@@ -224,7 +224,8 @@ def probe_ceilings(n_elems: int) -> dict:
     """The practical ceilings of this machine, from the hand-written probes of
     libq4probe.so: the step's byte mix (12.125 B per element, the step's lane
     layout and work-group walk, trivial arithmetic) over as many elements as
-    the workload has (rounded up to 512), a plain copy and a read."""
+    the workload has (rounded up to 512), a plain copy, an in-place update
+    of one buffer and a read."""
     import torch
 
     from bit_adamw_update_amd import probe
@@ -239,6 +240,9 @@ def probe_ceilings(n_elems: int) -> dict:
     b = torch.empty_like(a)
     ms = _time_launches(lambda: probe.copy(b, a), PROBE_LAUNCHES)
     out["copy_ceiling_gbs"] = 2 * COPY_PROBE_BYTES / (ms * 1e-3) / 1e9
+    # the same bytes read and written back in place, as the step's state is
+    ms = _time_launches(lambda: probe.update_in_place(a), PROBE_LAUNCHES)
+    out["in_place_ceiling_gbs"] = 2 * COPY_PROBE_BYTES / (ms * 1e-3) / 1e9
     del a, b
     torch.cuda.empty_cache()
     r = torch.ones(READ_PROBE_BYTES // 4, dtype=torch.int32, device="cuda")

@@ -25,6 +25,8 @@ def load_library():
         L.q4probe_byte_mix.restype = C.c_int
         L.q4probe_copy.argtypes = [vp, vp, C.c_size_t, vp]
         L.q4probe_copy.restype = C.c_int
+        L.q4probe_update_in_place.argtypes = [vp, C.c_size_t, vp]
+        L.q4probe_update_in_place.restype = C.c_int
         L.q4probe_read_sink_words.argtypes = []
         L.q4probe_read_sink_words.restype = i64
         L.q4probe_read.argtypes = [vp, C.c_size_t, vp, vp]
@@ -73,6 +75,12 @@ def copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:
     nbytes = src.numel() * src.element_size()
     assert dst.numel() * dst.element_size() >= nbytes
     _ok(load_library().q4probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, _stream(stream)), "q4probe_copy")
+
+
+def update_in_place(x: torch.Tensor, stream=None) -> None:
+    assert x.dtype == torch.float32
+    _ok(load_library().q4probe_update_in_place(x.data_ptr(), x.numel() * 4, _stream(stream)),
+        "q4probe_update_in_place")
 
 
 def read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:

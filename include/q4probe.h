@@ -46,6 +46,11 @@ int q4probe_byte_mix(float* param, const uint16_t* grad, uint8_t* m_codes, uint8
 /* dst <- src, `bytes` (a positive multiple of 16) read and written once. */
 int q4probe_copy(void* dst, const void* src, size_t bytes, void* stream);
 
+/* x <- x * 0.999f (FP32) in place: `bytes` (a positive multiple of 16) read
+ * and written back to the same addresses, the way the step rewrites its
+ * state. */
+int q4probe_update_in_place(float* x, size_t bytes, void* stream);
+
 /* Words a q4probe_read sink must hold. */
 int64_t q4probe_read_sink_words(void);
 

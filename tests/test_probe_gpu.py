@@ -1,7 +1,8 @@
 """The bandwidth probes (libq4probe.so) do the memory work they claim: the
 byte-mix probe reads and rewrites every byte of its mix (masters, codes and
 scales changed as its arithmetic says, nothing outside touched), the copy
-copies and the read probe reads everything."""
+copies, the in-place update rewrites every element and the read probe reads
+everything."""
 import numpy as np
 import pytest
 import torch
@@ -50,3 +51,14 @@ def test_copy_and_read():
     # the XOR over all threads' partial XORs is the XOR of every word read
     ref = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
     assert np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32)) == ref
+
+
+def test_update_in_place():
+    """Every element scaled by 0.999f once, in the segment part and the tail."""
+    n = (1 << 20) + 12
+    x = torch.randn(n, device="cuda")
+    ref = x * torch.tensor(0.999, dtype=torch.float32, device="cuda")
+    print("in-place probe", flush=True)
+    probe.update_in_place(x)
+    torch.cuda.synchronize()
+    assert torch.equal(x.view(torch.int32), ref.view(torch.int32))
