@@ -17,7 +17,7 @@ RULE_STATE_RTN, RULE_STATE_SR, RULE_UPDATE_RTN, RULE_UPDATE_SR = range(4)
 HP_REUSE_TABLE, HP_CHECK_POINTERS, HP_GRAD_STATS = 1, 2, 4
 ACC_FIRST, ACC_LAST, ACC_REUSE_TABLE = 1, 2, 4
 TF_LM_HEAD = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_NDIM = 8
 
 STATUS = {0: "Q4_OK", 1: "Q4_ERR_INVALID_ARG", 2: "Q4_ERR_SHAPE", 3: "Q4_ERR_ALIGNMENT", 4: "Q4_ERR_CONFLICT",
@@ -42,7 +42,7 @@ class Q4Tensor(C.Structure):
                 ("shape", C.c_int64 * MAX_NDIM), ("numel", C.c_int64),
                 ("param", C.c_void_p), ("grad", C.c_void_p), ("m_codes", C.c_void_p), ("m_scales", C.c_void_p),
                 ("v_codes", C.c_void_p), ("v_scales", C.c_void_p), ("v_row", C.c_void_p), ("v_col", C.c_void_p),
-                ("m_fp32", C.c_void_p), ("v_fp32", C.c_void_p)]
+                ("m_fp32", C.c_void_p), ("v_fp32", C.c_void_p), ("elem_offset", C.c_int64)]
 
 
 class Q4StateBytes(C.Structure):

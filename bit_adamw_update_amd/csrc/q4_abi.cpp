@@ -137,10 +137,15 @@ q4_status check_tensors(const Resolved& r, const q4_tensor* t, int32_t n, bool n
             return fail(Q4_ERR_SHAPE, "tensor %d: numel %lld != product of shape %lld", i, (long long)x.numel,
                         (long long)prod);
         if (x.numel >= kMaxNumel) return fail(Q4_ERR_SHAPE, "tensor %d: numel must be < 2^34", i);
+        if (x.elem_offset < 0 || x.elem_offset % kChunkElems != 0 || x.elem_offset >= kMaxNumel - x.numel)
+            return fail(Q4_ERR_SHAPE, "tensor %d: elem_offset %lld must be a multiple of 512 in [0, 2^34 - numel)", i,
+                        (long long)x.elem_offset);
         if (x.numel == 0) continue;
         const int kind = kind_of(r, x);
         if (kind == KIND_FACTORED && (x.numel / x.shape[0]) >= (int64_t(1) << 31))
             return fail(Q4_ERR_SHAPE, "tensor %d: factored matrix needs numel/shape[0] < 2^31", i);
+        if (kind == KIND_FACTORED && x.elem_offset != 0)
+            return fail(Q4_ERR_SHAPE, "tensor %d: a factored matrix cannot be a shard (elem_offset must be 0)", i);
         struct P { const void* p; const char* name; };
         std::vector<P> need;
         if (need_param_grad) {
@@ -275,6 +280,7 @@ void plan_layout(const Resolved& r, const q4_tensor* t, int32_t n, Plan& P, uint
         d.cols = (d.kind == KIND_FACTORED && x.numel > 0) ? x.numel / x.shape[0] : 0;
         d.tensor_id = x.tensor_id;
         d.flags = x.flags;
+        d.ctr_base = (uint32_t)((uint64_t)x.elem_offset >> 2);
         d.chunk_begin = P.total_chunks;
         P.chunks[i] = P.total_chunks;
         const int64_t nch = (x.numel + kChunkElems - 1) / kChunkElems;

@@ -51,7 +51,7 @@ struct alignas(16) DevTensor {
     uint32_t tensor_id;
     uint32_t flags;
     int32_t kind;
-    int32_t pad;
+    uint32_t ctr_base;     // Philox counter of element 0: (elem_offset / 4) mod 2^32
 };
 static_assert(sizeof(DevTensor) == 128, "DevTensor layout");
 

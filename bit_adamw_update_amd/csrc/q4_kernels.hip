@@ -173,8 +173,11 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     const gptr<float> mscales = G(T.m_scales) + lc * kBlocksPerChunk;
     const gptr<float> vscales = G(T.v_scales) + lc * kBlocksPerChunk;
     const int lb4 = lane >> 4;  // the lane's block within the chunk
-    // the element-independent part of the stochastic-rounding draws
+    // the element-independent part of the stochastic-rounding draws, and
+    // the counter of the lane's first element: its index in the whole tensor
+    // (a shard's elements start at elem_offset) over 4, modulo 2^32
     const PhiloxFixed pf = philox_fixed(sc.step, T.tensor_id, sc.key0, sc.key1);
+    const uint32_t ctr0 = (uint32_t)(e0 >> 2) + T.ctr_base;
 
     // ---- loads
     // While a wave issues its loads it runs at raised priority, so the
@@ -334,7 +337,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
         float um[4];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            if ((k & 3) == 0) uniforms4((uint32_t)(e0 >> 2) + (k >> 2), 0u, pf, sc.key0, sc.key1, um);
+            if ((k & 3) == 0) uniforms4(ctr0 + (k >> 2), 0u, pf, sc.key0, sc.key1, um);
             const float x = fminf(fmaxf(m1[k] * inv_m, -1.0f), 1.0f);
             const int idx = rtn_index(m_entry(x), x);
             const float Lidx = lds.lev_m[idx];
@@ -381,7 +384,7 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     float uv[4];
     auto draw_v = [&](int k) {
         if (V_SR && (k & 3) == 0)
-            uniforms4((uint32_t)(e0 >> 2) + (k >> 2), 1u, pf, sc.key0, sc.key1, uv);
+            uniforms4(ctr0 + (k >> 2), 1u, pf, sc.key0, sc.key1, uv);
     };
     uint32_t vword = 0;
     float xx[8], xq[8];

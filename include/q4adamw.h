@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define Q4ADAMW_ABI_VERSION 2u
+#define Q4ADAMW_ABI_VERSION 3u
 #define Q4ADAMW_LAYOUT_VERSION 1u
 #define Q4ADAMW_BLOCK 128
 #define Q4ADAMW_MAX_NDIM 8
@@ -150,7 +150,21 @@ typedef struct {
  * Codes: element 2j in the low nibble of byte j, element 2j+1 in the high
  * nibble (0 when n is odd).  Q4_RECIPE_BLOCK8: m_codes and v_codes are
  * uint8[n], byte i holding element i.  Blocks are parameter-local: block b
- * covers elements [128 b, min(128 b + 128, n)). */
+ * covers elements [128 b, min(128 b + 128, n)).
+ * A shard (a data-parallel rank's share of a tensor, ZeRO style): blocks
+ * [b0, b1) of a tensor passed as a tensor of their own, with every pointer
+ * advanced to block b0 (param + 128 b0, m_codes + 64 b0, m_scales + b0, ...;
+ * the byte codes of Q4_RECIPE_BLOCK8 + 128 b0), numel the shard's length,
+ * elem_offset = 128 b0, and the whole tensor's tensor_id and flags.  b0 is
+ * a multiple of 4 (elem_offset of 512), so the advanced pointers keep the
+ * 16-byte alignment every pointer needs (a multiple of 32 keeps each
+ * shard's scales on whole 128-byte lines, the layout the step runs best
+ * on).  The
+ * stochastic-rounding draws then use the element's index in the whole
+ * tensor, so the shards of a tensor, stepped in one call or in several, give
+ * bit for bit what the whole tensor gives.  A shard ends on a block
+ * boundary unless it ends the tensor.  Factored matrices (the row and column
+ * statistics span the whole matrix) take elem_offset = 0. */
 typedef struct {
     uint32_t tensor_id; /* Philox counter word; stable across steps, distinct per tensor */
     uint32_t flags;     /* Q4_TF_* */
@@ -168,6 +182,7 @@ typedef struct {
     float* v_col;
     float* m_fp32;
     float* v_fp32;
+    int64_t elem_offset; /* index of element 0 in the whole tensor: 0, or 128 b0 (a multiple of 512) */
 } q4_tensor;
 
 typedef struct {

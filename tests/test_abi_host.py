@@ -60,7 +60,7 @@ def test_every_header_is_served_by_a_library():
 
 
 def test_abi_version_and_status_strings():
-    assert q4.q4adamw_abi_version() == 2 == q4.api.ABI_VERSION
+    assert q4.q4adamw_abi_version() == 3 == q4.api.ABI_VERSION
     assert q4.q4adamw_status_string(0) == "ok"
     assert "workspace" in q4.q4adamw_status_string(7)
 
@@ -137,7 +137,7 @@ def test_default_configs_follow_table2():
         q4.CB_NF4, q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, q4.RULE_STATE_RTN, 1)
     f = q4.q4adamw_default_config(q4.RECIPE_FACTORED)
     assert (f.v_codebook, f.v_rule, f.eden) == (q4.CB_DYN4_NZ, q4.RULE_STATE_RTN, 0)
-    assert f.block == 128 and f.abi_version == 2
+    assert f.block == 128 and f.abi_version == 3
 
 
 @pytest.mark.parametrize("step", [1, 2, 10, 1000, 123456789])
@@ -224,6 +224,24 @@ def test_validation_errors():
     cf = q4.q4adamw_default_config(q4.RECIPE_FACTORED)
     q4.q4adamw_validate(cf, hp(), [fake_tensor((64, 32), factored=True), fake_tensor((64,))])
     assert status_of(V, cf, hp(), [fake_tensor((64, 32))]) == 1
+
+
+def test_shard_offsets_are_validated():
+    """A shard starts on a 512-element boundary (its pointers stay 16-byte
+    aligned) inside the 2^34-element range of the Philox counter; a
+    factored matrix cannot be a shard."""
+    cfg = q4.q4adamw_default_config(q4.RECIPE_ZIP_SR)
+    V = q4.q4adamw_validate
+    ok = fake_tensor((1000,)); ok.elem_offset = 512 * 37
+    V(cfg, hp(), [ok])
+    for off in (-512, 128, 64, 1, (1 << 34) - 512):
+        bad = fake_tensor((1000,)); bad.elem_offset = off
+        assert status_of(V, cfg, hp(), [bad]) == 2, off
+    cf = q4.q4adamw_default_config(q4.RECIPE_FACTORED)
+    mat = fake_tensor((64, 32), factored=True); mat.elem_offset = 512
+    assert status_of(V, cf, hp(), [mat]) == 2
+    vec = fake_tensor((2048,)); vec.elem_offset = 512
+    V(cf, hp(), [vec])
 
 
 def test_step_refuses_before_any_device_work_on_bad_input():
