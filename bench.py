@@ -223,17 +223,20 @@ def _time_launches(fn, launches: int) -> float:
 def probe_ceilings(n_elems: int) -> dict:
     """The practical ceilings of this machine, from the hand-written probes of
     libq4probe.so: the step's byte mix (12.125 B per element, the step's lane
-    layout and work-group walk, trivial arithmetic) over as many elements as
-    the workload has (rounded up to 512), a plain copy, an in-place update
-    of one buffer and a read."""
+    layout, trivial arithmetic) over as many elements as the workload has
+    (rounded up to 512) in its fastest known form (chunks taken from a queue
+    of runs) and, on the same buffers, with the step's own work-group walk;
+    then a plain copy, an in-place update of one buffer and a read."""
     import torch
 
     from bit_adamw_update_amd import probe
     n = (n_elems + 511) // 512 * 512
     bm = probe.ByteMix(n)
-    ms = _time_launches(bm.run, PROBE_LAUNCHES)
-    out = {"byte_mix_ceiling_gbs": probe.byte_mix_bytes(n) / (ms * 1e-3) / 1e9, "byte_mix_elems": n,
-           "byte_mix_ms": ms}
+    nbytes = probe.byte_mix_bytes(n)
+    ms = _time_launches(bm.run_queue, PROBE_LAUNCHES)
+    ms_walk = _time_launches(bm.run, PROBE_LAUNCHES)
+    out = {"byte_mix_ceiling_gbs": nbytes / (ms * 1e-3) / 1e9, "byte_mix_elems": n, "byte_mix_ms": ms,
+           "byte_mix_step_walk_gbs": nbytes / (ms_walk * 1e-3) / 1e9}
     del bm
     torch.cuda.empty_cache()
     a = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")

@@ -21,6 +21,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 
 #include "../../include/q4probe.h"
@@ -39,6 +40,36 @@ __device__ __forceinline__ int64_t next_chunk(int64_t c, int& j, int run, int64_
     return c + (groups * run - (run - 1)) * kWaves;
 }
 
+// One chunk of the byte mix: 512 elements, lane l on elements 8l .. 8l+7.
+__device__ __forceinline__ void mix_chunk(float* __restrict__ param, const uint16_t* __restrict__ grad,
+                                          uint8_t* __restrict__ mcodes, uint8_t* __restrict__ vcodes,
+                                          float* __restrict__ mscales, float* __restrict__ vscales, int64_t c,
+                                          int lane, float a) {
+    const int64_t c0 = c * kChunk;
+    const gptr<float> p = (gptr<float>)param + c0 + lane * 8;
+    const gptr<const uint16_t> g = (gptr<const uint16_t>)grad + c0 + lane * 8;
+    const gptr<uint32_t> mc = (gptr<uint32_t>)(mcodes + (c0 >> 1)) + lane;
+    const gptr<uint32_t> vc = (gptr<uint32_t>)(vcodes + (c0 >> 1)) + lane;
+    const int64_t blk = c * 4 + (lane >> 4);
+    f32x4 x = *reinterpret_cast<const gptr<const f32x4>>(p);
+    f32x4 y = *reinterpret_cast<const gptr<const f32x4>>(p + 4);
+    const u32x4 q = *reinterpret_cast<const gptr<const u32x4>>(g);
+    const uint32_t m = *mc, v = *vc;
+    const float sm = ((gptr<float>)mscales)[blk], sv = ((gptr<float>)vscales)[blk];
+    // trivial, data-dependent arithmetic: nothing can be elided
+    const float gq = __uint_as_float(q.x << 16) + __uint_as_float(q.w & 0xFFFF0000u);
+    x = x * a + gq;
+    y = y * a + gq;
+    *reinterpret_cast<gptr<f32x4>>(p) = x;
+    *reinterpret_cast<gptr<f32x4>>(p + 4) = y;
+    *mc = m ^ q.y;
+    *vc = v ^ q.z;
+    if ((lane & 15) == 0) {
+        ((gptr<float>)mscales)[blk] = sm * a;
+        ((gptr<float>)vscales)[blk] = sv * a;
+    }
+}
+
 __global__ __launch_bounds__(256) void k_byte_mix(float* __restrict__ param, const uint16_t* __restrict__ grad,
                                                    uint8_t* __restrict__ mcodes, uint8_t* __restrict__ vcodes,
                                                    float* __restrict__ mscales, float* __restrict__ vscales,
@@ -47,30 +78,33 @@ __global__ __launch_bounds__(256) void k_byte_mix(float* __restrict__ param, con
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t groups = gridDim.x;
     int64_t c = (int64_t)blockIdx.x * run * kWaves + wave;
-    for (int j = 0; c < chunks; c = next_chunk(c, j, run, groups)) {
-        const int64_t c0 = c * kChunk;
-        const gptr<float> p = (gptr<float>)param + c0 + lane * 8;
-        const gptr<const uint16_t> g = (gptr<const uint16_t>)grad + c0 + lane * 8;
-        const gptr<uint32_t> mc = (gptr<uint32_t>)(mcodes + (c0 >> 1)) + lane;
-        const gptr<uint32_t> vc = (gptr<uint32_t>)(vcodes + (c0 >> 1)) + lane;
-        const int64_t blk = c * 4 + (lane >> 4);
-        f32x4 x = *reinterpret_cast<const gptr<const f32x4>>(p);
-        f32x4 y = *reinterpret_cast<const gptr<const f32x4>>(p + 4);
-        const u32x4 q = *reinterpret_cast<const gptr<const u32x4>>(g);
-        const uint32_t m = *mc, v = *vc;
-        const float sm = ((gptr<float>)mscales)[blk], sv = ((gptr<float>)vscales)[blk];
-        // trivial, data-dependent arithmetic: nothing can be elided
-        const float gq = __uint_as_float(q.x << 16) + __uint_as_float(q.w & 0xFFFF0000u);
-        x = x * a + gq;
-        y = y * a + gq;
-        *reinterpret_cast<gptr<f32x4>>(p) = x;
-        *reinterpret_cast<gptr<f32x4>>(p + 4) = y;
-        *mc = m ^ q.y;
-        *vc = v ^ q.z;
-        if ((lane & 15) == 0) {
-            ((gptr<float>)mscales)[blk] = sm * a;
-            ((gptr<float>)vscales)[blk] = sv * a;
-        }
+    for (int j = 0; c < chunks; c = next_chunk(c, j, run, groups))
+        mix_chunk(param, grad, mcodes, vcodes, mscales, vscales, c, lane, a);
+}
+
+// The same chunks taken from a queue: one round of resident work-groups,
+// each taking the next run of `run` slabs from a counter (zero at launch)
+// until none is left, so the groups work on a window of neighbouring runs
+// and a group that finishes early takes more.  The fastest way found to
+// move this byte mix on gfx950 (5.25 TB/s against 5.07 for the step's own
+// walk; runs of 2 slabs 4.08, of 32 slabs 5.04).
+__global__ __launch_bounds__(256) void k_byte_mix_queue(float* __restrict__ param, const uint16_t* __restrict__ grad,
+                                                         uint8_t* __restrict__ mcodes, uint8_t* __restrict__ vcodes,
+                                                         float* __restrict__ mscales, float* __restrict__ vscales,
+                                                         int64_t chunks, int run, unsigned int* __restrict__ queue,
+                                                         float a) {
+    __shared__ unsigned int next;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t runs = ((chunks + kWaves - 1) / kWaves + run - 1) / run;
+    for (;;) {
+        __syncthreads();  // every wave has read the previous run
+        if (threadIdx.x == 0) next = atomicAdd(queue, 1u);
+        __syncthreads();
+        const int64_t r = __builtin_amdgcn_readfirstlane(next);
+        if (r >= runs) break;
+        for (int64_t c = r * run * kWaves + wave, s = 0; s < run && c < chunks; ++s, c += kWaves)
+            mix_chunk(param, grad, mcodes, vcodes, mscales, vscales, c, lane, a);
     }
 }
 
@@ -180,6 +214,52 @@ static unsigned segment_grid(int64_t n16, const void* kernel, std::atomic<int>& 
     const int64_t need = (n16 / kSegVec + 3) / 4 + 1;
     const int64_t cap = 2 * (int64_t)resident.load();
     return (unsigned)(need < cap ? need : cap);
+}
+
+// The queue counter of k_byte_mix_queue: a device word of this library, its
+// address looked up once per device.
+static __device__ unsigned int queue_word;
+
+static hipError_t queue_address(unsigned int** ptr) {
+    static std::mutex mu;
+    static unsigned int* addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(queue_word));
+        if (e != hipSuccess) return e;
+        addr[dev] = static_cast<unsigned int*>(p);
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
+int q4probe_byte_mix_queue(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
+                           float* v_scales, int64_t n, void* stream) {
+    if (n <= 0 || n % kChunk != 0) return Q4PROBE_ERR_ARG;
+    if (!param || !grad || !m_codes || !v_codes || !m_scales || !v_scales) return Q4PROBE_ERR_ARG;
+    if (!a16(param) || !a16(grad) || !a16(m_codes) || !a16(v_codes) || !a16(m_scales) || !a16(v_scales))
+        return Q4PROBE_ERR_ARG;
+    unsigned int* queue = nullptr;
+    if (queue_address(&queue) != hipSuccess) return Q4PROBE_ERR_HIP;
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    const int64_t chunks = n / kChunk;
+    const int64_t slabs = (chunks + kWaves - 1) / kWaves;
+    static std::atomic<int> resident{0};
+    if (resident.load() == 0) resident.store(resident_groups(reinterpret_cast<const void*>(k_byte_mix_queue)));
+    const int64_t groups = resident.load();
+    int run = kRun;
+    while (run > 1 && slabs / run < groups) run >>= 1;
+    const int64_t runs = (slabs + run - 1) / run;
+    if (hipMemsetAsync(queue, 0, sizeof(unsigned int), st) != hipSuccess) return Q4PROBE_ERR_HIP;
+    k_byte_mix_queue<<<(unsigned)(runs < groups ? runs : groups), 256, 0, st>>>(param, grad, m_codes, v_codes,
+                                                                               m_scales, v_scales, chunks, run, queue,
+                                                                               0.999f);
+    return hipGetLastError() == hipSuccess ? Q4PROBE_OK : Q4PROBE_ERR_HIP;
 }
 
 int q4probe_copy(void* dst, const void* src, size_t bytes, void* stream) {

@@ -25,6 +25,8 @@ def load_library():
         L.q4probe_byte_mix.restype = C.c_int
         L.q4probe_copy.argtypes = [vp, vp, C.c_size_t, vp]
         L.q4probe_copy.restype = C.c_int
+        L.q4probe_byte_mix_queue.argtypes = L.q4probe_byte_mix.argtypes
+        L.q4probe_byte_mix_queue.restype = C.c_int
         L.q4probe_update_in_place.argtypes = [vp, C.c_size_t, vp]
         L.q4probe_update_in_place.restype = C.c_int
         L.q4probe_read_sink_words.argtypes = []
@@ -65,10 +67,17 @@ class ByteMix:
         self.m_scales = torch.rand(n // 128, generator=g, device=device) + 0.5
         self.v_scales = torch.rand(n // 128, generator=g, device=device) + 0.5
 
+    def _args(self, stream):
+        return (self.param.data_ptr(), self.grad.data_ptr(), self.m_codes.data_ptr(), self.v_codes.data_ptr(),
+                self.m_scales.data_ptr(), self.v_scales.data_ptr(), self.n, _stream(stream))
+
     def run(self, stream=None) -> None:
-        _ok(load_library().q4probe_byte_mix(self.param.data_ptr(), self.grad.data_ptr(), self.m_codes.data_ptr(),
-                                            self.v_codes.data_ptr(), self.m_scales.data_ptr(),
-                                            self.v_scales.data_ptr(), self.n, _stream(stream)), "q4probe_byte_mix")
+        """The step's own lane layout and work-group walk."""
+        _ok(load_library().q4probe_byte_mix(*self._args(stream)), "q4probe_byte_mix")
+
+    def run_queue(self, stream=None) -> None:
+        """The same bytes taken from a queue of runs (the fastest form)."""
+        _ok(load_library().q4probe_byte_mix_queue(*self._args(stream)), "q4probe_byte_mix_queue")
 
 
 def copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

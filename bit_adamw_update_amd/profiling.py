@@ -48,6 +48,7 @@ PASSES = {
 }
 COPY_KERNEL = "k_copy"
 BYTE_MIX_KERNEL = "k_byte_mix"
+BYTE_MIX_QUEUE_KERNEL = "k_byte_mix_queue"
 
 
 def kernel_hash() -> str:
@@ -155,8 +156,10 @@ def counters(out: str, name: str) -> dict:
     return d
 
 
-def _pick(d: dict, prefix: str) -> list:
-    return [k for k in d if _short(k).startswith(prefix)]
+def _pick(d: dict, name: str) -> list:
+    """The keys of d (full kernel names) whose short name is `name`: every
+    instantiation of that kernel template, and no other kernel."""
+    return [k for k in d if _short(k) == name]
 
 
 # ---------------------------------------------------------------------------
@@ -192,10 +195,12 @@ def summarize(workload: str, recipe: str, out: str, steps: int, warmup: int, des
         lines.append(f"alg_bytes_per_launch: {alg}")
         lines.append(f"alg_gbs: {alg / avg / 1e9:.1f}")
         lines.append(f"frac_of_8tbs: {alg / avg / 8e12:.4f}")
-    bm = _pick(dur, BYTE_MIX_KERNEL)
-    if bm:
-        v = dur[bm[0]]
-        lines.append(f"byte_mix_probe_avg_ms: {sum(v[-steps:]) / len(v[-steps:]) / 1e6:.4f}")
+    for label, probe_kernel in (("byte_mix_probe_avg_ms", BYTE_MIX_QUEUE_KERNEL),
+                                ("byte_mix_step_walk_probe_avg_ms", BYTE_MIX_KERNEL)):
+        bm = _pick(dur, probe_kernel)
+        if bm:
+            v = dur[bm[0]]
+            lines.append(f"{label}: {sum(v[-steps:]) / len(v[-steps:]) / 1e6:.4f}")
     prefix = f"accumulate_{workload}_{recipe}" if STEP_BEFORE else f"{kern}_{workload}_{recipe}"
     trace_file = os.path.join(dest, f"{prefix}_trace.txt")
     os.makedirs(dest, exist_ok=True)
@@ -206,8 +211,8 @@ def summarize(workload: str, recipe: str, out: str, steps: int, warmup: int, des
     lines = head + ["# commands:"] + ["#   " + " ".join(pass_command(p, out, workload, recipe, steps, warmup))
                                       for p in ("fetch", "write", "sq")] + src + [""]
 
-    def per_dispatch(c, prefix, counter):
-        vals = [x for k in _pick(c, prefix) for x in c[k].get(counter, [])]
+    def per_dispatch(c, name, counter):
+        vals = [x for k in _pick(c, name) for x in c[k].get(counter, [])]
         return vals[-steps:] if vals else []
 
     copies_f = per_dispatch(cf, COPY_KERNEL, "FETCH_SIZE")

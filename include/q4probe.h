@@ -43,6 +43,13 @@ int64_t q4probe_byte_mix_bytes(int64_t n);
 int q4probe_byte_mix(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
                      float* v_scales, int64_t n, void* stream);
 
+/* The same byte mix and arithmetic as q4probe_byte_mix, its chunks taken
+ * by one round of resident work-groups from a queue (a device word of this
+ * library, zeroed before the launch; calls that overlap on one device race
+ * on it): the fastest way found to move this byte mix. */
+int q4probe_byte_mix_queue(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
+                           float* v_scales, int64_t n, void* stream);
+
 /* dst <- src, `bytes` (a positive multiple of 16) read and written once. */
 int q4probe_copy(void* dst, const void* src, size_t bytes, void* stream);
 

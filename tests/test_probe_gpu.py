@@ -1,5 +1,5 @@
 """The bandwidth probes (libq4probe.so) do the memory work they claim: the
-byte-mix probe reads and rewrites every byte of its mix (masters, codes and
+byte-mix probe, in both its walks, reads and rewrites every byte of its mix (masters, codes and
 scales changed as its arithmetic says, nothing outside touched), the copy
 copies, the in-place update rewrites every element and the read probe reads
 everything."""
@@ -12,13 +12,17 @@ from bit_adamw_update_amd import probe
 pytestmark = pytest.mark.gpu
 
 
-def test_byte_mix_touches_exactly_its_bytes():
-    n = 512 * 37
+# 37 chunks: one slab-run and a ragged slab; 512 * 4 * 8 * 3000 + 512 * 5:
+# more runs of 8 slabs than resident groups, so the queue hands out runs
+# again, and a ragged last run
+@pytest.mark.parametrize("n", [512 * 37, 512 * (4 * 8 * 3000 + 5)], ids=["small", "queue_laps"])
+@pytest.mark.parametrize("form", ["step_walk", "queue"])
+def test_byte_mix_touches_exactly_its_bytes(form, n):
     bm = probe.ByteMix(n)
     before = {f: getattr(bm, f).clone() for f in ("param", "grad", "m_codes", "v_codes", "m_scales", "v_scales")}
     guard = torch.full((4096,), 7, dtype=torch.uint8, device="cuda")
-    print("byte mix probe", n, flush=True)
-    bm.run()
+    print("byte mix probe", form, n, flush=True)
+    bm.run() if form == "step_walk" else bm.run_queue()
     torch.cuda.synchronize()
     assert probe.byte_mix_bytes(n) == 12 * n + n // 8
     a = np.float32(0.999)

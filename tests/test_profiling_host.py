@@ -14,6 +14,8 @@ HDR_PMC = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","T
            '"Kernel_Name","Workgroup_Size","LDS_Block_Size","Scratch_Size","VGPR_Count","Accum_VGPR_Count",'
            '"SGPR_Count","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"')
 STEP = "void q4::k_fused_step<0, 2, 3, false>(q4::DevTensor const*, long const*, int, long, int, q4::StepScalars)"
+MIX = "(anonymous namespace)::k_byte_mix(float*, unsigned short const*, unsigned char*, long, int, float)"
+MIX_QUEUE = "(anonymous namespace)::k_byte_mix_queue(float*, unsigned short const*, long, int, unsigned int*, float)"
 COPY = "(anonymous namespace)::k_copy(unsigned int __attribute__((ext_vector_type(4)))*, unsigned int const*, long)"
 
 
@@ -41,6 +43,11 @@ def test_summaries_from_synthetic_csv(tmp_path):
     for d in range(12):
         rows.append(f'"KERNEL_DISPATCH","Agent 1",1,0,1,{100 + d},10,"{COPY}",{100 + d},{t},{t + 2000}')
         t += 2100
+    # both byte-mix probes: one short name is a prefix of the other's
+    for name, dur in ((MIX_QUEUE, 3000), (MIX, 3300)):
+        for d in range(steps):
+            rows.append(f'"KERNEL_DISPATCH","Agent 1",1,0,1,{200 + d},11,"{name}",{200 + d},{t},{t + dur}')
+            t += dur + 100
     _write(os.path.join(out, "trace", "host", "trace_kernel_trace.csv"), [HDR_TRACE] + rows)
     copy_kib = bench.COPY_PROBE_BYTES / 1024 / 2           # a counter that reads half the bytes
     for name, counter, step_val in (("fetch", "FETCH_SIZE", 1000.0), ("write", "WRITE_SIZE", 600.0)):
@@ -72,5 +79,7 @@ def test_summaries_from_synthetic_csv(tmp_path):
     assert float(vals["traffic_bytes_per_launch"]) == (1000.0 + 600.0) * 1024 * 2
     assert float(vals["valu_insts_per_element"]) == round(1000.0 * 64 / wl.numel, 3)
     assert vals["kernel_source_sha256_16"] == profiling.kernel_hash()
+    assert float(vals["byte_mix_probe_avg_ms"]) == 0.003
+    assert float(vals["byte_mix_step_walk_probe_avg_ms"]) == 0.0033
     # the benchmark reads the counted traffic back from the committed file
     assert abs(float(vals["VALUBusy"]) - 50.0) < 1e-9
