@@ -150,7 +150,8 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
     constexpr bool V_SR = VRULE == Q4_RULE_STATE_SR || VRULE == Q4_RULE_UPDATE_SR;
     constexpr bool V_UPD = VRULE == Q4_RULE_UPDATE_SR || VRULE == Q4_RULE_UPDATE_RTN;
     const int sub = lane & 15, row_base = lane & 48;
-    const uint32_t rb4x4 = ((uint32_t)row_base << 2) * 0x01010101u;
+    const int rb4 = row_base << 2;
+    const uint32_t rb4x4 = (uint32_t)rb4 * 0x01010101u;
     const int64_t n = T.numel;
     const int64_t blk = lc * kBlocksPerChunk + (lane >> 4);
     // the chunk's bases are wave-uniform (scalar registers); a lane adds a
@@ -415,16 +416,19 @@ __device__ __forceinline__ void step_chunk(const DevTensor& T, const int64_t lc,
             }
             const int lo = floor_index(fthr, flo, x);
             const bool hit = x == fthr;
-            const int src = row_base + lo;
-            const float rlo = bperm(root_own, src);
-            const float rhe = bperm(rnext_eps, src);
-            const float rdf = bperm(rdiff, src);
+            // ds_bpermute byte address of lane row_base + lo
+            const int src4 = (lo << 2) + rb4;
+            const float rlo = bperm_addr(root_own, src4);
+            const float rhe = bperm_addr(rnext_eps, src4);
+            const float rdf = bperm_addr(rdiff, src4);
             // P(up) = (r(a_lo) - r(v)) / (r(a_lo) - r(a_hi)), r(a) = 1/(sqrt(a) + eps_sr),
             // multiplied out so that nothing cancels next to a_lo = 0
             const float num = (sv[k] - rlo) * rhe;
             const float den = rdf * (sv[k] + sc.eps_sr);
-            const bool up = !hit && (uv[k & 3] * den < num);
-            vword |= (uint32_t)(lo + (up ? 1 : 0)) << (4 * k);
+            // both compares in every lane, joined as bits: a short-circuit
+            // here becomes a branch per element around the draw's compare
+            const bool up = (uv[k & 3] * den < num) & !hit;
+            vword |= (uint32_t)(lo + (int)up) << (4 * k);
         }
     } else {
 #pragma unroll
