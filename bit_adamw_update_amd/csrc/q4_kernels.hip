@@ -1227,25 +1227,20 @@ __global__ __launch_bounds__(256) void k_dequant(DevTensor T, float* __restrict_
 // Launchers
 // ---------------------------------------------------------------------------
 
-// Grid of the chunk-walking steps: up to max_mult times the resident
-// work-groups (the queued groups even out the finishing times of the
-// resident ones), but no more than leave every wavefront some
+// Grid of the chunk-walking steps that loop: up to max_mult times the
+// resident work-groups (the queued groups even out the finishing times of
+// the resident ones), but no more than leave every wavefront some
 // min_chunks_per_wave chunks, since each group sets up its tables once; at
-// least the resident groups, never more groups than chunk groups.  The
-// best settings differ by kernel (gfx950, alternating processes on one box,
-// GPT-162M / GPT-2.7B sets):
-//   memory-bound steps (compact tables, 8-bit, FP32): 8x and 5 chunks;
-//     against 4x and 20: ZE-EDEN 0.320 -> 0.3125 ms and 6.371 -> 6.343 ms,
-//     8-bit 0.369 -> 0.360 ms, FP32 (in a form with per-element loads)
-//     1.808 -> 1.762 ms;
-//   the ZIP-SR kernel, whose groups each copy a 24.5 KB table: 4x and 10
-//     chunks, 0.338 -> 0.332 ms (8x and 5 chunks: 0.341 ms);
+// least the resident groups, never more groups than chunk groups
+// (gfx950, alternating processes on one box, GPT-162M / GPT-2.7B sets):
+//   FP32 step: 8x and 5 chunks (against 4x and 20, in a form with
+//     per-element loads, 1.808 -> 1.762 ms);
 //   steps with factored matrices: 2x (Qwen3-0.6B set: 4x 1.83 ms, 2x
 //     1.76 ms, 8x 2.05 ms).
 struct GridPolicy {
     int64_t max_mult, min_chunks_per_wave;
 };
-constexpr GridPolicy kGridMemory{8, 5}, kGridFlat{4, 10}, kGridMatrices{2, 10};
+constexpr GridPolicy kGridFp32{8, 5}, kGridMatrices{2, 10};
 
 template <class K>
 static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds,
@@ -1270,9 +1265,9 @@ static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_ca
     return (int)(groups < cap ? (groups > 0 ? groups : 1) : cap);
 }
 
-// Grid and run length of the quantized steps: the grid of step_grid over
-// slabs, and runs of kRunSlabs slabs while the set still has a run for
-// every resident group (halved until it does, down to single slabs).
+// Grid and run length of the quantized steps: runs of kRunSlabs slabs
+// while the set still has a run for every resident group (halved until it
+// does, down to single slabs), the grid of step_grid over slabs.
 struct RunLaunch {
     int grid, run_slabs;
 };
@@ -1285,6 +1280,41 @@ static RunLaunch run_launch(K kernel, int64_t total_chunks, std::atomic<int>& pe
     while (r > 1 && slabs / r < cap) r >>= 1;
     const int64_t runs = (slabs + r - 1) / r;
     return {(int)(runs < cap ? (runs > 0 ? runs : 1) : cap), r};
+}
+
+// Most work-groups of one launch; a set with more runs loops over them.
+constexpr int64_t kMaxRunGroups = int64_t(1) << 22;
+
+// One work-group per run: the dispatcher starts the groups in order as
+// earlier ones finish, so it hands out the runs like a queue, the fastest
+// order found for these steps' bytes.  On the GPT-2.7B set, against the
+// earlier grids of 4x-8x the resident groups looping over runs (alternating
+// processes, one box, two rounds): ZIP-SR 6.634 -> 6.425 ms, ZE-EDEN
+// 6.352 -> 6.229 ms, 8-bit 7.427 -> 7.331 ms; Llama-1.1B ZIP-SR 2.789 ->
+// 2.699 ms, GPT-162M ZIP-SR 0.327 -> 0.316 ms.  Grids of 16x-32x that loop
+// were slower than both (ZIP-SR 6.84 ms).  Runs are of kRunSlabs slabs,
+// shortened while the set has fewer runs than resident groups.
+template <class K>
+static RunLaunch run_per_group(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds) {
+    static std::atomic<int> cus{0};
+    if (cus.load() == 0) {
+        int dev = 0;
+        hipDeviceProp_t prop;
+        const bool ok = hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess;
+        cus.store(ok && prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256);
+    }
+    int per_cu = per_cu_cache.load();
+    if (per_cu == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, dyn_lds) != hipSuccess || per_cu < 1)
+            per_cu = 1;
+        per_cu_cache.store(per_cu);
+    }
+    const int64_t resident = (int64_t)per_cu * cus.load();
+    const int64_t slabs = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
+    int r = kRunSlabs;
+    while (r > 1 && slabs / r < resident) r >>= 1;
+    const int64_t runs = (slabs + r - 1) / r;
+    return {(int)(runs < 1 ? 1 : (runs > kMaxRunGroups ? kMaxRunGroups : runs)), r};
 }
 
 #define Q4_VARIANTS(X)                                              \
@@ -1313,9 +1343,9 @@ template <int A, int B, int C, bool CLIP, bool MATS>
 static hipError_t launch_step_kernel(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
                                      int n_tensors, int64_t total_chunks, hipStream_t stream) {
     static std::atomic<int> occ{0};
-    const GridPolicy& pol = MATS ? kGridMatrices : (flat_tables<B, C>() ? kGridFlat : kGridMemory);
     const size_t dl = (MATS && !flat_tables<B, C>()) ? kCap7Lds : 0;
-    const RunLaunch L = run_launch(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ, dl, pol);
+    const RunLaunch L = MATS ? run_launch(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ, dl, kGridMatrices)
+                             : run_per_group(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ, dl);
     k_fused_step<A, B, C, CLIP, MATS><<<L.grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks,
                                                                    L.run_slabs, sc);
     return hipGetLastError();
@@ -1354,7 +1384,7 @@ hipError_t launch_fp32_step(const StepScalars& sc, const DevTensor* d_tab, const
                             int n_tensors, int64_t total_chunks, hipStream_t stream) {
     if (total_chunks <= 0) return hipSuccess;
     static std::atomic<int> occ{0};
-    const int grid = step_grid(k_fp32_step, total_chunks, occ, 0, kGridMemory);
+    const int grid = step_grid(k_fp32_step, total_chunks, occ, 0, kGridFp32);
     k_fp32_step<<<grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, sc);
     return hipGetLastError();
 }
@@ -1464,11 +1494,11 @@ hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, con
     if (total_chunks <= 0) return hipSuccess;
     if (sc.flags & SF_CLIP) {
         static std::atomic<int> occ{0};
-        const RunLaunch L = run_launch(k_step8<true>, total_chunks, occ, 0, kGridMemory);
+        const RunLaunch L = run_per_group(k_step8<true>, total_chunks, occ, 0);
         k_step8<true><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     } else {
         static std::atomic<int> occ{0};
-        const RunLaunch L = run_launch(k_step8<false>, total_chunks, occ, 0, kGridMemory);
+        const RunLaunch L = run_per_group(k_step8<false>, total_chunks, occ, 0);
         k_step8<false><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     }
     return hipGetLastError();
