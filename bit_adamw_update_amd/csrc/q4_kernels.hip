@@ -1292,10 +1292,16 @@ constexpr int64_t kMaxRunGroups = int64_t(1) << 22;
 // processes, one box, two rounds): ZIP-SR 6.634 -> 6.425 ms, ZE-EDEN
 // 6.352 -> 6.229 ms, 8-bit 7.427 -> 7.331 ms; Llama-1.1B ZIP-SR 2.789 ->
 // 2.699 ms, GPT-162M ZIP-SR 0.327 -> 0.316 ms.  Grids of 16x-32x that loop
-// were slower than both (ZIP-SR 6.84 ms).  Runs are of kRunSlabs slabs,
-// shortened while the set has fewer runs than resident groups.
+// were slower than both (ZIP-SR 6.84 ms).  Runs are of max_run slabs,
+// shortened while the set has fewer runs than resident groups.  The best
+// length depends on the group's setup: the ZIP-SR kernels, whose groups
+// each copy a 24.5 KB table, take runs of 8 (GPT-2.7B: 4 slabs 6.525 ms, 8
+// 6.357, 16 6.361, 32 6.410); the others take runs of 4 (ZE-EDEN 6.146 ms
+// against 6.207 with 8 and 6.338 with 16; 8-bit 7.259 against 7.321).
+constexpr int kRunSlabsFlat = 8, kRunSlabsCompact = 4;
 template <class K>
-static RunLaunch run_per_group(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds) {
+static RunLaunch run_per_group(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds,
+                               int max_run) {
     static std::atomic<int> cus{0};
     if (cus.load() == 0) {
         int dev = 0;
@@ -1311,7 +1317,7 @@ static RunLaunch run_per_group(K kernel, int64_t total_chunks, std::atomic<int>&
     }
     const int64_t resident = (int64_t)per_cu * cus.load();
     const int64_t slabs = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
-    int r = kRunSlabs;
+    int r = max_run;
     while (r > 1 && slabs / r < resident) r >>= 1;
     const int64_t runs = (slabs + r - 1) / r;
     return {(int)(runs < 1 ? 1 : (runs > kMaxRunGroups ? kMaxRunGroups : runs)), r};
@@ -1345,7 +1351,8 @@ static hipError_t launch_step_kernel(const StepScalars& sc, const DevTensor* d_t
     static std::atomic<int> occ{0};
     const size_t dl = (MATS && !flat_tables<B, C>()) ? kCap7Lds : 0;
     const RunLaunch L = MATS ? run_launch(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ, dl, kGridMatrices)
-                             : run_per_group(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ, dl);
+                             : run_per_group(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ, dl,
+                                             flat_tables<B, C>() ? kRunSlabsFlat : kRunSlabsCompact);
     k_fused_step<A, B, C, CLIP, MATS><<<L.grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks,
                                                                    L.run_slabs, sc);
     return hipGetLastError();
@@ -1494,11 +1501,11 @@ hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, con
     if (total_chunks <= 0) return hipSuccess;
     if (sc.flags & SF_CLIP) {
         static std::atomic<int> occ{0};
-        const RunLaunch L = run_per_group(k_step8<true>, total_chunks, occ, 0);
+        const RunLaunch L = run_per_group(k_step8<true>, total_chunks, occ, 0, kRunSlabsCompact);
         k_step8<true><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     } else {
         static std::atomic<int> occ{0};
-        const RunLaunch L = run_per_group(k_step8<false>, total_chunks, occ, 0);
+        const RunLaunch L = run_per_group(k_step8<false>, total_chunks, occ, 0, kRunSlabsCompact);
         k_step8<false><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     }
     return hipGetLastError();

@@ -8,9 +8,9 @@
 // bytes per element), with the step's lane layout (8 consecutive elements
 // per lane, a 128-element block per 16-lane row, 16-byte accesses for
 // masters and gradients, 4 bytes per moment's codes, the row's scale read by
-// all its lanes and written by one) and its work distribution (4-wavefront
-// groups walking runs of consecutive slabs of 4 chunks, at most 4x the
-// resident groups), but only trivial arithmetic.  Its time is what this byte
+// all its lanes and written by one) and its work distribution (one
+// 4-wavefront group per run of consecutive slabs of 4 chunks), but only
+// trivial arithmetic.  Its time is what this byte
 // mix costs on the memory system, whatever the optimizer computes.
 //
 // k_copy is a plain copy (known bytes read and written, 16 bytes per lane
@@ -196,11 +196,13 @@ int q4probe_byte_mix(float* param, const uint16_t* grad, uint8_t* m_codes, uint8
     const int64_t slabs = (chunks + kWaves - 1) / kWaves;
     static std::atomic<int> resident{0};
     if (resident.load() == 0) resident.store(resident_groups(reinterpret_cast<const void*>(k_byte_mix)));
-    const int64_t cap = 4 * (int64_t)resident.load();
+    // one work-group per run, as the quantized steps launch (a set with
+    // more than 2^22 runs loops over them)
     int run = kRun;
-    while (run > 1 && slabs / run < cap) run >>= 1;
+    while (run > 1 && slabs / run < resident.load()) run >>= 1;
     const int64_t runs = (slabs + run - 1) / run;
-    const int grid = (int)(runs < cap ? runs : cap);
+    const int64_t max_groups = int64_t(1) << 22;
+    const int grid = (int)(runs < max_groups ? runs : max_groups);
     k_byte_mix<<<grid, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(param, grad, m_codes, v_codes, m_scales,
                                                                        v_scales, chunks, run, 0.999f);
     return hipGetLastError() == hipSuccess ? Q4PROBE_OK : Q4PROBE_ERR_HIP;
