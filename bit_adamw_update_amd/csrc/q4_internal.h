@@ -20,11 +20,11 @@ constexpr int kColGroup = 64;          // columns per finalize work-group (4 ban
 constexpr int kAccGroups = 2048;       // work-groups of the chunk-order accumulation pass (at most)
 // The quantized steps number chunks in a prefix where every tensor starts at
 // a multiple of kStepAlignChunks (8 chunks = 32 block scales = one 128-byte
-// line of each scale array); a work-group walks runs of consecutive slabs
-// of kWavesPerGroup chunks (up to kRunSlabs where the launch loops over runs;
-// 4 or 8 where each group takes one run), at least 2 slabs (8 chunks) while
-// the set has a run for every resident group, so each scale line is written
-// whole by one work-group.
+// line of each scale array); a work-group of the steps takes one run of 4
+// or 8 consecutive slabs of kWavesPerGroup chunks (at least 2 slabs, 8
+// chunks, while the set has a run for every resident group), so each scale
+// line is written whole by one work-group.  The accumulation pass walks
+// runs of up to kRunSlabs slabs.
 constexpr int64_t kStepAlignChunks = 8;
 constexpr int kRunSlabs = 8;
 

@@ -1227,24 +1227,10 @@ __global__ __launch_bounds__(256) void k_dequant(DevTensor T, float* __restrict_
 // Launchers
 // ---------------------------------------------------------------------------
 
-// Grid of the chunk-walking steps that loop: up to max_mult times the
-// resident work-groups (the queued groups even out the finishing times of
-// the resident ones), but no more than leave every wavefront some
-// min_chunks_per_wave chunks, since each group sets up its tables once; at
-// least the resident groups, never more groups than chunk groups
-// (gfx950, alternating processes on one box, GPT-162M / GPT-2.7B sets):
-//   FP32 step: 8x and 5 chunks (against 4x and 20, in a form with
-//     per-element loads, 1.808 -> 1.762 ms);
-//   steps with factored matrices: 2x (Qwen3-0.6B set: 4x 1.83 ms, 2x
-//     1.76 ms, 8x 2.05 ms).
-struct GridPolicy {
-    int64_t max_mult, min_chunks_per_wave;
-};
-constexpr GridPolicy kGridFp32{8, 5}, kGridMatrices{2, 10};
-
+// Resident 256-thread work-groups of a kernel on the current device (its
+// occupancy per CU, cached by the caller, times the CUs; no dynamic LDS).
 template <class K>
-static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds,
-                     const GridPolicy& pol) {
+static int64_t resident_groups(K kernel, std::atomic<int>& per_cu_cache) {
     static std::atomic<int> cus{0};
     if (cus.load() == 0) {
         int dev = 0;
@@ -1254,68 +1240,54 @@ static int step_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_ca
     }
     int per_cu = per_cu_cache.load();
     if (per_cu == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, dyn_lds) != hipSuccess || per_cu < 1)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess || per_cu < 1)
             per_cu = 1;
         per_cu_cache.store(per_cu);
     }
-    const int64_t groups = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
-    const int64_t resident = (int64_t)per_cu * cus.load();
-    int64_t cap = total_chunks / (kWavesPerGroup * pol.min_chunks_per_wave);
-    cap = cap < resident ? resident : (cap > pol.max_mult * resident ? pol.max_mult * resident : cap);
-    return (int)(groups < cap ? (groups > 0 ? groups : 1) : cap);
+    return (int64_t)per_cu * cus.load();
 }
 
-// Grid and run length of the quantized steps: runs of kRunSlabs slabs
-// while the set still has a run for every resident group (halved until it
-// does, down to single slabs), the grid of step_grid over slabs.
-struct RunLaunch {
-    int grid, run_slabs;
-};
+// Grid of the FP32 step, whose groups loop over chunks: 8x the resident
+// work-groups (the queued groups even out the finishing times of the
+// resident ones), but no more than leave every wavefront ~5 chunks, at least
+// the resident groups, never more groups than chunk groups.  Against 4x and
+// 20 chunks (gfx950, a form with per-element loads): 1.808 -> 1.762 ms on
+// the GPT-162M set; one group per 16 chunks was 5% slower on GPT-2.7B.
 template <class K>
-static RunLaunch run_launch(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds,
-                            const GridPolicy& pol) {
-    const int cap = step_grid(kernel, total_chunks, per_cu_cache, dyn_lds, pol);
-    const int64_t slabs = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
-    int r = kRunSlabs;
-    while (r > 1 && slabs / r < cap) r >>= 1;
-    const int64_t runs = (slabs + r - 1) / r;
-    return {(int)(runs < cap ? (runs > 0 ? runs : 1) : cap), r};
+static int fp32_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache) {
+    const int64_t groups = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
+    const int64_t resident = resident_groups(kernel, per_cu_cache);
+    int64_t cap = total_chunks / (kWavesPerGroup * 5);
+    cap = cap < resident ? resident : (cap > 8 * resident ? 8 * resident : cap);
+    return (int)(groups < cap ? (groups > 0 ? groups : 1) : cap);
 }
 
 // Most work-groups of one launch; a set with more runs loops over them.
 constexpr int64_t kMaxRunGroups = int64_t(1) << 22;
 
-// One work-group per run: the dispatcher starts the groups in order as
-// earlier ones finish, so it hands out the runs like a queue, the fastest
-// order found for these steps' bytes.  On the GPT-2.7B set, against the
-// earlier grids of 4x-8x the resident groups looping over runs (alternating
-// processes, one box, two rounds): ZIP-SR 6.634 -> 6.425 ms, ZE-EDEN
-// 6.352 -> 6.229 ms, 8-bit 7.427 -> 7.331 ms; Llama-1.1B ZIP-SR 2.789 ->
-// 2.699 ms, GPT-162M ZIP-SR 0.327 -> 0.316 ms.  Grids of 16x-32x that loop
-// were slower than both (ZIP-SR 6.84 ms).  Runs are of max_run slabs,
-// shortened while the set has fewer runs than resident groups.  The best
-// length depends on the group's setup: the ZIP-SR kernels, whose groups
-// each copy a 24.5 KB table, take runs of 8 (GPT-2.7B: 4 slabs 6.525 ms, 8
-// 6.357, 16 6.361, 32 6.410); the others take runs of 4 (ZE-EDEN 6.146 ms
-// against 6.207 with 8 and 6.338 with 16; 8-bit 7.259 against 7.321).
+// Grid and run length of the quantized steps: one work-group per run of
+// slabs.  The dispatcher starts the groups in order as earlier ones finish,
+// so it hands out the runs like a queue, the fastest order found for these
+// steps' bytes.  Against the earlier grids of a few times the resident
+// groups looping over runs (gfx950, alternating processes, one box):
+// GPT-2.7B ZIP-SR 6.634 -> 6.425 ms, ZE-EDEN 6.352 -> 6.229 ms, 8-bit
+// 7.427 -> 7.331 ms; Llama-1.1B ZIP-SR 2.789 -> 2.699 ms; GPT-162M ZIP-SR
+// 0.327 -> 0.316 ms; the Qwen3-0.6B factored step 1.653 -> 1.525 ms (from
+// accumulated statistics 1.408 -> 1.265 ms).  Grids of 16x-32x the resident
+// groups that loop were slower than both (ZIP-SR 6.84 ms).  Runs are of
+// max_run slabs, shortened while the set has fewer runs than resident
+// groups.  The best length depends on the group's setup: the ZIP-SR
+// kernels, whose groups each copy a 24.5 KB table, take runs of 8 (GPT-2.7B:
+// 4 slabs 6.525 ms, 8 6.357, 16 6.361, 32 6.410); the others take runs of 4
+// (ZE-EDEN 6.146 ms against 6.207 with 8 and 6.338 with 16; 8-bit 7.259
+// against 7.321 with 8 and 7.41 with 2; factored 1.525 against 1.573 with 8).
+struct RunLaunch {
+    int grid, run_slabs;
+};
 constexpr int kRunSlabsFlat = 8, kRunSlabsCompact = 4;
 template <class K>
-static RunLaunch run_per_group(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, size_t dyn_lds,
-                               int max_run) {
-    static std::atomic<int> cus{0};
-    if (cus.load() == 0) {
-        int dev = 0;
-        hipDeviceProp_t prop;
-        const bool ok = hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess;
-        cus.store(ok && prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256);
-    }
-    int per_cu = per_cu_cache.load();
-    if (per_cu == 0) {
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, dyn_lds) != hipSuccess || per_cu < 1)
-            per_cu = 1;
-        per_cu_cache.store(per_cu);
-    }
-    const int64_t resident = (int64_t)per_cu * cus.load();
+static RunLaunch run_per_group(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, int max_run) {
+    const int64_t resident = resident_groups(kernel, per_cu_cache);
     const int64_t slabs = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
     int r = max_run;
     while (r > 1 && slabs / r < resident) r >>= 1;
@@ -1340,21 +1312,14 @@ bool variant_supported(const Variant& v) {
     return false;
 }
 
-// Reserved (unused) LDS that caps a 4-wave work-group of the step at 7 per
-// CU (160 KiB of LDS): with factored matrices the kernel that fits 8 ran the
-// Qwen3-0.6B set 3% slower than at 7 (same box).
-constexpr size_t kCap7Lds = 19456;
-
 template <int A, int B, int C, bool CLIP, bool MATS>
 static hipError_t launch_step_kernel(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
                                      int n_tensors, int64_t total_chunks, hipStream_t stream) {
     static std::atomic<int> occ{0};
-    const size_t dl = (MATS && !flat_tables<B, C>()) ? kCap7Lds : 0;
-    const RunLaunch L = MATS ? run_launch(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ, dl, kGridMatrices)
-                             : run_per_group(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ, dl,
-                                             flat_tables<B, C>() ? kRunSlabsFlat : kRunSlabsCompact);
-    k_fused_step<A, B, C, CLIP, MATS><<<L.grid, 256, dl, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks,
-                                                                   L.run_slabs, sc);
+    const RunLaunch L = run_per_group(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ,
+                                      flat_tables<B, C>() ? kRunSlabsFlat : kRunSlabsCompact);
+    k_fused_step<A, B, C, CLIP, MATS><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks,
+                                                                  L.run_slabs, sc);
     return hipGetLastError();
 }
 
@@ -1391,7 +1356,7 @@ hipError_t launch_fp32_step(const StepScalars& sc, const DevTensor* d_tab, const
                             int n_tensors, int64_t total_chunks, hipStream_t stream) {
     if (total_chunks <= 0) return hipSuccess;
     static std::atomic<int> occ{0};
-    const int grid = step_grid(k_fp32_step, total_chunks, occ, 0, kGridFp32);
+    const int grid = fp32_grid(k_fp32_step, total_chunks, occ);
     k_fp32_step<<<grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, sc);
     return hipGetLastError();
 }
@@ -1501,11 +1466,11 @@ hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, con
     if (total_chunks <= 0) return hipSuccess;
     if (sc.flags & SF_CLIP) {
         static std::atomic<int> occ{0};
-        const RunLaunch L = run_per_group(k_step8<true>, total_chunks, occ, 0, kRunSlabsCompact);
+        const RunLaunch L = run_per_group(k_step8<true>, total_chunks, occ, kRunSlabsCompact);
         k_step8<true><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     } else {
         static std::atomic<int> occ{0};
-        const RunLaunch L = run_per_group(k_step8<false>, total_chunks, occ, 0, kRunSlabsCompact);
+        const RunLaunch L = run_per_group(k_step8<false>, total_chunks, occ, kRunSlabsCompact);
         k_step8<false><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     }
     return hipGetLastError();
