@@ -544,15 +544,15 @@ void k_fused_step(const DevTensor* __restrict__ tab,
         // stage the bucket tables and sorted levels in LDS
         const BucketEntry* gm = enc_table_global<MCB>();
         const BucketEntry* gv = enc_table_global<VCB>();
-        for (int i = threadIdx.x; i < Enc<VCB>::SIZE; i += blockDim.x) lds.enc_v[i] = gv[i];
+        for (int i = threadIdx.x; i < Enc<VCB>::SIZE; i += 256) lds.enc_v[i] = gv[i];
         if constexpr (FLAT) {
             // each flat slot takes the compact entry of a value inside it
             // (built at compile time, copied in 16-byte pieces)
             copy_flat_table<MCB>(lds.flat);
         } else {
-            for (int i = threadIdx.x; i < Enc<MCB>::SIZE; i += blockDim.x) lds.enc_m[i] = gm[i];
+            for (int i = threadIdx.x; i < Enc<MCB>::SIZE; i += 256) lds.enc_m[i] = gm[i];
             if constexpr (VCB == Q4_CB_DYN4)
-                for (int i = threadIdx.x; i < Enc<VCB>::NPOS; i += blockDim.x) lds.floor_v[i] = c_floor_dyn4.e[i];
+                for (int i = threadIdx.x; i < Enc<VCB>::NPOS; i += 256) lds.floor_v[i] = c_floor_dyn4.e[i];
         }
         if (threadIdx.x < 16) {
             const int t = threadIdx.x;

@@ -281,13 +281,25 @@ __device__ const FlatTable<Q4_CB_NF4> c_flat_nf4 = FlatTable<Q4_CB_NF4>();
 __device__ const FlatTable<Q4_CB_SDYN4> c_flat_sdyn4 = FlatTable<Q4_CB_SDYN4>();
 
 // Copies the flat table of MCB into `dst` (LDS, 16-byte aligned, kFlatAlloc
-// entries); every thread of the work-group takes part.
+// entries), by a 256-thread work-group.  Each thread issues all of its loads
+// before its first store, so the copy waits for L2 once, not once per piece.
 template <int MCB> __device__ __forceinline__ void copy_flat_table(BucketEntry* dst) {
     typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
     const u32x4_t* src = reinterpret_cast<const u32x4_t*>(MCB == Q4_CB_NF4 ? c_flat_nf4.e : c_flat_sdyn4.e);
     u32x4_t* d = reinterpret_cast<u32x4_t*>(dst);
     constexpr int n16 = (int)(sizeof(BucketEntry) * kFlatAlloc / 16);
-    for (int i = threadIdx.x; i < n16; i += blockDim.x) d[i] = src[i];
+    static_assert(n16 > 5 * 256 && n16 <= 6 * 256, "five full passes of 256 pieces and a partial sixth");
+    const int t = (int)threadIdx.x;
+    const bool last = t < n16 - 5 * 256;
+    const u32x4_t a0 = src[t], a1 = src[t + 256], a2 = src[t + 512], a3 = src[t + 768], a4 = src[t + 1024];
+    u32x4_t a5 = {0u, 0u, 0u, 0u};
+    if (last) a5 = src[t + 1280];
+    d[t] = a0;
+    d[t + 256] = a1;
+    d[t + 512] = a2;
+    d[t + 768] = a3;
+    d[t + 1024] = a4;
+    if (last) d[t + 1280] = a5;
 }
 
 // ---------------------------------------------------------------------------
