@@ -322,22 +322,19 @@ template <int MCB> __device__ __forceinline__ void copy_flat_table(BucketEntry* 
 
 __constant__ uint32_t c_cb8[2][256] = {Q4_CB8_BITS_SDYN8, Q4_CB8_BITS_DYN8};
 
-struct Step8Lds {
-    float dec_m[256], dec_v[256];   // code-indexed levels
-    float mid_p[128];               // SDyn8's positive midpoints ascending, +inf padded
-    float mid_v[256];               // Dyn8's midpoints ascending, +inf padded
-    float2 pair_m[128], pair_v[256];  // {mid[i], mid[i + 1]}
-    uint8_t floor_m[Q4_RTN8_M_NB], floor_v[Q4_RTN8_V_NB];  // midpoints below each bucket
-};
 
-// Count of sorted, +inf padded table entries strictly below x (N a power of two).
-template <int N>
-__device__ __forceinline__ int count_below_sorted(const float* mid, float x) {
-    int idx = 0;
-#pragma unroll
-    for (int s = N / 2; s > 0; s >>= 1) idx += mid[idx + s - 1] < x ? s : 0;
-    return idx;
-}
+// The 8-bit tables as the step reads them, formed at compile time and
+// copied into LDS by each work-group: code-indexed levels; {mid[i],
+// mid[i + 1]} over SDyn8's positive midpoints and Dyn8's midpoints,
+// ascending and +inf padded (each midpoint the FP32 sum of adjacent levels
+// halved, as the definition forms it); and per bucket the number of
+// midpoints below it.
+struct alignas(16) Step8Lds {
+    float dec_m[256], dec_v[256];
+    float2 pair_m[128], pair_v[256];
+    uint8_t floor_m[Q4_RTN8_M_NB], floor_v[Q4_RTN8_V_NB];
+};
+static_assert(sizeof(Step8Lds) % 16 == 0, "copied in 16-byte pieces");
 
 // #{midpoints < bits2f(key)} for a non-negative key; keys outside the
 // bucketed range clamp to the first or last bucket (in bounds for any key).
@@ -362,23 +359,53 @@ __device__ __forceinline__ uint32_t rtn8_v(const Step8Lds& lds, float x) {
     return count_below8<Q4_RTN8_V_SHIFT, Q4_RTN8_V_LO, Q4_RTN8_V_NB>(lds.floor_v, lds.pair_v, __float_as_uint(x));
 }
 
-// Fills the tables; every thread of a 256-thread group takes part.
-__device__ void step8_tables(Step8Lds& lds) {
-    const int t = threadIdx.x;
-    const float inf = __builtin_inff();
-    lds.dec_m[t] = bits2f(c_cb8[0][t]);
-    lds.dec_v[t] = bits2f(c_cb8[1][t]);
-    // the same FP32 sum and halving the definition forms; SDyn8's codes
-    // 0..127 ascend from 0, Dyn8's codes 0..255 ascend from 0
-    if (t < 128) lds.mid_p[t] = t < 127 ? (bits2f(c_cb8[0][t]) + bits2f(c_cb8[0][t + 1])) * 0.5f : inf;
-    lds.mid_v[t] = t < 255 ? (bits2f(c_cb8[1][t]) + bits2f(c_cb8[1][t + 1])) * 0.5f : inf;
-    __syncthreads();
-    if (t < 128) lds.pair_m[t] = float2{lds.mid_p[t], t < 127 ? lds.mid_p[t + 1] : inf};
-    lds.pair_v[t] = float2{lds.mid_v[t], t < 255 ? lds.mid_v[t + 1] : inf};
-    for (int b = t; b < Q4_RTN8_M_NB; b += 256)
-        lds.floor_m[b] = (uint8_t)count_below_sorted<128>(lds.mid_p, bits2f((uint32_t)(b + Q4_RTN8_M_LO) << Q4_RTN8_M_SHIFT));
-    for (int b = t; b < Q4_RTN8_V_NB; b += 256)
-        lds.floor_v[b] = (uint8_t)count_below_sorted<256>(lds.mid_v, bits2f((uint32_t)(b + Q4_RTN8_V_LO) << Q4_RTN8_V_SHIFT));
+// The tables' values, formed once at compile time.
+struct Step8Table {
+    Step8Lds t;
+    constexpr Step8Table() : t() {
+        constexpr uint32_t cb_m[256] = Q4_CB8_BITS_SDYN8, cb_v[256] = Q4_CB8_BITS_DYN8;
+        const float inf = __builtin_inff();
+        float mid_p[128] = {}, mid_v[256] = {};
+        for (int i = 0; i < 256; ++i) {
+            t.dec_m[i] = bits2f(cb_m[i]);
+            t.dec_v[i] = bits2f(cb_v[i]);
+        }
+        // SDyn8's codes 0..127 ascend from 0; Dyn8's codes 0..255 ascend from 0
+        for (int i = 0; i < 128; ++i) mid_p[i] = i < 127 ? (bits2f(cb_m[i]) + bits2f(cb_m[i + 1])) * 0.5f : inf;
+        for (int i = 0; i < 256; ++i) mid_v[i] = i < 255 ? (bits2f(cb_v[i]) + bits2f(cb_v[i + 1])) * 0.5f : inf;
+        for (int i = 0; i < 128; ++i) t.pair_m[i] = float2{mid_p[i], i < 127 ? mid_p[i + 1] : inf};
+        for (int i = 0; i < 256; ++i) t.pair_v[i] = float2{mid_v[i], i < 255 ? mid_v[i + 1] : inf};
+        for (int b = 0; b < Q4_RTN8_M_NB; ++b) {
+            const float x = bits2f((uint32_t)(b + Q4_RTN8_M_LO) << Q4_RTN8_M_SHIFT);
+            int n = 0;
+            for (int i = 0; i < 128; ++i) n += mid_p[i] < x ? 1 : 0;
+            t.floor_m[b] = (uint8_t)n;
+        }
+        for (int b = 0; b < Q4_RTN8_V_NB; ++b) {
+            const float x = bits2f((uint32_t)(b + Q4_RTN8_V_LO) << Q4_RTN8_V_SHIFT);
+            int n = 0;
+            for (int i = 0; i < 256; ++i) n += mid_v[i] < x ? 1 : 0;
+            t.floor_v[b] = (uint8_t)n;
+        }
+    }
+};
+__device__ const Step8Table c_step8 = Step8Table();
+
+// Copies the tables into LDS; every thread of a 256-thread group takes part
+// (all of its loads before its first store), and the group synchronizes.
+__device__ __forceinline__ void step8_tables(Step8Lds& lds) {
+    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+    constexpr int n16 = (int)(sizeof(Step8Lds) / 16);
+    static_assert(n16 > 256 && n16 <= 512, "one full pass of 256 pieces and a partial second");
+    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(&c_step8.t);
+    u32x4_t* d = reinterpret_cast<u32x4_t*>(&lds);
+    const int t = (int)threadIdx.x;
+    const bool second = t < n16 - 256;
+    const u32x4_t a0 = src[t];
+    u32x4_t a1 = {0u, 0u, 0u, 0u};
+    if (second) a1 = src[t + 256];
+    d[t] = a0;
+    if (second) d[t + 256] = a1;
     __syncthreads();
 }
 
