@@ -224,8 +224,9 @@ def probe_ceilings(n_elems: int) -> dict:
     """The practical ceilings of this machine, from the hand-written probes of
     libq4probe.so: the step's byte mix (12.125 B per element, the step's lane
     layout, trivial arithmetic) over as many elements as the workload has
-    (rounded up to 512) in its fastest known form (chunks taken from a queue
-    of runs) and, on the same buffers, with the step's own work-group walk;
+    (rounded up to 512), on the same buffers with runs taken from a queue and
+    with the step's own launch of one work-group per run (the ceiling is the
+    faster: the queue on the largest sets, the step's launch on small ones);
     then a plain copy, an in-place update of one buffer and a read."""
     import torch
 
@@ -233,9 +234,11 @@ def probe_ceilings(n_elems: int) -> dict:
     n = (n_elems + 511) // 512 * 512
     bm = probe.ByteMix(n)
     nbytes = probe.byte_mix_bytes(n)
-    ms = _time_launches(bm.run_queue, PROBE_LAUNCHES)
+    ms_queue = _time_launches(bm.run_queue, PROBE_LAUNCHES)
     ms_walk = _time_launches(bm.run, PROBE_LAUNCHES)
+    ms = min(ms_queue, ms_walk)
     out = {"byte_mix_ceiling_gbs": nbytes / (ms * 1e-3) / 1e9, "byte_mix_elems": n, "byte_mix_ms": ms,
+           "byte_mix_queue_gbs": nbytes / (ms_queue * 1e-3) / 1e9,
            "byte_mix_step_walk_gbs": nbytes / (ms_walk * 1e-3) / 1e9}
     del bm
     torch.cuda.empty_cache()
