@@ -4,6 +4,7 @@
 // and enqueues nothing when it returns an error.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -342,7 +343,10 @@ void plan_layout(const Resolved& r, const q4_tensor* t, int32_t n, Plan& P, uint
     P.off_prow = o;      o = round256(o + sizeof(double) * prow);
     P.off_pcol = o;      o = round256(o + sizeof(double) * pcol);
     P.off_pmean = o;     o = round256(o + sizeof(double) * pmean);
-    P.off_sqpart = o;    o = round256(o + sizeof(double) * (size_t)(kAccGroups + P.total_tiles));
+    // the chunk pass runs over all tensors, or over the non-matrix ones when
+    // the tile kernel takes the matrices: room for the larger launch
+    const int64_t acc_groups = std::max(acc_launch(P.total_chunks).groups, acc_launch(P.total_chunks1).groups);
+    P.off_sqpart = o;    o = round256(o + sizeof(double) * (size_t)(acc_groups + P.total_tiles + kSqStageGroups));
     P.total = o;
     if (ws) {  // resolve offsets into device addresses
         for (DevMatrix& m : P.mats) {

@@ -17,7 +17,6 @@ constexpr int kBandRows = 256;         // rows per band of the row/column partia
 constexpr int kTileCols = 512;         // columns per tile (64 lanes x 8 BF16)
 constexpr int kGroup = 256;            // rows per finalize work-group
 constexpr int kColGroup = 64;          // columns per finalize work-group (4 band slices of 64 lanes)
-constexpr int kAccGroups = 2048;       // work-groups of the chunk-order accumulation pass (at most)
 // The quantized steps number chunks in a prefix where every tensor starts at
 // a multiple of kStepAlignChunks (8 chunks = 32 block scales = one 128-byte
 // line of each scale array); a work-group of the steps takes one run of 4
@@ -119,11 +118,22 @@ hipError_t launch_factored_stats(const DevMatrix* d_mats, int n_mats, int64_t to
                                  hipStream_t stream);
 // One pass over the gradients: mode GradMode; with `last` it also leaves the
 // factored row/column partials of matrices (when `tiles_for_matrices`) and
-// the binary64 sums of squares in sq_part (kAccGroups + total_tiles slots),
-// then their total in *sq.
+// the binary64 sums of squares in sq_part (acc_launch(chunks).groups +
+// total_tiles slots, then kSqStageGroups more for the first stage of the
+// total), then their total in *sq.
 // With last and matrices, the tile kernel takes the matrices and the chunk
 // pass runs over d_tab1 / d_chunks1 (the other tensors alone, each entry
 // keeping its chunk_begin in the full prefix for the flat offset).
+// Work-groups and run length of the chunk-order accumulation pass over
+// total_chunks chunks: one group per run of up to 4 slabs (shorter runs
+// while the set has fewer than 2048 of them), at most 2^22 groups, each
+// leaving one partial sum of squares when it is the last pass.
+struct AccLaunch {
+    int64_t groups;
+    int run_slabs;
+};
+AccLaunch acc_launch(int64_t total_chunks);
+constexpr int kSqStageGroups = 256;  // work-groups of the total's first stage
 hipError_t launch_grad_pass(int mode, bool last, bool tiles_for_matrices, const DevTensor* d_tab,
                             const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks, const DevMatrix* d_mats,
                             int n_mats, int64_t total_tiles, const DevTensor* d_tab1, const int64_t* d_chunks1,
