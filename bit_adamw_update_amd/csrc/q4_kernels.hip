@@ -613,14 +613,15 @@ __device__ __forceinline__ void fp32_adamw(const StepScalars& sc, float g, float
 // instruction) ran the GPT-162M set at 1.9 TB/s.
 __global__ __launch_bounds__(256) void k_fp32_step(const DevTensor* __restrict__ tab,
                                                     const int64_t* __restrict__ chunk_begin, int n_tensors,
-                                                    int64_t total_chunks, StepScalars sc) {
+                                                    int64_t total_chunks, int run_slabs, StepScalars sc) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int le = lane * 8;
     const float gs = (sc.flags & SF_CLIP) ? *clip_of_table(tab) : 1.0f;
-    int t = first_tensor(chunk_begin, n_tensors, (int64_t)blockIdx.x * kWavesPerGroup + wave);
-    for (int64_t c = (int64_t)blockIdx.x * kWavesPerGroup + wave; c < total_chunks;
-         c += (int64_t)gridDim.x * kWavesPerGroup) {
+    const int64_t ngroups = gridDim.x;
+    int64_t c = (int64_t)blockIdx.x * run_slabs * kWavesPerGroup + wave;
+    int t = first_tensor(chunk_begin, n_tensors, c);
+    for (int j = 0; c < total_chunks; c = next_chunk(c, j, run_slabs, ngroups)) {
         while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
         const DevTensor T = tab[t];
         const int64_t c0 = (c - T.chunk_begin) * kChunkElems;  // wave-uniform
@@ -1261,21 +1262,6 @@ static int64_t resident_groups(K kernel, std::atomic<int>& per_cu_cache) {
     return (int64_t)per_cu * cus.load();
 }
 
-// Grid of the FP32 step, whose groups loop over chunks: 8x the resident
-// work-groups (the queued groups even out the finishing times of the
-// resident ones), but no more than leave every wavefront ~5 chunks, at least
-// the resident groups, never more groups than chunk groups.  Against 4x and
-// 20 chunks (gfx950, a form with per-element loads): 1.808 -> 1.762 ms on
-// the GPT-162M set; one group per 16 chunks was 5% slower on GPT-2.7B.
-template <class K>
-static int fp32_grid(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache) {
-    const int64_t groups = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
-    const int64_t resident = resident_groups(kernel, per_cu_cache);
-    int64_t cap = total_chunks / (kWavesPerGroup * 5);
-    cap = cap < resident ? resident : (cap > 8 * resident ? 8 * resident : cap);
-    return (int)(groups < cap ? (groups > 0 ? groups : 1) : cap);
-}
-
 // Most work-groups of one launch; a set with more runs loops over them.
 constexpr int64_t kMaxRunGroups = int64_t(1) << 22;
 
@@ -1287,10 +1273,11 @@ constexpr int64_t kMaxRunGroups = int64_t(1) << 22;
 // GPT-2.7B ZIP-SR 6.634 -> 6.425 ms, ZE-EDEN 6.352 -> 6.229 ms, 8-bit
 // 7.427 -> 7.331 ms; Llama-1.1B ZIP-SR 2.789 -> 2.699 ms; GPT-162M ZIP-SR
 // 0.327 -> 0.316 ms; the Qwen3-0.6B factored step 1.653 -> 1.525 ms (from
-// accumulated statistics 1.408 -> 1.265 ms).  Grids of 16x-32x the resident
-// groups that loop were slower than both (ZIP-SR 6.84 ms).  Runs are of
-// max_run slabs, shortened while the set has fewer runs than resident
-// groups.  The best length depends on the group's setup: the ZIP-SR
+// accumulated statistics 1.408 -> 1.265 ms); the FP32 step, whose groups
+// had swept the chunks grid-stride, 13.925 -> 13.49 ms.  Grids of 16x-32x
+// the resident groups that loop were slower than both (ZIP-SR 6.84 ms).
+// Runs are of max_run slabs, shortened while the set has fewer runs than
+// resident groups.  The best length depends on the group's setup: the ZIP-SR
 // kernels, whose groups each copy a 24.5 KB table, take runs of 8 (GPT-2.7B:
 // 4 slabs 6.525 ms, 8 6.357, 16 6.361, 32 6.410); the others take runs of 4
 // (ZE-EDEN 6.146 ms against 6.207 with 8 and 6.338 with 16; 8-bit 7.259
@@ -1370,8 +1357,8 @@ hipError_t launch_fp32_step(const StepScalars& sc, const DevTensor* d_tab, const
                             int n_tensors, int64_t total_chunks, hipStream_t stream) {
     if (total_chunks <= 0) return hipSuccess;
     static std::atomic<int> occ{0};
-    const int grid = fp32_grid(k_fp32_step, total_chunks, occ);
-    k_fp32_step<<<grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, sc);
+    const RunLaunch L = run_per_group(k_fp32_step, total_chunks, occ, kRunSlabsCompact);
+    k_fp32_step<<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     return hipGetLastError();
 }
 
