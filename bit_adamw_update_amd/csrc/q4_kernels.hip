@@ -540,32 +540,48 @@ void k_fused_step(const DevTensor* __restrict__ tab,
                                                      int64_t total_chunks, int run_slabs, StepScalars sc) {
     constexpr bool FLAT = flat_tables<VCB, VRULE>();
     __shared__ StepLds<MCB, VCB, FLAT> lds;
-    {
-        // stage the bucket tables and sorted levels in LDS
-        const BucketEntry* gm = enc_table_global<MCB>();
-        const BucketEntry* gv = enc_table_global<VCB>();
-        for (int i = threadIdx.x; i < Enc<VCB>::SIZE; i += 256) lds.enc_v[i] = gv[i];
-        if constexpr (FLAT) {
-            // each flat slot takes the compact entry of a value inside it
-            // (built at compile time, copied in 16-byte pieces)
-            copy_flat_table<MCB>(lds.flat);
-        } else {
-            for (int i = threadIdx.x; i < Enc<MCB>::SIZE; i += 256) lds.enc_m[i] = gm[i];
-            if constexpr (VCB == Q4_CB_DYN4)
-                for (int i = threadIdx.x; i < Enc<VCB>::NPOS; i += 256) lds.floor_v[i] = c_floor_dyn4.e[i];
-        }
-        if (threadIdx.x < 16) {
-            const int t = threadIdx.x;
-            lds.lev_m[t] = t < Book<MCB>::N ? sorted_level_rt<MCB>(t) : 1.0f;
-            lds.lev_v[t] = t < Book<VCB>::N ? sorted_level_rt<VCB>(t) : 1.0f;
-        }
-    }
     const int lane = threadIdx.x & 63;
     const int sub = lane & 15;
     LaneBooks lb;
-    lb.dec_m = bits2f(c_decode[MCB][sub]);
-    lb.dec_v = bits2f(c_decode[VCB][sub]);
-    lb.lev_v = sub < Book<VCB>::N ? sorted_level_rt<VCB>(sub) : 1.0f;
+    {
+        // Stage the bucket tables and sorted levels in LDS.  Every global
+        // load of the setup is issued before the first LDS store, so a
+        // work-group's setup waits for L2 once (the loads use in-bounds
+        // indices in every thread; only the stores are conditional).
+        static_assert(Enc<VCB>::SIZE <= 256 && Enc<MCB>::SIZE <= 256 && Enc<VCB>::NPOS <= 256,
+                      "one table entry per thread");
+        const int t = threadIdx.x;
+        const BucketEntry ev = enc_table_global<VCB>()[t < Enc<VCB>::SIZE ? t : 0];
+        BucketEntry em{};
+        FloorEntry ef{};
+        FlatPieces fp{};
+        if constexpr (FLAT) {
+            // each flat slot takes the compact entry of a value inside it
+            // (built at compile time, copied in 16-byte pieces)
+            fp = load_flat_table<MCB>();
+        } else {
+            em = enc_table_global<MCB>()[t < Enc<MCB>::SIZE ? t : 0];
+            if constexpr (VCB == Q4_CB_DYN4) ef = c_floor_dyn4.e[t < Enc<VCB>::NPOS ? t : 0];
+        }
+        // lane `sub`'s levels: lanes 0..15 of the group also fill the sorted
+        // level tables
+        const float lev_m = sub < Book<MCB>::N ? sorted_level_rt<MCB>(sub) : 1.0f;
+        lb.dec_m = bits2f(c_decode[MCB][sub]);
+        lb.dec_v = bits2f(c_decode[VCB][sub]);
+        lb.lev_v = sub < Book<VCB>::N ? sorted_level_rt<VCB>(sub) : 1.0f;
+        if (t < Enc<VCB>::SIZE) lds.enc_v[t] = ev;
+        if constexpr (FLAT) {
+            store_flat_table(lds.flat, fp);
+        } else {
+            if (t < Enc<MCB>::SIZE) lds.enc_m[t] = em;
+            if constexpr (VCB == Q4_CB_DYN4)
+                if (t < Enc<VCB>::NPOS) lds.floor_v[t] = ef;
+        }
+        if (t < 16) {
+            lds.lev_m[t] = lev_m;
+            lds.lev_v[t] = lb.lev_v;
+        }
+    }
     __syncthreads();
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

@@ -280,26 +280,41 @@ static_assert(sizeof(BucketEntry) * kFlatAlloc % 16 == 0, "the flat table is cop
 __device__ const FlatTable<Q4_CB_NF4> c_flat_nf4 = FlatTable<Q4_CB_NF4>();
 __device__ const FlatTable<Q4_CB_SDYN4> c_flat_sdyn4 = FlatTable<Q4_CB_SDYN4>();
 
-// Copies the flat table of MCB into `dst` (LDS, 16-byte aligned, kFlatAlloc
-// entries), by a 256-thread work-group.  Each thread issues all of its loads
-// before its first store, so the copy waits for L2 once, not once per piece.
-template <int MCB> __device__ __forceinline__ void copy_flat_table(BucketEntry* dst) {
-    typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(MCB == Q4_CB_NF4 ? c_flat_nf4.e : c_flat_sdyn4.e);
-    u32x4_t* d = reinterpret_cast<u32x4_t*>(dst);
-    constexpr int n16 = (int)(sizeof(BucketEntry) * kFlatAlloc / 16);
-    static_assert(n16 > 5 * 256 && n16 <= 6 * 256, "five full passes of 256 pieces and a partial sixth");
+// The flat table of MCB copied into LDS by a 256-thread work-group in two
+// halves: each thread loads its pieces (load_flat_table), and only then
+// stores them (store_flat_table), so the copy waits for L2 once, not once
+// per piece.  The step kernels issue their other setup loads in between.
+typedef uint32_t FlatPiece __attribute__((ext_vector_type(4)));
+struct FlatPieces {
+    FlatPiece a0, a1, a2, a3, a4, a5;
+};
+constexpr int kFlatPieces = (int)(sizeof(BucketEntry) * kFlatAlloc / 16);
+static_assert(kFlatPieces > 5 * 256 && kFlatPieces <= 6 * 256, "five full passes of 256 pieces and a partial sixth");
+template <int MCB> __device__ __forceinline__ FlatPieces load_flat_table() {
+    const FlatPiece* src = reinterpret_cast<const FlatPiece*>(MCB == Q4_CB_NF4 ? c_flat_nf4.e : c_flat_sdyn4.e);
     const int t = (int)threadIdx.x;
-    const bool last = t < n16 - 5 * 256;
-    const u32x4_t a0 = src[t], a1 = src[t + 256], a2 = src[t + 512], a3 = src[t + 768], a4 = src[t + 1024];
-    u32x4_t a5 = {0u, 0u, 0u, 0u};
-    if (last) a5 = src[t + 1280];
-    d[t] = a0;
-    d[t + 256] = a1;
-    d[t + 512] = a2;
-    d[t + 768] = a3;
-    d[t + 1024] = a4;
-    if (last) d[t + 1280] = a5;
+    FlatPieces p;
+    p.a0 = src[t];
+    p.a1 = src[t + 256];
+    p.a2 = src[t + 512];
+    p.a3 = src[t + 768];
+    p.a4 = src[t + 1024];
+    p.a5 = src[t < kFlatPieces - 1280 ? t + 1280 : 0];  // in bounds; stored only where it is a piece
+    return p;
+}
+// `dst`: LDS, 16-byte aligned, kFlatAlloc entries.
+__device__ __forceinline__ void store_flat_table(BucketEntry* dst, const FlatPieces& p) {
+    FlatPiece* d = reinterpret_cast<FlatPiece*>(dst);
+    const int t = (int)threadIdx.x;
+    d[t] = p.a0;
+    d[t + 256] = p.a1;
+    d[t + 512] = p.a2;
+    d[t + 768] = p.a3;
+    d[t + 1024] = p.a4;
+    if (t < kFlatPieces - 1280) d[t + 1280] = p.a5;
+}
+template <int MCB> __device__ __forceinline__ void copy_flat_table(BucketEntry* dst) {
+    store_flat_table(dst, load_flat_table<MCB>());
 }
 
 // ---------------------------------------------------------------------------
