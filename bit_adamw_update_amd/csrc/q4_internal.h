@@ -22,10 +22,8 @@ constexpr int kColGroup = 64;          // columns per finalize work-group (4 ban
 // line of each scale array); a work-group of the steps takes one run of 4
 // or 8 consecutive slabs of kWavesPerGroup chunks (at least 2 slabs, 8
 // chunks, while the set has a run for every resident group), so each scale
-// line is written whole by one work-group.  The accumulation pass walks
-// runs of up to kRunSlabs slabs.
+// line is written whole by one work-group.
 constexpr int64_t kStepAlignChunks = 8;
-constexpr int kRunSlabs = 8;
 
 // Gradient pass modes: read the gradient for its statistics only, copy the
 // microbatch into it, or add the microbatch to it.
@@ -116,14 +114,6 @@ hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, con
 hipError_t launch_factored_stats(const DevMatrix* d_mats, int n_mats, int64_t total_tiles, int64_t total_rgroups,
                                  int64_t total_cgroups, float beta2, float omb2, const float* clip, bool partials_ready,
                                  hipStream_t stream);
-// One pass over the gradients: mode GradMode; with `last` it also leaves the
-// factored row/column partials of matrices (when `tiles_for_matrices`) and
-// the binary64 sums of squares in sq_part (acc_launch(chunks).groups +
-// total_tiles slots, then kSqStageGroups more for the first stage of the
-// total), then their total in *sq.
-// With last and matrices, the tile kernel takes the matrices and the chunk
-// pass runs over d_tab1 / d_chunks1 (the other tensors alone, each entry
-// keeping its chunk_begin in the full prefix for the flat offset).
 // Work-groups and run length of the chunk-order accumulation pass over
 // total_chunks chunks: one group per run of up to 4 slabs (shorter runs
 // while the set has fewer than 2048 of them), at most 2^22 groups, each
@@ -134,6 +124,14 @@ struct AccLaunch {
 };
 AccLaunch acc_launch(int64_t total_chunks);
 constexpr int kSqStageGroups = 256;  // work-groups of the total's first stage
+// One pass over the gradients: mode GradMode; with `last` it also leaves the
+// factored row/column partials of matrices (when `tiles_for_matrices`) and
+// the binary64 sums of squares in sq_part (acc_launch(chunks).groups +
+// total_tiles slots, then kSqStageGroups more for the first stage of the
+// total), then their total in *sq.
+// With last and matrices, the tile kernel takes the matrices and the chunk
+// pass runs over d_tab1 / d_chunks1 (the other tensors alone, each entry
+// keeping its chunk_begin in the full prefix for the flat offset).
 hipError_t launch_grad_pass(int mode, bool last, bool tiles_for_matrices, const DevTensor* d_tab,
                             const int64_t* d_chunk_begin, int n_tensors, int64_t total_chunks, const DevMatrix* d_mats,
                             int n_mats, int64_t total_tiles, const DevTensor* d_tab1, const int64_t* d_chunks1,
