@@ -106,6 +106,14 @@ def test_zero_size_tensors_between_others():
     run_windows(inputs.custom(shapes, grad_kind="masked", seed=43), 4)
 
 
+def test_mid_size_set_takes_short_runs():
+    """About 10.2 M elements: the one-group-per-run launch takes runs of 2
+    slabs here (fewer than 4 x 2,048 resident groups' worth of slabs)."""
+    shapes = [(1024, 4096), (2048, 2048), (1_000_003,), (777, 1031), (4097,)]
+    _flush("block8 mid-size set")
+    run_windows(inputs.custom(shapes, grad_kind="masked", seed=45), 3)
+
+
 def test_two_thousand_small_tensors():
     rng = np.random.default_rng(30)
     shapes = [(int(rng.integers(1, 1501)),) for _ in range(2000)]
