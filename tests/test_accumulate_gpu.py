@@ -83,6 +83,27 @@ def test_accumulation_and_norm_match_oracle(recipe):
     assert abs(st.grad_norm() - ref) <= 1e-12 * ref
 
 
+@pytest.mark.parametrize("recipe", ["zip_sr", "factored"])
+def test_mid_size_accumulation_and_norm(recipe):
+    """About 10.2 M elements: the accumulation pass takes one work-group per
+    run of 2 slabs (about 2,500 partial sums, totalled in two stages); the
+    factored recipe's matrices go through the tile pass instead, the vector
+    through the chunk pass."""
+    shapes = [(1024, 4096), (2048, 2048), (1_000_003,), (777, 1031), (4097,)]
+    w, st, params, grads, offsets, total = setup(recipe, seed=35, shapes=shapes)
+    _flush(f"accumulate mid-size {recipe}")
+    micro = microbatches(w, 2, offsets, total)
+    for k, flat in enumerate(micro):
+        m = torch.from_numpy(flat.view(np.int16)).view(torch.bfloat16).cuda()
+        st.accumulate(params, grads, m, first=(k == 0), last=(k == len(micro) - 1))
+    norm = st.grad_norm()
+    acc = host_accumulate(w, micro, offsets)
+    for i in range(len(w.tensors)):
+        assert np.array_equal(grads[i].view(torch.uint16).cpu().numpy(), acc[i]), f"tensor {i}"
+    ref = np.sqrt(sum(O.grad_sumsq(a) for a in acc))
+    assert abs(norm - ref) <= 1e-12 * ref
+
+
 def _variant_cfg(variant):
     cfg = q4.q4adamw_default_config(q4.RECIPE_CUSTOM)
     cfg.m_codebook, cfg.v_codebook, cfg.m_rule, cfg.v_rule, cfg.eden = variant
