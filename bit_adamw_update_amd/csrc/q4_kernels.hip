@@ -1307,6 +1307,9 @@ static RunLaunch run_per_group(K kernel, int64_t total_chunks, std::atomic<int>&
     const int64_t resident = resident_groups(kernel, per_cu_cache);
     const int64_t slabs = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
     int r = max_run;
+    // a set of fewer than 8 rounds of groups takes runs of at most 4 slabs,
+    // for a finer last round (GPT-162M ZIP-SR 0.3177 -> 0.3161 ms)
+    if (r > 4 && slabs / r < 8 * resident) r = 4;
     while (r > 1 && slabs / r < resident) r >>= 1;
     const int64_t runs = (slabs + r - 1) / r;
     return {(int)(runs < 1 ? 1 : (runs > kMaxRunGroups ? kMaxRunGroups : runs)), r};

@@ -94,8 +94,9 @@ def test_mid_size_set_takes_short_runs(recipe):
 
 def test_zip_sr_set_takes_runs_of_4():
     """About 19.1 M elements (about 9,300 slabs): the ZIP-SR kernel, whose
-    groups take runs of up to 8 slabs, halves them to 4 here (fewer than 8 x
-    1,536 resident groups' worth of slabs).  Every element, 2 steps."""
+    groups take runs of up to 8 slabs, takes runs of 4 here (fewer than 8
+    rounds of 1,536 resident groups, and more than 4 x 1,536 slabs).  Every
+    element, 2 steps."""
     shapes = [(4096, 4096), (1_500_001,), (1031, 777), (3,)]
     w = inputs.custom(shapes, grad_kind="masked", seed=34)
     _flush("zip_sr runs of 4")
