@@ -220,28 +220,39 @@ def _time_launches(fn, launches: int) -> float:
     return s.elapsed_time(e) / launches
 
 
-def probe_ceilings(n_elems: int) -> dict:
-    """The practical ceilings of this box, from the hand-written probes of
-    libq4probe.so: the step's byte mix (12.125 B per element, the step's lane
-    layout, trivial arithmetic) over as many elements as the workload has
-    (rounded up to 512), on the same buffers with runs taken from a queue and
-    with the step's own launch of one work-group per run (the ceiling is the
-    faster: the queue on the largest sets, the step's launch on small ones);
-    then a plain copy, an in-place update of one buffer and a read."""
+def byte_mix_ceiling(n_elems: int, bits: int = 4) -> dict:
+    """The step's byte mix (libq4probe.so: 12.125 B per element with 4-bit
+    codes, 14.125 B with the 8-bit step's bytes; the step's lane layout,
+    trivial arithmetic) over as many elements as the workload has (rounded
+    up to 512), on the same buffers with runs taken from a queue and with the
+    step's own launch of one work-group per run. The ceiling is the faster:
+    the queue on the largest sets, the step's launch on small ones."""
     import torch
 
     from bit_adamw_update_amd import probe
     n = (n_elems + 511) // 512 * 512
-    bm = probe.ByteMix(n)
-    nbytes = probe.byte_mix_bytes(n)
+    bm = probe.ByteMix(n, bits=bits)
+    nbytes = bm.bytes()
     ms_queue = _time_launches(bm.run_queue, PROBE_LAUNCHES)
     ms_walk = _time_launches(bm.run, PROBE_LAUNCHES)
     ms = min(ms_queue, ms_walk)
     out = {"byte_mix_ceiling_gbs": nbytes / (ms * 1e-3) / 1e9, "byte_mix_elems": n, "byte_mix_ms": ms,
+           "byte_mix_code_bits": bits,
            "byte_mix_queue_gbs": nbytes / (ms_queue * 1e-3) / 1e9,
            "byte_mix_step_walk_gbs": nbytes / (ms_walk * 1e-3) / 1e9}
     del bm
     torch.cuda.empty_cache()
+    return out
+
+
+def probe_ceilings(n_elems: int, bits: int = 4) -> dict:
+    """The practical ceilings of this box, from the hand-written probes of
+    libq4probe.so: the step's byte mix (byte_mix_ceiling), then a plain copy,
+    an in-place update of one buffer and a read."""
+    import torch
+
+    from bit_adamw_update_amd import probe
+    out = byte_mix_ceiling(n_elems, bits)
     a = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     ms = _time_launches(lambda: probe.copy(b, a), PROBE_LAUNCHES)
@@ -353,7 +364,7 @@ def main():
                           "accumulate_ms": acc_ms, "accumulate_gbs": 6 * n / (acc_ms * 1e-3) / 1e9,
                           "step_ms": st_ms, "max_grad_norm": args.max_grad_norm,
                           # the same probes as the main run (the copy calibrates the counters)
-                          **probe_ceilings(n)}), flush=True)
+                          **probe_ceilings(n, 8 if args.recipe == "block8" else 4)}), flush=True)
         return
     r = time_workload(wl, args.recipe, args.steps, args.warmup,
                       lm_head_phase=wl.lm_head_switch)
@@ -394,7 +405,8 @@ def main():
                      "launch_ms": {"mean": avg_launch, "median": statistics.median(launch_ms),
                                    "min": min(launch_ms), "max": max(launch_ms)}},
     }
-    ceil = probe_ceilings(n)
+    # the 8-bit step's own byte mix for it; the 4-bit mix for the others
+    ceil = probe_ceilings(n, 8 if args.recipe == "block8" else 4)
     log(f"probes: {ceil}")
     result["roofline"]["byte_mix_ceiling_gbs"] = ceil["byte_mix_ceiling_gbs"]
     result["roofline"]["frac_of_ceiling"] = achieved / ceil["byte_mix_ceiling_gbs"]
@@ -424,9 +436,16 @@ def main():
                 "step_launch_ms": avg, "alg_gbs": (b2 + extra) / (avg * 1e-3) / 1e9,
                 "frac_of_peak": (b2 + extra) / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS,
                 "alg_bytes_per_param": (b2 + extra) / w2.numel, "warmup_run": v["warmup_run"]}
-            log(f"{wname}/{rec}: {variants[f'{wname}/{rec}']}")
             del v
             torch.cuda.empty_cache()
+            if rec == "block8":
+                # the 8-bit step against its own byte mix, over the same elements
+                c8 = byte_mix_ceiling(w2.numel, bits=8)
+                variants[f"{wname}/{rec}"].update(
+                    byte_mix8_ceiling_gbs=c8["byte_mix_ceiling_gbs"], byte_mix8_queue_gbs=c8["byte_mix_queue_gbs"],
+                    byte_mix8_step_walk_gbs=c8["byte_mix_step_walk_gbs"],
+                    frac_of_ceiling=variants[f"{wname}/{rec}"]["alg_gbs"] / c8["byte_mix_ceiling_gbs"])
+            log(f"{wname}/{rec}: {variants[f'{wname}/{rec}']}")
         # the step before ([A] "State representation"): accumulation pass with
         # statistics, then the step that reuses them (no second gradient read)
         for wname, rec, clip in (("qwen3-0.6b-factored", "factored", 0.0), ("gpt-2.7b", "zip_sr", 1.0)):

@@ -13,6 +13,9 @@
 // trivial arithmetic.  Its time is what this byte
 // mix costs on the memory system, whatever the optimizer computes.
 //
+// k_byte_mix8 does the same for the 8-bit blockwise step: one code byte per
+// element and moment (8 bytes per lane), 14.125 bytes per element.
+//
 // k_copy is a plain copy (known bytes read and written, 16 bytes per lane
 // access), which also calibrates the HBM traffic counters; k_update rewrites
 // a buffer in place, as the step rewrites its masters, codes and scales;
@@ -28,11 +31,14 @@
 
 namespace {
 
-constexpr int kChunk = 512, kWaves = 4, kRun = 8;
+// runs of slabs: 8 as the ZIP-SR steps take them (the 4-bit mix), 4 as the
+// 8-bit step does
+constexpr int kChunk = 512, kWaves = 4, kRun = 8, kRun8 = 4;
 
 template <class T> using gptr = __attribute__((address_space(1))) T*;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int64_t next_chunk(int64_t c, int& j, int run, int64_t groups) {
     if (++j < run) return c + kWaves;
@@ -40,21 +46,35 @@ __device__ __forceinline__ int64_t next_chunk(int64_t c, int& j, int run, int64_
     return c + (groups * run - (run - 1)) * kWaves;
 }
 
-// One chunk of the byte mix: 512 elements, lane l on elements 8l .. 8l+7.
+// A lane's codes of one moment: 8 nibbles (4-bit codes) or 8 bytes.
+template <int BITS> struct LaneCodes;
+template <> struct LaneCodes<4> {
+    typedef uint32_t T;
+    __device__ static T mix(T c, const u32x4& q, int w) { return c ^ (w ? q.z : q.y); }
+};
+template <> struct LaneCodes<8> {
+    typedef u32x2 T;
+    __device__ static T mix(T c, const u32x4& q, int w) { return c ^ (w ? q.zw : q.xy); }
+};
+
+// One chunk of the byte mix: 512 elements, lane l on elements 8l .. 8l+7,
+// BITS-bit codes.
+template <int BITS>
 __device__ __forceinline__ void mix_chunk(float* __restrict__ param, const uint16_t* __restrict__ grad,
                                           uint8_t* __restrict__ mcodes, uint8_t* __restrict__ vcodes,
                                           float* __restrict__ mscales, float* __restrict__ vscales, int64_t c,
                                           int lane, float a) {
+    typedef typename LaneCodes<BITS>::T CodeT;
     const int64_t c0 = c * kChunk;
     const gptr<float> p = (gptr<float>)param + c0 + lane * 8;
     const gptr<const uint16_t> g = (gptr<const uint16_t>)grad + c0 + lane * 8;
-    const gptr<uint32_t> mc = (gptr<uint32_t>)(mcodes + (c0 >> 1)) + lane;
-    const gptr<uint32_t> vc = (gptr<uint32_t>)(vcodes + (c0 >> 1)) + lane;
+    const gptr<CodeT> mc = (gptr<CodeT>)(mcodes + c0 * BITS / 8) + lane;
+    const gptr<CodeT> vc = (gptr<CodeT>)(vcodes + c0 * BITS / 8) + lane;
     const int64_t blk = c * 4 + (lane >> 4);
     f32x4 x = *reinterpret_cast<const gptr<const f32x4>>(p);
     f32x4 y = *reinterpret_cast<const gptr<const f32x4>>(p + 4);
     const u32x4 q = *reinterpret_cast<const gptr<const u32x4>>(g);
-    const uint32_t m = *mc, v = *vc;
+    const CodeT m = *mc, v = *vc;
     const float sm = ((gptr<float>)mscales)[blk], sv = ((gptr<float>)vscales)[blk];
     // trivial, data-dependent arithmetic: nothing can be elided
     const float gq = __uint_as_float(q.x << 16) + __uint_as_float(q.w & 0xFFFF0000u);
@@ -62,14 +82,15 @@ __device__ __forceinline__ void mix_chunk(float* __restrict__ param, const uint1
     y = y * a + gq;
     *reinterpret_cast<gptr<f32x4>>(p) = x;
     *reinterpret_cast<gptr<f32x4>>(p + 4) = y;
-    *mc = m ^ q.y;
-    *vc = v ^ q.z;
+    *mc = LaneCodes<BITS>::mix(m, q, 0);
+    *vc = LaneCodes<BITS>::mix(v, q, 1);
     if ((lane & 15) == 0) {
         ((gptr<float>)mscales)[blk] = sm * a;
         ((gptr<float>)vscales)[blk] = sv * a;
     }
 }
 
+template <int BITS>
 __global__ __launch_bounds__(256) void k_byte_mix(float* __restrict__ param, const uint16_t* __restrict__ grad,
                                                    uint8_t* __restrict__ mcodes, uint8_t* __restrict__ vcodes,
                                                    float* __restrict__ mscales, float* __restrict__ vscales,
@@ -79,7 +100,7 @@ __global__ __launch_bounds__(256) void k_byte_mix(float* __restrict__ param, con
     const int64_t groups = gridDim.x;
     int64_t c = (int64_t)blockIdx.x * run * kWaves + wave;
     for (int j = 0; c < chunks; c = next_chunk(c, j, run, groups))
-        mix_chunk(param, grad, mcodes, vcodes, mscales, vscales, c, lane, a);
+        mix_chunk<BITS>(param, grad, mcodes, vcodes, mscales, vscales, c, lane, a);
 }
 
 // The same chunks taken from a queue: one round of resident work-groups,
@@ -88,6 +109,7 @@ __global__ __launch_bounds__(256) void k_byte_mix(float* __restrict__ param, con
 // and a group that finishes early takes more.  The fastest way found to
 // move this byte mix on gfx950 (5.25 TB/s against 5.07 for the step's own
 // walk; runs of 2 slabs 4.08, of 32 slabs 5.04).
+template <int BITS>
 __global__ __launch_bounds__(256) void k_byte_mix_queue(float* __restrict__ param, const uint16_t* __restrict__ grad,
                                                          uint8_t* __restrict__ mcodes, uint8_t* __restrict__ vcodes,
                                                          float* __restrict__ mscales, float* __restrict__ vscales,
@@ -104,7 +126,7 @@ __global__ __launch_bounds__(256) void k_byte_mix_queue(float* __restrict__ para
         const int64_t r = __builtin_amdgcn_readfirstlane(next);
         if (r >= runs) break;
         for (int64_t c = r * run * kWaves + wave, s = 0; s < run && c < chunks; ++s, c += kWaves)
-            mix_chunk(param, grad, mcodes, vcodes, mscales, vscales, c, lane, a);
+            mix_chunk<BITS>(param, grad, mcodes, vcodes, mscales, vscales, c, lane, a);
     }
 }
 
@@ -180,49 +202,11 @@ int resident_groups(const void* kernel) {
 
 bool a16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-}  // namespace
-
-extern "C" {
-
-int64_t q4probe_byte_mix_bytes(int64_t n) { return n <= 0 ? 0 : 10 * n + 2 * n + (n / 128) * 16; }
-
-int q4probe_byte_mix(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
-                     float* v_scales, int64_t n, void* stream) {
-    if (n <= 0 || n % kChunk != 0) return Q4PROBE_ERR_ARG;
-    if (!param || !grad || !m_codes || !v_codes || !m_scales || !v_scales) return Q4PROBE_ERR_ARG;
-    if (!a16(param) || !a16(grad) || !a16(m_codes) || !a16(v_codes) || !a16(m_scales) || !a16(v_scales))
-        return Q4PROBE_ERR_ARG;
-    const int64_t chunks = n / kChunk;
-    const int64_t slabs = (chunks + kWaves - 1) / kWaves;
-    static std::atomic<int> resident{0};
-    if (resident.load() == 0) resident.store(resident_groups(reinterpret_cast<const void*>(k_byte_mix)));
-    // one work-group per run, as the quantized steps launch (a set with
-    // more than 2^22 runs loops over them)
-    int run = kRun;
-    while (run > 1 && slabs / run < resident.load()) run >>= 1;
-    const int64_t runs = (slabs + run - 1) / run;
-    const int64_t max_groups = int64_t(1) << 22;
-    const int grid = (int)(runs < max_groups ? runs : max_groups);
-    k_byte_mix<<<grid, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(param, grad, m_codes, v_codes, m_scales,
-                                                                       v_scales, chunks, run, 0.999f);
-    return hipGetLastError() == hipSuccess ? Q4PROBE_OK : Q4PROBE_ERR_HIP;
-}
-
-// Work-groups of the wave-contiguous probes: 2x the resident groups (4096
-// on gfx950, as fast as 8192 and faster than 2048 or 16384), never more than
-// one segment per wavefront.
-static unsigned segment_grid(int64_t n16, const void* kernel, std::atomic<int>& resident) {
-    if (resident.load() == 0) resident.store(resident_groups(kernel));
-    const int64_t need = (n16 / kSegVec + 3) / 4 + 1;
-    const int64_t cap = 2 * (int64_t)resident.load();
-    return (unsigned)(need < cap ? need : cap);
-}
-
 // The queue counter of k_byte_mix_queue: a device word of this library, its
 // address looked up once per device.
-static __device__ unsigned int queue_word;
+__device__ unsigned int queue_word;
 
-static hipError_t queue_address(unsigned int** ptr) {
+hipError_t queue_address(unsigned int** ptr) {
     static std::mutex mu;
     static unsigned int* addr[64] = {};
     int dev = 0;
@@ -240,28 +224,94 @@ static hipError_t queue_address(unsigned int** ptr) {
     return hipSuccess;
 }
 
-int q4probe_byte_mix_queue(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
-                           float* v_scales, int64_t n, void* stream) {
-    if (n <= 0 || n % kChunk != 0) return Q4PROBE_ERR_ARG;
-    if (!param || !grad || !m_codes || !v_codes || !m_scales || !v_scales) return Q4PROBE_ERR_ARG;
-    if (!a16(param) || !a16(grad) || !a16(m_codes) || !a16(v_codes) || !a16(m_scales) || !a16(v_scales))
-        return Q4PROBE_ERR_ARG;
+bool mix_args_ok(const float* param, const uint16_t* grad, const uint8_t* m_codes, const uint8_t* v_codes,
+                 const float* m_scales, const float* v_scales, int64_t n) {
+    if (n <= 0 || n % kChunk != 0) return false;
+    if (!param || !grad || !m_codes || !v_codes || !m_scales || !v_scales) return false;
+    return a16(param) && a16(grad) && a16(m_codes) && a16(v_codes) && a16(m_scales) && a16(v_scales);
+}
+
+// One work-group per run of `max_run` slabs, as the quantized steps launch
+// (runs halved while the set has fewer than one per resident group; a set
+// with more than 2^22 runs loops over them).
+template <int BITS>
+int launch_mix(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
+               float* v_scales, int64_t n, int max_run, void* stream) {
+    if (!mix_args_ok(param, grad, m_codes, v_codes, m_scales, v_scales, n)) return Q4PROBE_ERR_ARG;
+    const int64_t chunks = n / kChunk;
+    const int64_t slabs = (chunks + kWaves - 1) / kWaves;
+    static std::atomic<int> resident{0};
+    if (resident.load() == 0) resident.store(resident_groups(reinterpret_cast<const void*>(k_byte_mix<BITS>)));
+    int run = max_run;
+    while (run > 1 && slabs / run < resident.load()) run >>= 1;
+    const int64_t runs = (slabs + run - 1) / run;
+    const int64_t max_groups = int64_t(1) << 22;
+    const int grid = (int)(runs < max_groups ? runs : max_groups);
+    k_byte_mix<BITS><<<grid, 256, 0, reinterpret_cast<hipStream_t>(stream)>>>(param, grad, m_codes, v_codes,
+                                                                             m_scales, v_scales, chunks, run, 0.999f);
+    return hipGetLastError() == hipSuccess ? Q4PROBE_OK : Q4PROBE_ERR_HIP;
+}
+
+// One round of resident work-groups taking runs of `max_run` slabs from the
+// queue word, zeroed before the launch.
+template <int BITS>
+int launch_mix_queue(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
+                     float* v_scales, int64_t n, int max_run, void* stream) {
+    if (!mix_args_ok(param, grad, m_codes, v_codes, m_scales, v_scales, n)) return Q4PROBE_ERR_ARG;
     unsigned int* queue = nullptr;
     if (queue_address(&queue) != hipSuccess) return Q4PROBE_ERR_HIP;
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const int64_t chunks = n / kChunk;
     const int64_t slabs = (chunks + kWaves - 1) / kWaves;
     static std::atomic<int> resident{0};
-    if (resident.load() == 0) resident.store(resident_groups(reinterpret_cast<const void*>(k_byte_mix_queue)));
+    if (resident.load() == 0)
+        resident.store(resident_groups(reinterpret_cast<const void*>(k_byte_mix_queue<BITS>)));
     const int64_t groups = resident.load();
-    int run = kRun;
+    int run = max_run;
     while (run > 1 && slabs / run < groups) run >>= 1;
     const int64_t runs = (slabs + run - 1) / run;
     if (hipMemsetAsync(queue, 0, sizeof(unsigned int), st) != hipSuccess) return Q4PROBE_ERR_HIP;
-    k_byte_mix_queue<<<(unsigned)(runs < groups ? runs : groups), 256, 0, st>>>(param, grad, m_codes, v_codes,
-                                                                               m_scales, v_scales, chunks, run, queue,
-                                                                               0.999f);
+    k_byte_mix_queue<BITS><<<(unsigned)(runs < groups ? runs : groups), 256, 0, st>>>(
+        param, grad, m_codes, v_codes, m_scales, v_scales, chunks, run, queue, 0.999f);
     return hipGetLastError() == hipSuccess ? Q4PROBE_OK : Q4PROBE_ERR_HIP;
+}
+
+// Work-groups of the wave-contiguous probes: 2x the resident groups (4096
+// on gfx950, as fast as 8192 and faster than 2048 or 16384), never more than
+// one segment per wavefront.
+unsigned segment_grid(int64_t n16, const void* kernel, std::atomic<int>& resident) {
+    if (resident.load() == 0) resident.store(resident_groups(kernel));
+    const int64_t need = (n16 / kSegVec + 3) / 4 + 1;
+    const int64_t cap = 2 * (int64_t)resident.load();
+    return (unsigned)(need < cap ? need : cap);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t q4probe_byte_mix_bytes(int64_t n) { return n <= 0 ? 0 : 10 * n + 2 * n + (n / 128) * 16; }
+
+int q4probe_byte_mix(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
+                     float* v_scales, int64_t n, void* stream) {
+    return launch_mix<4>(param, grad, m_codes, v_codes, m_scales, v_scales, n, kRun, stream);
+}
+
+int q4probe_byte_mix_queue(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
+                           float* v_scales, int64_t n, void* stream) {
+    return launch_mix_queue<4>(param, grad, m_codes, v_codes, m_scales, v_scales, n, kRun, stream);
+}
+
+int64_t q4probe_byte_mix8_bytes(int64_t n) { return n <= 0 ? 0 : 10 * n + 4 * n + (n / 128) * 16; }
+
+int q4probe_byte_mix8(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
+                      float* v_scales, int64_t n, void* stream) {
+    return launch_mix<8>(param, grad, m_codes, v_codes, m_scales, v_scales, n, kRun8, stream);
+}
+
+int q4probe_byte_mix8_queue(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
+                            float* v_scales, int64_t n, void* stream) {
+    return launch_mix_queue<8>(param, grad, m_codes, v_codes, m_scales, v_scales, n, kRun8, stream);
 }
 
 int q4probe_copy(void* dst, const void* src, size_t bytes, void* stream) {

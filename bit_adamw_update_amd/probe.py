@@ -27,6 +27,12 @@ def load_library():
         L.q4probe_copy.restype = C.c_int
         L.q4probe_byte_mix_queue.argtypes = L.q4probe_byte_mix.argtypes
         L.q4probe_byte_mix_queue.restype = C.c_int
+        L.q4probe_byte_mix8_bytes.argtypes = [i64]
+        L.q4probe_byte_mix8_bytes.restype = i64
+        L.q4probe_byte_mix8.argtypes = L.q4probe_byte_mix.argtypes
+        L.q4probe_byte_mix8.restype = C.c_int
+        L.q4probe_byte_mix8_queue.argtypes = L.q4probe_byte_mix.argtypes
+        L.q4probe_byte_mix8_queue.restype = C.c_int
         L.q4probe_update_in_place.argtypes = [vp, C.c_size_t, vp]
         L.q4probe_update_in_place.restype = C.c_int
         L.q4probe_read_sink_words.argtypes = []
@@ -48,22 +54,26 @@ def _ok(rc: int, what: str) -> None:
         raise RuntimeError(f"{what} failed with status {rc}")
 
 
-def byte_mix_bytes(n: int) -> int:
-    return int(load_library().q4probe_byte_mix_bytes(n))
+def byte_mix_bytes(n: int, bits: int = 4) -> int:
+    L = load_library()
+    return int(L.q4probe_byte_mix_bytes(n) if bits == 4 else L.q4probe_byte_mix8_bytes(n))
 
 
 class ByteMix:
-    """Buffers of the step's byte mix for n elements (n a multiple of 512),
-    filled with non-zero data."""
+    """Buffers of a step's byte mix for n elements (n a multiple of 512),
+    filled with non-zero data: the 4-bit steps' (bits=4) or the 8-bit
+    step's (bits=8)."""
 
-    def __init__(self, n: int, device="cuda"):
-        assert n > 0 and n % 512 == 0
+    def __init__(self, n: int, device="cuda", bits: int = 4):
+        assert n > 0 and n % 512 == 0 and bits in (4, 8)
         self.n = n
+        self.bits = bits
         g = torch.Generator(device=device).manual_seed(7)
         self.param = torch.randn(n, generator=g, device=device) * 0.02
         self.grad = (torch.randn(n, generator=g, device=device) * 1e-3).to(torch.bfloat16)
-        self.m_codes = torch.randint(0, 256, (n // 2,), generator=g, device=device, dtype=torch.uint8)
-        self.v_codes = torch.randint(0, 256, (n // 2,), generator=g, device=device, dtype=torch.uint8)
+        ncode = n * bits // 8
+        self.m_codes = torch.randint(0, 256, (ncode,), generator=g, device=device, dtype=torch.uint8)
+        self.v_codes = torch.randint(0, 256, (ncode,), generator=g, device=device, dtype=torch.uint8)
         self.m_scales = torch.rand(n // 128, generator=g, device=device) + 0.5
         self.v_scales = torch.rand(n // 128, generator=g, device=device) + 0.5
 
@@ -71,13 +81,18 @@ class ByteMix:
         return (self.param.data_ptr(), self.grad.data_ptr(), self.m_codes.data_ptr(), self.v_codes.data_ptr(),
                 self.m_scales.data_ptr(), self.v_scales.data_ptr(), self.n, _stream(stream))
 
+    def bytes(self) -> int:
+        return byte_mix_bytes(self.n, self.bits)
+
     def run(self, stream=None) -> None:
         """The step's own lane layout and work-group walk."""
-        _ok(load_library().q4probe_byte_mix(*self._args(stream)), "q4probe_byte_mix")
+        name = "q4probe_byte_mix" if self.bits == 4 else "q4probe_byte_mix8"
+        _ok(getattr(load_library(), name)(*self._args(stream)), name)
 
     def run_queue(self, stream=None) -> None:
-        """The same bytes taken from a queue of runs (the fastest form)."""
-        _ok(load_library().q4probe_byte_mix_queue(*self._args(stream)), "q4probe_byte_mix_queue")
+        """The same bytes taken from a queue of runs."""
+        name = "q4probe_byte_mix_queue" if self.bits == 4 else "q4probe_byte_mix8_queue"
+        _ok(getattr(load_library(), name)(*self._args(stream)), name)
 
 
 def copy(dst: torch.Tensor, src: torch.Tensor, stream=None) -> None:

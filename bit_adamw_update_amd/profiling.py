@@ -201,6 +201,9 @@ def summarize(workload: str, recipe: str, out: str, steps: int, warmup: int, des
         if bm:
             v = dur[bm[0]]
             lines.append(f"{label}: {sum(v[-steps:]) / len(v[-steps:]) / 1e6:.4f}")
+    if _pick(dur, BYTE_MIX_KERNEL) or _pick(dur, BYTE_MIX_QUEUE_KERNEL):
+        # bench.py probes the 8-bit step's own byte mix, the 4-bit one otherwise
+        lines.append(f"byte_mix_probe_code_bits: {8 if recipe == 'block8' else 4}")
     prefix = f"accumulate_{workload}_{recipe}" if STEP_BEFORE else f"{kern}_{workload}_{recipe}"
     trace_file = os.path.join(dest, f"{prefix}_trace.txt")
     os.makedirs(dest, exist_ok=True)

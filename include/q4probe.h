@@ -50,6 +50,23 @@ int q4probe_byte_mix(float* param, const uint16_t* grad, uint8_t* m_codes, uint8
 int q4probe_byte_mix_queue(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
                            float* v_scales, int64_t n, void* stream);
 
+/* Bytes one q4probe_byte_mix8 call moves for n elements: 14.125 n. */
+int64_t q4probe_byte_mix8_bytes(int64_t n);
+
+/* The byte mix of the 8-bit blockwise step (AReno docs "4-bit AdamW",
+ * section "Requirements and errors", names the 8-bit blockwise AdamW; one
+ * byte per code and 128-element blocks here): as
+ * q4probe_byte_mix, with m_codes and v_codes holding n bytes each, read and
+ * rewritten 8 bytes per lane, and the work-groups taking runs of 4 slabs as
+ * the 8-bit step does. */
+int q4probe_byte_mix8(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
+                      float* v_scales, int64_t n, void* stream);
+
+/* The 8-bit byte mix taken from the queue, as q4probe_byte_mix_queue (the
+ * same device word: calls that overlap on one device race on it). */
+int q4probe_byte_mix8_queue(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes,
+                            float* m_scales, float* v_scales, int64_t n, void* stream);
+
 /* dst <- src, `bytes` (a positive multiple of 16) read and written once. */
 int q4probe_copy(void* dst, const void* src, size_t bytes, void* stream);
 

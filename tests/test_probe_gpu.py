@@ -1,5 +1,6 @@
 """The bandwidth probes (libq4probe.so) do the memory work they claim: the
-byte-mix probe, in both its walks, reads and rewrites every byte of its mix (masters, codes and
+byte-mix probes (4-bit and 8-bit codes), in both their walks, read and
+rewrite every byte of their mix (masters, codes and
 scales changed as its arithmetic says, nothing outside touched), the copy
 copies, the in-place update rewrites every element and the read probe reads
 everything."""
@@ -17,14 +18,15 @@ pytestmark = pytest.mark.gpu
 # again, and a ragged last run
 @pytest.mark.parametrize("n", [512 * 37, 512 * (4 * 8 * 3000 + 5)], ids=["small", "queue_laps"])
 @pytest.mark.parametrize("form", ["step_walk", "queue"])
-def test_byte_mix_touches_exactly_its_bytes(form, n):
-    bm = probe.ByteMix(n)
+@pytest.mark.parametrize("bits", [4, 8])
+def test_byte_mix_touches_exactly_its_bytes(bits, form, n):
+    bm = probe.ByteMix(n, bits=bits)
     before = {f: getattr(bm, f).clone() for f in ("param", "grad", "m_codes", "v_codes", "m_scales", "v_scales")}
     guard = torch.full((4096,), 7, dtype=torch.uint8, device="cuda")
-    print("byte mix probe", form, n, flush=True)
+    print("byte mix probe", bits, form, n, flush=True)
     bm.run() if form == "step_walk" else bm.run_queue()
     torch.cuda.synchronize()
-    assert probe.byte_mix_bytes(n) == 12 * n + n // 8
+    assert bm.bytes() == 12 * n + n // 8 + (2 * n if bits == 8 else 0)
     a = np.float32(0.999)
     p0 = before["param"].cpu().numpy()
     q = before["grad"].view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32).reshape(-1, 8)
@@ -32,10 +34,14 @@ def test_byte_mix_touches_exactly_its_bytes(form, n):
     gq = ((q[:, 0] << 16).view(np.float32) + ((q[:, 7] << 16) & 0xFFFF0000).view(np.float32)).astype(np.float32)
     expect = (p0.reshape(-1, 8) * a + gq[:, None]).reshape(-1)
     assert np.array_equal(bm.param.cpu().numpy().view(np.uint32), expect.view(np.uint32))
-    for codes, word in (("m_codes", 1), ("v_codes", 2)):
-        c0 = before[codes].cpu().numpy().view(np.uint32)
-        g32 = before["grad"].view(torch.int16).cpu().numpy().view(np.uint32).reshape(-1, 4)[:, word]
-        assert np.array_equal(getattr(bm, codes).cpu().numpy().view(np.uint32), c0 ^ g32)
+    # lane l's 4-bit codes (one word) take its gradient word 1 (m) or 2 (v);
+    # its 8-bit codes (two words) take words 0-1 (m) or 2-3 (v)
+    words = {4: ((1,), (2,)), 8: ((0, 1), (2, 3))}[bits]
+    g32 = before["grad"].view(torch.int16).cpu().numpy().view(np.uint32).reshape(-1, 4)
+    for codes, w in zip(("m_codes", "v_codes"), words):
+        c0 = before[codes].cpu().numpy().view(np.uint32).reshape(-1, len(w))
+        got = getattr(bm, codes).cpu().numpy().view(np.uint32).reshape(-1, len(w))
+        assert np.array_equal(got, c0 ^ g32[:, list(w)])
     for sc in ("m_scales", "v_scales"):
         assert np.array_equal(getattr(bm, sc).cpu().numpy(), before[sc].cpu().numpy() * a)
     assert torch.equal(bm.grad.view(torch.int16), before["grad"].view(torch.int16))
