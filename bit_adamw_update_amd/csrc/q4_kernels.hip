@@ -659,16 +659,18 @@ __device__ __forceinline__ void fp32_adamw(const StepScalars& sc, float g, float
     v = vv;
 }
 
-// K1's lane layout (8 consecutive elements per lane, 16-byte accesses;
-// scalar accesses only in a tensor's last partial lane) over the plain chunk
-// prefix, grid-stride.  Per-element loads (lanes 32 bytes apart in every
+// K1's lane layout (lane s of row r on elements 128r + 4s .. +3 and
+// 128r + 64 + 4s .. +3 of the chunk, 16-byte accesses; scalar accesses only
+// in a tensor's last partial lane) over the plain chunk prefix, in runs of
+// slabs.  Every stream is read once and written once, all of them
+// nontemporal.  Per-element loads (lanes 32 bytes apart in every
 // instruction) ran the GPT-162M set at 1.9 TB/s.
 __global__ __launch_bounds__(256) void k_fp32_step(const DevTensor* __restrict__ tab,
                                                     const int64_t* __restrict__ chunk_begin, int n_tensors,
                                                     int64_t total_chunks, int run_slabs, StepScalars sc) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int le = lane * 8;
+    const int le = (lane & 48) * 8 + (lane & 15) * 4;
     const float gs = (sc.flags & SF_CLIP) ? *clip_of_table(tab) : 1.0f;
     const int64_t ngroups = gridDim.x;
     int64_t c = (int64_t)blockIdx.x * run_slabs * kWavesPerGroup + wave;
@@ -681,39 +683,41 @@ __global__ __launch_bounds__(256) void k_fp32_step(const DevTensor* __restrict__
         const gptr<float> M = G(T.m32) + c0;
         const gptr<float> V = G(T.v32) + c0;
         const gptr<const uint16_t> Gr = G(T.grad) + c0;
-        if (c0 + le + 8 <= T.numel) {
+        if (c0 + le + 68 <= T.numel) {
             float p[8], m[8], v[8], g[8];
-            const f32x4 pa = *reinterpret_cast<const gptr<const f32x4>>(P + le);
-            const f32x4 pb = *reinterpret_cast<const gptr<const f32x4>>(P + le + 4);
-            const f32x4 ma = *reinterpret_cast<const gptr<const f32x4>>(M + le);
-            const f32x4 mb = *reinterpret_cast<const gptr<const f32x4>>(M + le + 4);
-            const f32x4 va = *reinterpret_cast<const gptr<const f32x4>>(V + le);
-            const f32x4 vb = *reinterpret_cast<const gptr<const f32x4>>(V + le + 4);
-            const u32x4 gq = *reinterpret_cast<const gptr<const u32x4>>(Gr + le);
+            const f32x4 pa = __builtin_nontemporal_load(reinterpret_cast<const gptr<const f32x4>>(P + le));
+            const f32x4 pb = __builtin_nontemporal_load(reinterpret_cast<const gptr<const f32x4>>(P + le + 64));
+            const f32x4 ma = __builtin_nontemporal_load(reinterpret_cast<const gptr<const f32x4>>(M + le));
+            const f32x4 mb = __builtin_nontemporal_load(reinterpret_cast<const gptr<const f32x4>>(M + le + 64));
+            const f32x4 va = __builtin_nontemporal_load(reinterpret_cast<const gptr<const f32x4>>(V + le));
+            const f32x4 vb = __builtin_nontemporal_load(reinterpret_cast<const gptr<const f32x4>>(V + le + 64));
+            const u32x2 ga = __builtin_nontemporal_load(reinterpret_cast<const gptr<const u32x2>>(Gr + le));
+            const u32x2 gb = __builtin_nontemporal_load(reinterpret_cast<const gptr<const u32x2>>(Gr + le + 64));
             p[0] = pa.x; p[1] = pa.y; p[2] = pa.z; p[3] = pa.w; p[4] = pb.x; p[5] = pb.y; p[6] = pb.z; p[7] = pb.w;
             m[0] = ma.x; m[1] = ma.y; m[2] = ma.z; m[3] = ma.w; m[4] = mb.x; m[5] = mb.y; m[6] = mb.z; m[7] = mb.w;
             v[0] = va.x; v[1] = va.y; v[2] = va.z; v[3] = va.w; v[4] = vb.x; v[5] = vb.y; v[6] = vb.z; v[7] = vb.w;
-            const uint32_t gw[4] = {gq.x, gq.y, gq.z, gq.w};
+            const uint32_t gw[4] = {ga.x, ga.y, gb.x, gb.y};
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 g[k] = bf16_to_f32((k & 1) ? gw[k >> 1] >> 16 : gw[k >> 1] & 0xFFFFu) * gs;
                 fp32_adamw(sc, g[k], p[k], m[k], v[k]);
             }
-            *reinterpret_cast<gptr<f32x4>>(P + le) = f32x4{p[0], p[1], p[2], p[3]};
-            *reinterpret_cast<gptr<f32x4>>(P + le + 4) = f32x4{p[4], p[5], p[6], p[7]};
-            *reinterpret_cast<gptr<f32x4>>(M + le) = f32x4{m[0], m[1], m[2], m[3]};
-            *reinterpret_cast<gptr<f32x4>>(M + le + 4) = f32x4{m[4], m[5], m[6], m[7]};
-            *reinterpret_cast<gptr<f32x4>>(V + le) = f32x4{v[0], v[1], v[2], v[3]};
-            *reinterpret_cast<gptr<f32x4>>(V + le + 4) = f32x4{v[4], v[5], v[6], v[7]};
+            __builtin_nontemporal_store(f32x4{p[0], p[1], p[2], p[3]}, reinterpret_cast<gptr<f32x4>>(P + le));
+            __builtin_nontemporal_store(f32x4{p[4], p[5], p[6], p[7]}, reinterpret_cast<gptr<f32x4>>(P + le + 64));
+            __builtin_nontemporal_store(f32x4{m[0], m[1], m[2], m[3]}, reinterpret_cast<gptr<f32x4>>(M + le));
+            __builtin_nontemporal_store(f32x4{m[4], m[5], m[6], m[7]}, reinterpret_cast<gptr<f32x4>>(M + le + 64));
+            __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<gptr<f32x4>>(V + le));
+            __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<gptr<f32x4>>(V + le + 64));
         } else {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                if (c0 + le + k < T.numel) {
-                    float p = P[le + k], m = M[le + k], v = V[le + k];
-                    fp32_adamw(sc, bf16_to_f32(Gr[le + k]) * gs, p, m, v);
-                    P[le + k] = p;
-                    M[le + k] = m;
-                    V[le + k] = v;
+                const int o = le + (k < 4 ? k : 60 + k);
+                if (c0 + o < T.numel) {
+                    float p = P[o], m = M[o], v = V[o];
+                    fp32_adamw(sc, bf16_to_f32(Gr[o]) * gs, p, m, v);
+                    P[o] = p;
+                    M[o] = m;
+                    V[o] = v;
                 }
             }
         }
@@ -724,9 +728,10 @@ __global__ __launch_bounds__(256) void k_fp32_step(const DevTensor* __restrict__
 // K1 of the 8-bit recipe: SDyn8 m, Dyn8 v, one byte per code
 // ---------------------------------------------------------------------------
 //
-// Same lane layout as K1 (8 consecutive elements per lane, a 128-block per
-// 16-lane row).  A code is one byte, so a lane's 8 codes of a moment are one
-// 8-byte access.  256-entry maps do not fit ds_bpermute's 64 lanes: decoding
+// Same lane layout as K1 (a 128-block per 16-lane row, lane s on its
+// elements 4s .. 4s+3 and 64+4s .. 64+4s+3; masters and gradients
+// nontemporal).  A code is one byte, so a lane's 8 codes of a moment are two
+// 4-byte accesses.  256-entry maps do not fit ds_bpermute's 64 lanes: decoding
 // reads a code-indexed table in LDS, and the nearest level comes from the
 // bucket tables of q4_quant.h (Step8Lds, rtn8_m, rtn8_v).
 
@@ -736,14 +741,17 @@ __device__ __forceinline__ void step8_chunk(const DevTensor& T, const int64_t lc
     const int sub = lane & 15;
     const int64_t n = T.numel;
     const int64_t blk = lc * kBlocksPerChunk + (lane >> 4);
-    const int64_t e0 = blk * kBlock + sub * 8;
-    int nv = 8;
+    const int64_t e0 = blk * kBlock + sub * 4;
+    int nva = 4, nvb = 4;  // valid elements of the lane's two halves
     bool blk_ok = true;
     if (!FULL) {
-        const int64_t rem = n - e0;
-        nv = rem >= 8 ? 8 : (rem > 0 ? (int)rem : 0);
+        const int64_t ra = n - e0, rb2 = n - (e0 + 64);
+        nva = ra >= 4 ? 4 : (ra > 0 ? (int)ra : 0);
+        nvb = rb2 >= 4 ? 4 : (rb2 > 0 ? (int)rb2 : 0);
         blk_ok = blk * kBlock < n;
     }
+    const bool lane_full = FULL || nvb == 4;
+    auto valid = [&](int k) { return FULL || (k < 4 ? k < nva : k - 4 < nvb); };
     const gptr<float> param = G(T.param);
     const gptr<const uint16_t> grad = G(T.grad);
     const gptr<uint8_t> mcodes = G(T.m_codes);
@@ -755,26 +763,29 @@ __device__ __forceinline__ void step8_chunk(const DevTensor& T, const int64_t lc
     __builtin_amdgcn_s_setprio(2);
     float p[8], g[8];
     uint32_t mc[2] = {0u, 0u}, vc[2] = {0u, 0u};
-    if (FULL || nv == 8) {
-        const f32x4 a = *reinterpret_cast<const gptr<const f32x4>>(param + e0);
-        const f32x4 b = *reinterpret_cast<const gptr<const f32x4>>(param + e0 + 4);
+    if (lane_full) {
+        const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const gptr<const f32x4>>(param + e0));
+        const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const gptr<const f32x4>>(param + e0 + 64));
         p[0] = a.x; p[1] = a.y; p[2] = a.z; p[3] = a.w; p[4] = b.x; p[5] = b.y; p[6] = b.z; p[7] = b.w;
-        const u32x4 gq = *reinterpret_cast<const gptr<const u32x4>>(grad + e0);
-        g[0] = bf16_to_f32(gq.x & 0xFFFFu); g[1] = bf16_to_f32(gq.x >> 16);
-        g[2] = bf16_to_f32(gq.y & 0xFFFFu); g[3] = bf16_to_f32(gq.y >> 16);
-        g[4] = bf16_to_f32(gq.z & 0xFFFFu); g[5] = bf16_to_f32(gq.z >> 16);
-        g[6] = bf16_to_f32(gq.w & 0xFFFFu); g[7] = bf16_to_f32(gq.w >> 16);
-        const u32x2 m8 = *reinterpret_cast<const gptr<const u32x2>>(mcodes + e0);
-        const u32x2 v8 = *reinterpret_cast<const gptr<const u32x2>>(vcodes + e0);
-        mc[0] = m8.x; mc[1] = m8.y; vc[0] = v8.x; vc[1] = v8.y;
+        const u32x2 ga = __builtin_nontemporal_load(reinterpret_cast<const gptr<const u32x2>>(grad + e0));
+        const u32x2 gb = __builtin_nontemporal_load(reinterpret_cast<const gptr<const u32x2>>(grad + e0 + 64));
+        g[0] = bf16_to_f32(ga.x & 0xFFFFu); g[1] = bf16_to_f32(ga.x >> 16);
+        g[2] = bf16_to_f32(ga.y & 0xFFFFu); g[3] = bf16_to_f32(ga.y >> 16);
+        g[4] = bf16_to_f32(gb.x & 0xFFFFu); g[5] = bf16_to_f32(gb.x >> 16);
+        g[6] = bf16_to_f32(gb.y & 0xFFFFu); g[7] = bf16_to_f32(gb.y >> 16);
+        mc[0] = *reinterpret_cast<const gptr<const uint32_t>>(mcodes + e0);
+        mc[1] = *reinterpret_cast<const gptr<const uint32_t>>(mcodes + e0 + 64);
+        vc[0] = *reinterpret_cast<const gptr<const uint32_t>>(vcodes + e0);
+        vc[1] = *reinterpret_cast<const gptr<const uint32_t>>(vcodes + e0 + 64);
     } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            p[k] = k < nv ? param[e0 + k] : 0.0f;
-            g[k] = k < nv ? bf16_to_f32(grad[e0 + k]) : 0.0f;
-            if (k < nv) {
-                mc[k >> 2] |= (uint32_t)mcodes[e0 + k] << (8 * (k & 3));
-                vc[k >> 2] |= (uint32_t)vcodes[e0 + k] << (8 * (k & 3));
+            const int64_t o = e0 + (k < 4 ? k : 60 + k);
+            p[k] = valid(k) ? param[o] : 0.0f;
+            g[k] = valid(k) ? bf16_to_f32(grad[o]) : 0.0f;
+            if (valid(k)) {
+                mc[k >> 2] |= (uint32_t)mcodes[o] << (8 * (k & 3));
+                vc[k >> 2] |= (uint32_t)vcodes[o] << (8 * (k & 3));
             }
         }
     }
@@ -797,18 +808,18 @@ __device__ __forceinline__ void step8_chunk(const DevTensor& T, const int64_t lc
         v1[k] = __builtin_fmaf(sc.beta2, v0, sc.omb2 * (g[k] * g[k]));
         const float denom = __builtin_fmaf(__builtin_amdgcn_sqrtf(v1[k]), sc.rsbc2, sc.eps);
         p[k] = __builtin_fmaf(-sc.step_size, m1[k] * __builtin_amdgcn_rcpf(denom), p[k] * sc.decay);
-        if (!FULL && k >= nv) {
+        if (!valid(k)) {
             m1[k] = 0.0f;
             v1[k] = 0.0f;
         }
     }
-    if (FULL || nv == 8) {
-        *reinterpret_cast<gptr<f32x4>>(param + e0) = f32x4{p[0], p[1], p[2], p[3]};
-        *reinterpret_cast<gptr<f32x4>>(param + e0 + 4) = f32x4{p[4], p[5], p[6], p[7]};
+    if (lane_full) {
+        __builtin_nontemporal_store(f32x4{p[0], p[1], p[2], p[3]}, reinterpret_cast<gptr<f32x4>>(param + e0));
+        __builtin_nontemporal_store(f32x4{p[4], p[5], p[6], p[7]}, reinterpret_cast<gptr<f32x4>>(param + e0 + 64));
     } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-            if (k < nv) param[e0 + k] = p[k];
+            if (valid(k)) param[e0 + (k < 4 ? k : 60 + k)] = p[k];
     }
 
     float am = 0.0f, av = 0.0f;
@@ -828,15 +839,18 @@ __device__ __forceinline__ void step8_chunk(const DevTensor& T, const int64_t lc
         mw[k >> 2] |= rtn8_m(lds, xm) << (8 * (k & 3));
         vw[k >> 2] |= rtn8_v(lds, xv) << (8 * (k & 3));
     }
-    if (FULL || nv == 8) {
-        *reinterpret_cast<gptr<u32x2>>(mcodes + e0) = u32x2{mw[0], mw[1]};
-        *reinterpret_cast<gptr<u32x2>>(vcodes + e0) = u32x2{vw[0], vw[1]};
+    if (lane_full) {
+        *reinterpret_cast<gptr<uint32_t>>(mcodes + e0) = mw[0];
+        *reinterpret_cast<gptr<uint32_t>>(mcodes + e0 + 64) = mw[1];
+        *reinterpret_cast<gptr<uint32_t>>(vcodes + e0) = vw[0];
+        *reinterpret_cast<gptr<uint32_t>>(vcodes + e0 + 64) = vw[1];
     } else {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            if (k < nv) {
-                mcodes[e0 + k] = (uint8_t)(mw[k >> 2] >> (8 * (k & 3)));
-                vcodes[e0 + k] = (uint8_t)(vw[k >> 2] >> (8 * (k & 3)));
+            if (valid(k)) {
+                const int64_t o = e0 + (k < 4 ? k : 60 + k);
+                mcodes[o] = (uint8_t)(mw[k >> 2] >> (8 * (k & 3)));
+                vcodes[o] = (uint8_t)(vw[k >> 2] >> (8 * (k & 3)));
             }
         }
     }
@@ -1101,13 +1115,16 @@ __global__ __launch_bounds__(256) void k_grad_chunks(const DevTensor* __restrict
         uint32_t w[4] = {0u, 0u, 0u, 0u};
         if (nv == 8) {
             u32x4 q = u32x4{0u, 0u, 0u, 0u}, m = u32x4{0u, 0u, 0u, 0u};
-            if constexpr (MODE != GRAD_FIRST) q = *reinterpret_cast<const gptr<const u32x4>>(gp);
-            if constexpr (MODE != GRAD_STATS_ONLY) m = *reinterpret_cast<const gptr<const u32x4>>(mp);
+            // each instruction covers 1 KiB of whole lines, read and written
+            // once: streaming (nontemporal) accesses
+            if constexpr (MODE != GRAD_FIRST) q = __builtin_nontemporal_load(reinterpret_cast<const gptr<const u32x4>>(gp));
+            if constexpr (MODE != GRAD_STATS_ONLY) m = __builtin_nontemporal_load(reinterpret_cast<const gptr<const u32x4>>(mp));
             w[0] = grad_pair<MODE>(q.x, m.x);
             w[1] = grad_pair<MODE>(q.y, m.y);
             w[2] = grad_pair<MODE>(q.z, m.z);
             w[3] = grad_pair<MODE>(q.w, m.w);
-            if constexpr (MODE != GRAD_STATS_ONLY) *reinterpret_cast<gptr<u32x4>>(gp) = u32x4{w[0], w[1], w[2], w[3]};
+            if constexpr (MODE != GRAD_STATS_ONLY)
+                __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<gptr<u32x4>>(gp));
         } else {
 #pragma unroll
             for (int k = 0; k < 8; ++k) {

@@ -5,22 +5,25 @@
 // k_byte_mix moves exactly the bytes the packed 4-bit step moves per element
 // (FP32 master read and written, BF16 gradient read, two 4-bit code streams
 // read and written, two FP32 block-scale streams read and written: 12.125
-// bytes per element), with the step's lane layout (8 consecutive elements
-// per lane, a 128-element block per 16-lane row, 16-byte accesses for
-// masters and gradients, 4 bytes per moment's codes, the row's scale read by
-// all its lanes and written by one) and its work distribution (one
-// 4-wavefront group per run of consecutive slabs of 4 chunks), but only
-// trivial arithmetic.  Its time is what this byte
-// mix costs on the memory system, whatever the optimizer computes.
+// bytes per element), with the step's lane layout (a 128-element block per
+// 16-lane row, lane s on elements 4s .. 4s+3 and 64+4s .. 64+4s+3 of it, two
+// 16-byte accesses for masters, two 8-byte ones for gradients, two 16-bit
+// ones per moment's codes, the row's scale read by all its lanes and written
+// by one), its cache policy (masters and gradients nontemporal) and its work
+// distribution (one 4-wavefront group per run of consecutive slabs of 4
+// chunks), but only trivial arithmetic.  Its time is what this byte mix
+// costs on the memory system, whatever the optimizer computes.
 //
 // k_byte_mix8 does the same for the 8-bit blockwise step: one code byte per
-// element and moment (8 bytes per lane), 14.125 bytes per element.
+// element and moment (two 4-byte accesses per lane), 14.125 bytes per
+// element.
 //
 // k_copy is a plain copy (known bytes read and written, 16 bytes per lane
 // access), which also calibrates the HBM traffic counters; k_update rewrites
 // a buffer in place, as the step rewrites its masters, codes and scales;
 // k_read reads only.  Each takes the fastest of the forms measured on
-// gfx950, since it stands for what the memory system can do.
+// gfx950, since it stands for what the memory system can do (copy and
+// update stream nontemporal: 2% and 3.5% faster than the default policy).
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -46,19 +49,14 @@ __device__ __forceinline__ int64_t next_chunk(int64_t c, int& j, int run, int64_
     return c + (groups * run - (run - 1)) * kWaves;
 }
 
-// A lane's codes of one moment: 8 nibbles (4-bit codes) or 8 bytes.
+// A lane's codes of one moment in each half of its block: 4 nibbles (4-bit
+// codes) or 4 bytes.
 template <int BITS> struct LaneCodes;
-template <> struct LaneCodes<4> {
-    typedef uint32_t T;
-    __device__ static T mix(T c, const u32x4& q, int w) { return c ^ (w ? q.z : q.y); }
-};
-template <> struct LaneCodes<8> {
-    typedef u32x2 T;
-    __device__ static T mix(T c, const u32x4& q, int w) { return c ^ (w ? q.zw : q.xy); }
-};
+template <> struct LaneCodes<4> { typedef uint16_t T; };
+template <> struct LaneCodes<8> { typedef uint32_t T; };
 
-// One chunk of the byte mix: 512 elements, lane l on elements 8l .. 8l+7,
-// BITS-bit codes.
+// One chunk of the byte mix: 512 elements, lane s of row r on elements
+// 128r + 4s .. +3 and 128r + 64 + 4s .. +3, BITS-bit codes.
 template <int BITS>
 __device__ __forceinline__ void mix_chunk(float* __restrict__ param, const uint16_t* __restrict__ grad,
                                           uint8_t* __restrict__ mcodes, uint8_t* __restrict__ vcodes,
@@ -66,24 +64,29 @@ __device__ __forceinline__ void mix_chunk(float* __restrict__ param, const uint1
                                           int lane, float a) {
     typedef typename LaneCodes<BITS>::T CodeT;
     const int64_t c0 = c * kChunk;
-    const gptr<float> p = (gptr<float>)param + c0 + lane * 8;
-    const gptr<const uint16_t> g = (gptr<const uint16_t>)grad + c0 + lane * 8;
-    const gptr<CodeT> mc = (gptr<CodeT>)(mcodes + c0 * BITS / 8) + lane;
-    const gptr<CodeT> vc = (gptr<CodeT>)(vcodes + c0 * BITS / 8) + lane;
+    const int le = (lane & 48) * 8 + (lane & 15) * 4;
+    const gptr<float> p = (gptr<float>)param + c0 + le;
+    const gptr<const uint16_t> g = (gptr<const uint16_t>)grad + c0 + le;
+    const gptr<CodeT> mc = (gptr<CodeT>)(mcodes + (c0 + le) * BITS / 8);
+    const gptr<CodeT> vc = (gptr<CodeT>)(vcodes + (c0 + le) * BITS / 8);
+    constexpr int kHalf = 64 * BITS / 8 / sizeof(CodeT);  // the second half's codes, in CodeT units
     const int64_t blk = c * 4 + (lane >> 4);
-    f32x4 x = *reinterpret_cast<const gptr<const f32x4>>(p);
-    f32x4 y = *reinterpret_cast<const gptr<const f32x4>>(p + 4);
-    const u32x4 q = *reinterpret_cast<const gptr<const u32x4>>(g);
-    const CodeT m = *mc, v = *vc;
+    f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const gptr<const f32x4>>(p));
+    f32x4 y = __builtin_nontemporal_load(reinterpret_cast<const gptr<const f32x4>>(p + 64));
+    const u32x2 qa = __builtin_nontemporal_load(reinterpret_cast<const gptr<const u32x2>>(g));
+    const u32x2 qb = __builtin_nontemporal_load(reinterpret_cast<const gptr<const u32x2>>(g + 64));
+    const CodeT m0 = mc[0], m1 = mc[kHalf], v0 = vc[0], v1 = vc[kHalf];
     const float sm = ((gptr<float>)mscales)[blk], sv = ((gptr<float>)vscales)[blk];
     // trivial, data-dependent arithmetic: nothing can be elided
-    const float gq = __uint_as_float(q.x << 16) + __uint_as_float(q.w & 0xFFFF0000u);
+    const float gq = __uint_as_float(qa.x << 16) + __uint_as_float(qb.y & 0xFFFF0000u);
     x = x * a + gq;
     y = y * a + gq;
-    *reinterpret_cast<gptr<f32x4>>(p) = x;
-    *reinterpret_cast<gptr<f32x4>>(p + 4) = y;
-    *mc = LaneCodes<BITS>::mix(m, q, 0);
-    *vc = LaneCodes<BITS>::mix(v, q, 1);
+    __builtin_nontemporal_store(x, reinterpret_cast<gptr<f32x4>>(p));
+    __builtin_nontemporal_store(y, reinterpret_cast<gptr<f32x4>>(p + 64));
+    mc[0] = (CodeT)(m0 ^ qa.y);
+    mc[kHalf] = (CodeT)(m1 ^ qa.y);
+    vc[0] = (CodeT)(v0 ^ qb.x);
+    vc[kHalf] = (CodeT)(v1 ^ qb.x);
     if ((lane & 15) == 0) {
         ((gptr<float>)mscales)[blk] = sm * a;
         ((gptr<float>)vscales)[blk] = sv * a;
@@ -149,9 +152,9 @@ __global__ __launch_bounds__(256) void k_copy(u32x4* __restrict__ dst, const u32
         const int64_t b = sg * kSegVec + lane;
         u32x4 v[kSegLoads];
 #pragma unroll
-        for (int u = 0; u < kSegLoads; ++u) v[u] = ((gptr<const u32x4>)src)[b + 64 * u];
+        for (int u = 0; u < kSegLoads; ++u) v[u] = __builtin_nontemporal_load((gptr<const u32x4>)src + b + 64 * u);
 #pragma unroll
-        for (int u = 0; u < kSegLoads; ++u) ((gptr<u32x4>)dst)[b + 64 * u] = v[u];
+        for (int u = 0; u < kSegLoads; ++u) __builtin_nontemporal_store(v[u], (gptr<u32x4>)dst + b + 64 * u);
     }
     for (int64_t i = nseg * kSegVec + wave_id() * 64 + lane; i < n16; i += waves * 64)
         ((gptr<u32x4>)dst)[i] = ((gptr<const u32x4>)src)[i];
@@ -167,9 +170,9 @@ __global__ __launch_bounds__(256) void k_update(f32x4* __restrict__ x, int64_t n
         const int64_t b = sg * kSegVec + lane;
         f32x4 v[kSegLoads];
 #pragma unroll
-        for (int u = 0; u < kSegLoads; ++u) v[u] = ((gptr<const f32x4>)x)[b + 64 * u];
+        for (int u = 0; u < kSegLoads; ++u) v[u] = __builtin_nontemporal_load((gptr<const f32x4>)x + b + 64 * u);
 #pragma unroll
-        for (int u = 0; u < kSegLoads; ++u) ((gptr<f32x4>)x)[b + 64 * u] = v[u] * a;
+        for (int u = 0; u < kSegLoads; ++u) __builtin_nontemporal_store(v[u] * a, (gptr<f32x4>)x + b + 64 * u);
     }
     for (int64_t i = nseg * kSegVec + wave_id() * 64 + lane; i < n16; i += waves * 64)
         ((gptr<f32x4>)x)[i] = ((gptr<const f32x4>)x)[i] * a;

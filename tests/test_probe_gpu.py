@@ -28,20 +28,26 @@ def test_byte_mix_touches_exactly_its_bytes(bits, form, n):
     torch.cuda.synchronize()
     assert bm.bytes() == 12 * n + n // 8 + (2 * n if bits == 8 else 0)
     a = np.float32(0.999)
-    p0 = before["param"].cpu().numpy()
-    q = before["grad"].view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32).reshape(-1, 8)
-    # lane l's gradient term: low half of its first word plus high half of its fourth
-    gq = ((q[:, 0] << 16).view(np.float32) + ((q[:, 7] << 16) & 0xFFFF0000).view(np.float32)).astype(np.float32)
-    expect = (p0.reshape(-1, 8) * a + gq[:, None]).reshape(-1)
+    # element c*512 + 128r + 64h + 4s + e is value e of half h of lane s of
+    # row r in chunk c
+    shape = (-1, 4, 2, 16, 4)
+    p0 = before["param"].cpu().numpy().reshape(shape)
+    g16 = before["grad"].view(torch.int16).cpu().numpy().view(np.uint16).astype(np.uint32).reshape(shape)
+    # the lane's gradient term: its first half's first value plus its
+    # second half's last value
+    gq = ((g16[:, :, 0, :, 0] << 16).view(np.float32) + (g16[:, :, 1, :, 3] << 16).view(np.float32)).astype(np.float32)
+    expect = (p0 * a + gq[:, :, None, :, None]).reshape(-1)
     assert np.array_equal(bm.param.cpu().numpy().view(np.uint32), expect.view(np.uint32))
-    # lane l's 4-bit codes (one word) take its gradient word 1 (m) or 2 (v);
-    # its 8-bit codes (two words) take words 0-1 (m) or 2-3 (v)
-    words = {4: ((1,), (2,)), 8: ((0, 1), (2, 3))}[bits]
-    g32 = before["grad"].view(torch.int16).cpu().numpy().view(np.uint32).reshape(-1, 4)
-    for codes, w in zip(("m_codes", "v_codes"), words):
-        c0 = before[codes].cpu().numpy().view(np.uint32).reshape(-1, len(w))
-        got = getattr(bm, codes).cpu().numpy().view(np.uint32).reshape(-1, len(w))
-        assert np.array_equal(got, c0 ^ g32[:, list(w)])
+    # each half's codes of the lane (16 bits of 4-bit codes, 32 bits of
+    # 8-bit ones) take the first half's second gradient word (m) or the
+    # second half's first (v), cut to the codes' width
+    g32 = before["grad"].view(torch.int16).cpu().numpy().view(np.uint32).reshape(-1, 4, 2, 16, 2)
+    key = {"m_codes": g32[:, :, 0, :, 1], "v_codes": g32[:, :, 1, :, 0]}
+    cdt = {4: np.uint16, 8: np.uint32}[bits]
+    for codes in ("m_codes", "v_codes"):
+        c0 = before[codes].cpu().numpy().view(cdt).reshape(-1, 4, 2, 16)
+        got = getattr(bm, codes).cpu().numpy().view(cdt).reshape(-1, 4, 2, 16)
+        assert np.array_equal(got, c0 ^ key[codes].astype(cdt)[:, :, None, :])
     for sc in ("m_scales", "v_scales"):
         assert np.array_equal(getattr(bm, sc).cpu().numpy(), before[sc].cpu().numpy() * a)
     assert torch.equal(bm.grad.view(torch.int16), before["grad"].view(torch.int16))
