@@ -1009,8 +1009,11 @@ __global__ __launch_bounds__(256) void k_rowcol_partial(const DevMatrix* __restr
             if (r < r1) {
                 const int64_t off = r * M.cols + c0;
                 if (vec) {
-                    if constexpr (MODE != GRAD_FIRST) q[u] = *reinterpret_cast<const gptr<const u32x4>>(grad + off);
-                    if constexpr (MODE != GRAD_STATS_ONLY) mq[u] = *reinterpret_cast<const gptr<const u32x4>>(mic + off);
+                    // 1 KiB of whole lines per instruction: streaming loads
+                    if constexpr (MODE != GRAD_FIRST)
+                        q[u] = __builtin_nontemporal_load(reinterpret_cast<const gptr<const u32x4>>(grad + off));
+                    if constexpr (MODE != GRAD_STATS_ONLY)
+                        mq[u] = __builtin_nontemporal_load(reinterpret_cast<const gptr<const u32x4>>(mic + off));
                 } else {
                     uint32_t w[4] = {0u, 0u, 0u, 0u}, mw[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -1037,7 +1040,7 @@ __global__ __launch_bounds__(256) void k_rowcol_partial(const DevMatrix* __restr
                 for (int k = 0; k < 4; ++k) w[k] = grad_pair<MODE>(w[k], mw[k]);
                 const int64_t off = r * M.cols + c0;
                 if (vec) {
-                    *reinterpret_cast<gptr<u32x4>>(grad + off) = u32x4{w[0], w[1], w[2], w[3]};
+                    __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<gptr<u32x4>>(grad + off));
                 } else {
 #pragma unroll
                     for (int k = 0; k < 8; ++k)
