@@ -38,8 +38,8 @@ int64_t q4probe_byte_mix_bytes(int64_t n);
 /* The step's byte mix over n elements (n a positive multiple of 512):
  * param (n floats) and the codes (n/2 bytes each) and scales (n/128 floats
  * each) are read and rewritten in place with trivial arithmetic; grad (n
- * BF16 bit patterns) is read.  Same lane layout and work-group walk as the
- * step kernel. */
+ * BF16 bit patterns) is read.  Same lane layout, cache policy (masters and
+ * gradients nontemporal) and work-group walk as the step kernel. */
 int q4probe_byte_mix(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
                      float* v_scales, int64_t n, void* stream);
 
@@ -57,8 +57,8 @@ int64_t q4probe_byte_mix8_bytes(int64_t n);
  * section "Requirements and errors", names the 8-bit blockwise AdamW; one
  * byte per code and 128-element blocks here): as
  * q4probe_byte_mix, with m_codes and v_codes holding n bytes each, read and
- * rewritten 8 bytes per lane, and the work-groups taking runs of 4 slabs as
- * the 8-bit step does. */
+ * rewritten 8 bytes per lane (4 in each half of its block), and the
+ * work-groups taking runs of 4 slabs as the 8-bit step does. */
 int q4probe_byte_mix8(float* param, const uint16_t* grad, uint8_t* m_codes, uint8_t* v_codes, float* m_scales,
                       float* v_scales, int64_t n, void* stream);
 
