@@ -88,12 +88,17 @@ enum StepFlags : uint32_t {
 };
 
 // Workspace layout shared by host and kernels: the first 256 bytes hold the
-// gradient statistics' sum of squares (binary64, offset 0) and the clip
-// factor (FP32, offset 8); the tensor table starts at byte 256, so a kernel
-// that has the table finds the clip factor 248 bytes before it.
-constexpr size_t kWsOffSq = 0, kWsOffClip = 8, kWsOffTable = 256;
+// gradient statistics' sum of squares (binary64, offset 0), the clip factor
+// (FP32, offset 8) and the run queue of the 8-bit step (a 64-bit counter,
+// offset 16, zeroed before each launch); the tensor table starts at byte
+// 256, so a kernel that has the table finds the others before it.
+constexpr size_t kWsOffSq = 0, kWsOffClip = 8, kWsOffQueue = 16, kWsOffTable = 256;
 __host__ __device__ inline const float* clip_of_table(const DevTensor* tab) {
     return reinterpret_cast<const float*>(reinterpret_cast<const char*>(tab) - kWsOffTable + kWsOffClip);
+}
+__host__ __device__ inline unsigned long long* queue_of_table(const DevTensor* tab) {
+    return reinterpret_cast<unsigned long long*>(const_cast<char*>(reinterpret_cast<const char*>(tab)) - kWsOffTable +
+                                                 kWsOffQueue);
 }
 
 // Kernel variants that exist (m codebook, v codebook, v rule).

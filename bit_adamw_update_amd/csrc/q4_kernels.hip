@@ -860,28 +860,50 @@ __device__ __forceinline__ void step8_chunk(const DevTensor& T, const int64_t lc
     }
 }
 
+// One round of resident work-groups takes runs of run_slabs slabs from the
+// queue word of the workspace (zeroed by k_zero_queue just before the
+// launch), in increasing order, until none is left.  Each group builds its
+// tables once for all its runs.  For this byte mix the queue moves 6% more
+// than one group per run (the bandwidth probes' two forms of the 8-bit mix).
 template <bool CLIP>
-__global__ __launch_bounds__(256) void k_step8(const DevTensor* __restrict__ tab,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8))) void k_step8(const DevTensor* __restrict__ tab,
                                                 const int64_t* __restrict__ chunk_begin, int n_tensors,
                                                 int64_t total_chunks, int run_slabs, StepScalars sc) {
     __shared__ Step8Lds lds;
+    __shared__ unsigned long long next_run;
     step8_tables(lds);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const float gs = CLIP ? *clip_of_table(tab) : 1.0f;
-    const int64_t G = gridDim.x;
-    int64_t c = (int64_t)blockIdx.x * run_slabs * kWavesPerGroup + wave;
-    int t = first_tensor(chunk_begin, n_tensors, c);
-    for (int j = 0; c < total_chunks;) {
-        while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
-        const DevTensor T = tab[t];
-        const int64_t lc = c - chunk_begin[t];
-        if (lc * kChunkElems < T.numel) {  // beyond: a chunk that only aligns the next tensor
-            if ((lc + 1) * kChunkElems <= T.numel) step8_chunk<true, CLIP>(T, lc, sc, lds, lane, gs);
-            else step8_chunk<false, CLIP>(T, lc, sc, lds, lane, gs);
+    unsigned long long* const queue = queue_of_table(tab);
+    const int64_t run_chunks = (int64_t)run_slabs * kWavesPerGroup;
+    const int64_t runs = (total_chunks + run_chunks - 1) / run_chunks;
+    int t = -1;
+    for (;;) {
+        if (threadIdx.x == 0) next_run = atomicAdd(queue, 1ull);
+        __syncthreads();
+        const int64_t r = (int64_t)next_run;
+        __syncthreads();  // every wave has read the run before thread 0 takes the next
+        if (r >= runs) break;  // uniform over the group
+        int64_t c = r * run_chunks + wave;
+        // the runs a group takes increase, so its tensor index only moves on
+        if (t < 0) t = first_tensor(chunk_begin, n_tensors, c);
+        for (int s = 0; s < run_slabs && c < total_chunks; ++s, c += kWavesPerGroup) {
+            while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
+            const DevTensor T = tab[t];
+            const int64_t lc = c - chunk_begin[t];
+            if (lc * kChunkElems < T.numel) {  // beyond: a chunk that only aligns the next tensor
+                if ((lc + 1) * kChunkElems <= T.numel) step8_chunk<true, CLIP>(T, lc, sc, lds, lane, gs);
+                else step8_chunk<false, CLIP>(T, lc, sc, lds, lane, gs);
+            }
         }
-        c = next_chunk(c, j, run_slabs, G);
     }
+}
+
+// The 8-bit step's queue word set to 0 (a kernel, so that a captured graph
+// clears it on every replay).
+__global__ void k_zero_queue(unsigned long long* q) {
+    if (threadIdx.x == 0) *q = 0ull;
 }
 
 __global__ __launch_bounds__(256) void k_dequant8(DevTensor T, float* __restrict__ m_out, float* __restrict__ v_out) {
@@ -1550,16 +1572,26 @@ hipError_t launch_fill(void* p, size_t bytes, uint8_t value, hipStream_t stream)
     return hipGetLastError();
 }
 
+// One round of resident groups (no more than there are runs) over runs of
+// the length run_per_group picks.
+template <class K>
+static RunLaunch queue_launch(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, int max_run) {
+    const RunLaunch L = run_per_group(kernel, total_chunks, per_cu_cache, max_run);
+    const int64_t resident = resident_groups(kernel, per_cu_cache);
+    return {(int)(L.grid < resident ? L.grid : resident), L.run_slabs};
+}
+
 hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
                               int n_tensors, int64_t total_chunks, hipStream_t stream) {
     if (total_chunks <= 0) return hipSuccess;
+    k_zero_queue<<<1, 64, 0, stream>>>(queue_of_table(d_tab));
     if (sc.flags & SF_CLIP) {
         static std::atomic<int> occ{0};
-        const RunLaunch L = run_per_group(k_step8<true>, total_chunks, occ, kRunSlabsCompact);
+        const RunLaunch L = queue_launch(k_step8<true>, total_chunks, occ, kRunSlabsCompact);
         k_step8<true><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     } else {
         static std::atomic<int> occ{0};
-        const RunLaunch L = run_per_group(k_step8<false>, total_chunks, occ, kRunSlabsCompact);
+        const RunLaunch L = queue_launch(k_step8<false>, total_chunks, occ, kRunSlabsCompact);
         k_step8<false><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     }
     return hipGetLastError();
