@@ -1371,15 +1371,18 @@ constexpr int64_t kMaxRunGroups = int64_t(1) << 22;
 // had swept the chunks grid-stride, 13.925 -> 13.49 ms.  Grids of 16x-32x
 // the resident groups that loop were slower than both (ZIP-SR 6.84 ms).
 // Runs are of max_run slabs, shortened while the set has fewer runs than
-// resident groups.  The best length depends on the group's setup: the ZIP-SR
-// kernels, whose groups each copy a 24.5 KB table, take runs of 8 (GPT-2.7B:
-// 4 slabs 6.525 ms, 8 6.357, 16 6.361, 32 6.410); the others take runs of 4
-// (ZE-EDEN 6.146 ms against 6.207 with 8 and 6.338 with 16; 8-bit 7.259
-// against 7.321 with 8 and 7.41 with 2; factored 1.525 against 1.573 with 8).
+// resident groups.  The best length depends on the group's setup and on the
+// access policy.  Measured with the streaming row-block kernels, each pair in
+// one process over the same buffers (GPT-2.7B unless named): the ZIP-SR
+// kernels, whose groups each copy a 24.5 KB table, take runs of 8 (4 slabs
+// 1.7% slower, Llama-1.1B 1.4%; 16 slabs 2.3% slower); the others take runs
+// of 2, which fill one 128-byte line of each scale stream (ZE-EDEN 1.7% and
+// FP32 3.6% faster than 4, the factored step alike; 8 slabs 3-4% slower than
+// 4).  The 8-bit step takes runs of 4 from its queue.
 struct RunLaunch {
     int grid, run_slabs;
 };
-constexpr int kRunSlabsFlat = 8, kRunSlabsCompact = 4;
+constexpr int kRunSlabsFlat = 8, kRunSlabsCompact = 2, kRunSlabs8 = 4;
 template <class K>
 static RunLaunch run_per_group(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, int max_run) {
     const int64_t resident = resident_groups(kernel, per_cu_cache);
@@ -1587,11 +1590,11 @@ hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, con
     k_zero_queue<<<1, 64, 0, stream>>>(queue_of_table(d_tab));
     if (sc.flags & SF_CLIP) {
         static std::atomic<int> occ{0};
-        const RunLaunch L = queue_launch(k_step8<true>, total_chunks, occ, kRunSlabsCompact);
+        const RunLaunch L = queue_launch(k_step8<true>, total_chunks, occ, kRunSlabs8);
         k_step8<true><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     } else {
         static std::atomic<int> occ{0};
-        const RunLaunch L = queue_launch(k_step8<false>, total_chunks, occ, kRunSlabsCompact);
+        const RunLaunch L = queue_launch(k_step8<false>, total_chunks, occ, kRunSlabs8);
         k_step8<false><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks, L.run_slabs, sc);
     }
     return hipGetLastError();

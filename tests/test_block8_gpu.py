@@ -107,8 +107,9 @@ def test_zero_size_tensors_between_others():
 
 
 def test_mid_size_set_takes_short_runs():
-    """About 10.2 M elements: the one-group-per-run launch takes runs of 2
-    slabs here (fewer than 4 x 2,048 resident groups' worth of slabs)."""
+    """About 10.2 M elements: the resident groups take runs of 2 slabs from
+    the queue here, not 4 (fewer than 4 x 2,048 resident groups' worth of
+    slabs)."""
     shapes = [(1024, 4096), (2048, 2048), (1_000_003,), (777, 1031), (4097,)]
     _flush("block8 mid-size set")
     run_windows(inputs.custom(shapes, grad_kind="masked", seed=45), 3)

@@ -81,9 +81,9 @@ def test_mid_size_set_takes_short_runs(recipe):
     """A set of about 10.2 M elements (about 5,000 slabs of 4 chunks): with
     one work-group per run and at least as many runs as resident groups
     (1,536 for the ZIP-SR kernel, 2,048 for the others on MI355X), the
-    launch takes runs of 2 slabs here, between the single slabs of the tiny
-    sets and the 4- and 8-slab runs of the large ones.  Every element, 3
-    steps, tensors and matrices of uneven sizes."""
+    launch takes runs of 2 slabs here: shortened for the ZIP-SR kernel, whose
+    large sets take runs of 8, and the full length of the others.  Every
+    element, 3 steps, tensors and matrices of uneven sizes."""
     shapes = [(1024, 4096), (2048, 2048), (1_000_003,), (777, 1031), (4097,)]
     w = inputs.custom(shapes, grad_kind="masked", seed=33)
     _flush(f"mid-size set {recipe}")
