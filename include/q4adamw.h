@@ -267,9 +267,10 @@ q4_status q4adamw_init_state(const q4_config* cfg, const q4_tensor* t, int32_t n
  * norm gives s = 1 (the comparison with 1 fails), an infinite norm s = 0.
  * Stochastic rounding draws Philox4x32-10 with counter (i/4, step,
  * tensor_id, stream 0 for m / 1 for v), key (seed), word i mod 4.
- * `ws` (device, ws_bytes >= q4adamw_workspace_bytes) holds the tensor table
- * and the factored partial sums; it must not be used by another call that
- * overlaps on the device. */
+ * `ws` (device, ws_bytes >= q4adamw_workspace_bytes) holds the tensor table,
+ * the factored partial sums, the clip statistics and the 8-bit step's run
+ * queue (cleared on the stream before each 8-bit launch); it must not be
+ * used by another call that overlaps on the device. */
 q4_status q4adamw_step(const q4_config* cfg, const q4_hparams* hp, const q4_tensor* t, int32_t n_tensors,
                        void* ws, size_t ws_bytes, void* stream);
 
