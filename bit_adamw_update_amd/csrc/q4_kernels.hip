@@ -569,6 +569,17 @@ template <int MCB, int VCB, int VRULE> constexpr bool factored_maps() {
     return MCB == Q4_CB_NF4 && VCB == Q4_CB_DYN4_NZ && VRULE == Q4_RULE_STATE_RTN;
 }
 
+// Instantiations that walk a queue of runs instead of one work-group per
+// run: those of the ZE-EDEN maps without factored matrices.  Measured in one
+// process over the same buffers (GPT-2.7B ZE-EDEN): runs of 4 from the
+// queue 2.0% faster than one group per run of 2, runs of 8 4% slower.  The
+// queue loop takes this kernel to 72 VGPRs (7 wavefronts per SIMD, its
+// target) without spilling; the other instantiations of the compact tables
+// spill with it, and ZIP-SR is bound by its arithmetic.
+template <int MCB, int VCB, int VRULE, bool MATS> constexpr bool queue_walk() {
+    return factored_maps<MCB, VCB, VRULE>() && !MATS;
+}
+
 template <int MCB, int VCB, int VRULE, bool CLIP, bool MATS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves<VRULE>())))
 void k_fused_step(const DevTensor* __restrict__ tab,
@@ -624,11 +635,7 @@ void k_fused_step(const DevTensor* __restrict__ tab,
     // clipping is a separate instantiation: the unclipped kernel carries no
     // trace of it (its live values are what limits occupancy)
     const float gs = CLIP ? *clip_of_table(tab) : 1.0f;
-    const int64_t G = gridDim.x;
-    int64_t c = (int64_t)blockIdx.x * run_slabs * kWavesPerGroup + wave;
-    int t = first_tensor(chunk_begin, n_tensors, c);
-    for (int j = 0; c < total_chunks;) {
-        while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
+    auto chunk_of = [&](int64_t c, int t) {
         const DevTensor T = tab[t];
         const int64_t lc = c - chunk_begin[t];
         if (lc * kChunkElems < T.numel) {  // beyond: a chunk that only aligns the next tensor
@@ -641,7 +648,39 @@ void k_fused_step(const DevTensor* __restrict__ tab,
                 else step_chunk<MCB, VCB, VRULE, false, false, CLIP>(T, lc, c, sc, lds, lb, lane, gs);
             }
         }
-        c = next_chunk(c, j, run_slabs, G);
+    };
+    if constexpr (queue_walk<MCB, VCB, VRULE, MATS>()) {
+        // one round of resident groups taking runs from the workspace's queue
+        // word (zeroed just before the launch), in increasing order
+        __shared__ unsigned long long next_run;
+        unsigned long long* const queue = queue_of_table(tab);
+        const int64_t run_chunks = (int64_t)run_slabs * kWavesPerGroup;
+        const int64_t runs = (total_chunks + run_chunks - 1) / run_chunks;
+        int t = -1;
+        for (;;) {
+            if (threadIdx.x == 0) next_run = atomicAdd(queue, 1ull);
+            __syncthreads();
+            const unsigned long long rv = next_run;
+            __syncthreads();  // every wave has read the run before thread 0 takes the next
+            const int64_t r = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(rv >> 32)) << 32) |
+                                        __builtin_amdgcn_readfirstlane((uint32_t)rv));
+            if (r >= runs) break;
+            int64_t c = r * run_chunks + wave;
+            if (t < 0) t = first_tensor(chunk_begin, n_tensors, c);
+            for (int s = 0; s < run_slabs && c < total_chunks; ++s, c += kWavesPerGroup) {
+                while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
+                chunk_of(c, t);
+            }
+        }
+    } else {
+        const int64_t G = gridDim.x;
+        int64_t c = (int64_t)blockIdx.x * run_slabs * kWavesPerGroup + wave;
+        int t = first_tensor(chunk_begin, n_tensors, c);
+        for (int j = 0; c < total_chunks;) {
+            while (t + 1 < n_tensors && chunk_begin[t + 1] <= c) ++t;
+            chunk_of(c, t);
+            c = next_chunk(c, j, run_slabs, G);
+        }
     }
 }
 
@@ -1378,11 +1417,11 @@ constexpr int64_t kMaxRunGroups = int64_t(1) << 22;
 // 1.7% slower, Llama-1.1B 1.4%; 16 slabs 2.3% slower); the others take runs
 // of 2, which fill one 128-byte line of each scale stream (ZE-EDEN 1.7% and
 // FP32 3.6% faster than 4, the factored step alike; 8 slabs 3-4% slower than
-// 4).  The 8-bit step takes runs of 4 from its queue.
+// 4).  The 8-bit step and the ZE-EDEN kernel take runs of 4 from a queue.
 struct RunLaunch {
     int grid, run_slabs;
 };
-constexpr int kRunSlabsFlat = 8, kRunSlabsCompact = 2, kRunSlabs8 = 4;
+constexpr int kRunSlabsFlat = 8, kRunSlabsCompact = 2, kRunSlabs8 = 4, kRunSlabsQueue = 4;
 template <class K>
 static RunLaunch run_per_group(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, int max_run) {
     const int64_t resident = resident_groups(kernel, per_cu_cache);
@@ -1394,6 +1433,15 @@ static RunLaunch run_per_group(K kernel, int64_t total_chunks, std::atomic<int>&
     while (r > 1 && slabs / r < resident) r >>= 1;
     const int64_t runs = (slabs + r - 1) / r;
     return {(int)(runs < 1 ? 1 : (runs > kMaxRunGroups ? kMaxRunGroups : runs)), r};
+}
+
+// One round of resident groups (no more than there are runs) over runs of
+// the length run_per_group picks.
+template <class K>
+static RunLaunch queue_launch(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, int max_run) {
+    const RunLaunch L = run_per_group(kernel, total_chunks, per_cu_cache, max_run);
+    const int64_t resident = resident_groups(kernel, per_cu_cache);
+    return {(int)(L.grid < resident ? L.grid : resident), L.run_slabs};
 }
 
 #define Q4_VARIANTS(X)                                              \
@@ -1417,6 +1465,13 @@ template <int A, int B, int C, bool CLIP, bool MATS>
 static hipError_t launch_step_kernel(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
                                      int n_tensors, int64_t total_chunks, hipStream_t stream) {
     static std::atomic<int> occ{0};
+    if constexpr (queue_walk<A, B, C, MATS>()) {
+        k_zero_queue<<<1, 64, 0, stream>>>(queue_of_table(d_tab));
+        const RunLaunch L = queue_launch(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ, kRunSlabsQueue);
+        k_fused_step<A, B, C, CLIP, MATS><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors,
+                                                                      total_chunks, L.run_slabs, sc);
+        return hipGetLastError();
+    }
     const RunLaunch L = run_per_group(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ,
                                       flat_tables<B, C>() ? kRunSlabsFlat : kRunSlabsCompact);
     k_fused_step<A, B, C, CLIP, MATS><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors, total_chunks,
@@ -1573,15 +1628,6 @@ hipError_t launch_fill(void* p, size_t bytes, uint8_t value, hipStream_t stream)
     if (groups > 4096) groups = 4096;
     k_fill<<<(unsigned)groups, 256, 0, stream>>>((uint8_t*)p, bytes, value);
     return hipGetLastError();
-}
-
-// One round of resident groups (no more than there are runs) over runs of
-// the length run_per_group picks.
-template <class K>
-static RunLaunch queue_launch(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, int max_run) {
-    const RunLaunch L = run_per_group(kernel, total_chunks, per_cu_cache, max_run);
-    const int64_t resident = resident_groups(kernel, per_cu_cache);
-    return {(int)(L.grid < resident ? L.grid : resident), L.run_slabs};
 }
 
 hipError_t launch_block8_step(const StepScalars& sc, const DevTensor* d_tab, const int64_t* d_chunk_begin,
