@@ -569,18 +569,21 @@ template <int MCB, int VCB, int VRULE> constexpr bool factored_maps() {
     return MCB == Q4_CB_NF4 && VCB == Q4_CB_DYN4_NZ && VRULE == Q4_RULE_STATE_RTN;
 }
 
-// Instantiations that walk a queue of runs instead of one work-group per
-// run: those of the ZE-EDEN maps without factored matrices.  Measured in one
-// process over the same buffers (GPT-2.7B ZE-EDEN): runs of 4 from the
-// queue 2.0% faster than one group per run of 2, runs of 8 4% slower.  The
-// queue loop takes this kernel to 72 VGPRs (7 wavefronts per SIMD, its
+// Instantiations that also come in a form walking a queue of runs instead of
+// one work-group per run: those of the ZE-EDEN maps without factored
+// matrices, on large sets.  Measured in one process over the same buffers:
+// GPT-2.7B ZE-EDEN (about 180 runs of 4 per resident group) 2.0% faster with
+// runs of 4 from the queue than with one group per run of 2, runs of 8 4%
+// slower; GPT-162M ZE-EDEN (about 8 runs per group) 12% slower, so the
+// launch takes the queue only from kQueueMinRunsPerGroup runs per group.
+// The queue loop takes this kernel to 72 VGPRs (7 wavefronts per SIMD, its
 // target) without spilling; the other instantiations of the compact tables
 // spill with it, and ZIP-SR is bound by its arithmetic.
 template <int MCB, int VCB, int VRULE, bool MATS> constexpr bool queue_walk() {
     return factored_maps<MCB, VCB, VRULE>() && !MATS;
 }
 
-template <int MCB, int VCB, int VRULE, bool CLIP, bool MATS>
+template <int MCB, int VCB, int VRULE, bool CLIP, bool MATS, bool QUEUE = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves<VRULE>())))
 void k_fused_step(const DevTensor* __restrict__ tab,
                                                      const int64_t* __restrict__ chunk_begin, int n_tensors,
@@ -649,7 +652,8 @@ void k_fused_step(const DevTensor* __restrict__ tab,
             }
         }
     };
-    if constexpr (queue_walk<MCB, VCB, VRULE, MATS>()) {
+    static_assert(!QUEUE || queue_walk<MCB, VCB, VRULE, MATS>(), "no queue form for these maps");
+    if constexpr (QUEUE) {
         // one round of resident groups taking runs from the workspace's queue
         // word (zeroed just before the launch), in increasing order
         __shared__ unsigned long long next_run;
@@ -1417,11 +1421,13 @@ constexpr int64_t kMaxRunGroups = int64_t(1) << 22;
 // 1.7% slower, Llama-1.1B 1.4%; 16 slabs 2.3% slower); the others take runs
 // of 2, which fill one 128-byte line of each scale stream (ZE-EDEN 1.7% and
 // FP32 3.6% faster than 4, the factored step alike; 8 slabs 3-4% slower than
-// 4).  The 8-bit step and the ZE-EDEN kernel take runs of 4 from a queue.
+// 4).  The 8-bit step, and the ZE-EDEN kernel on large sets, take runs of 4
+// from a queue.
 struct RunLaunch {
     int grid, run_slabs;
 };
 constexpr int kRunSlabsFlat = 8, kRunSlabsCompact = 2, kRunSlabs8 = 4, kRunSlabsQueue = 4;
+constexpr int64_t kQueueMinRunsPerGroup = 64;
 template <class K>
 static RunLaunch run_per_group(K kernel, int64_t total_chunks, std::atomic<int>& per_cu_cache, int max_run) {
     const int64_t resident = resident_groups(kernel, per_cu_cache);
@@ -1466,11 +1472,17 @@ static hipError_t launch_step_kernel(const StepScalars& sc, const DevTensor* d_t
                                      int n_tensors, int64_t total_chunks, hipStream_t stream) {
     static std::atomic<int> occ{0};
     if constexpr (queue_walk<A, B, C, MATS>()) {
-        k_zero_queue<<<1, 64, 0, stream>>>(queue_of_table(d_tab));
-        const RunLaunch L = queue_launch(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ, kRunSlabsQueue);
-        k_fused_step<A, B, C, CLIP, MATS><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors,
-                                                                      total_chunks, L.run_slabs, sc);
-        return hipGetLastError();
+        static std::atomic<int> occq{0};
+        const int64_t resident = resident_groups(k_fused_step<A, B, C, CLIP, MATS, true>, occq);
+        const int64_t slabs = (total_chunks + kWavesPerGroup - 1) / kWavesPerGroup;
+        if ((slabs + kRunSlabsQueue - 1) / kRunSlabsQueue >= kQueueMinRunsPerGroup * resident) {
+            k_zero_queue<<<1, 64, 0, stream>>>(queue_of_table(d_tab));
+            const RunLaunch L =
+                queue_launch(k_fused_step<A, B, C, CLIP, MATS, true>, total_chunks, occq, kRunSlabsQueue);
+            k_fused_step<A, B, C, CLIP, MATS, true><<<L.grid, 256, 0, stream>>>(d_tab, d_chunk_begin, n_tensors,
+                                                                                total_chunks, L.run_slabs, sc);
+            return hipGetLastError();
+        }
     }
     const RunLaunch L = run_per_group(k_fused_step<A, B, C, CLIP, MATS>, total_chunks, occ,
                                       flat_tables<B, C>() ? kRunSlabsFlat : kRunSlabsCompact);
